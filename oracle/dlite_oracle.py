@@ -1,0 +1,256 @@
+"""Plain fp64 CPU oracle for the DLite draft step and greedy prefix accept.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import or run this module; the product library never
+does.  It is deliberately slow and direct: numpy float64 throughout, one
+library matmul per linear map, no fusion and no reordering beyond what the
+definitions below state.  It shares no code with the HIP implementation.
+
+Sources.  Citations name the page and its section:
+  [W]  "DLite 完全拆解" walkthrough, pinghaoyang.com.cn (the primary source);
+  [S]  DLite paper summary, yomxxx.com;
+  [F]  DFlash article, charlestar.github.io (shared verification math).
+
+Where the pages leave a step open the plainest reading is taken; each such
+reading is marked READING below.
+
+Pinned by the tests under tests/ (closed forms, worked examples printed on the
+pages, library cross-checks, invariants and special cases).  Parity status of
+the composed drafter: the pages print no value for any draft tensor, so the
+composition is pinned through its pinned parts plus invariants only.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------- pieces ---
+
+
+def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """RMS normalisation over the last axis with a learned gain.
+
+    [W] section "历史并没有消失，而是由目标模型编码": the official code normalises
+    the depth-embedded feature.  READING: RMSNorm with gain, eps = 1e-6.
+    """
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return gain * (x / np.sqrt(ms + eps))
+
+
+def feature_slots(H: np.ndarray, depth_emb: np.ndarray, gain: np.ndarray,
+                  eps: float) -> np.ndarray:
+    """z[b, l] = Norm(h^(l) + e_depth^(l)) for each of the m selected layers.
+
+    [W] "历史并没有消失，而是由目标模型编码", equation for z_t^(l): a learned
+    depth vector of width D is added to each layer's hidden state.  [W]
+    "沿序列维拼接，保留各层的独立身份": the m features stay m separate sequence
+    slots of width D (not one concatenated m*D vector).
+    H: [B, m, D]; depth_emb: [m, D]  ->  [B, m, D].
+    """
+    return rms_norm(H + depth_emb[None, :, :], gain, eps)
+
+
+def local_positions(m: int, K: int) -> np.ndarray:
+    """Local RoPE positions of the S = m + 1 + K slots of one request.
+
+    [W] "局部位置编码切断草稿端的全局位置增长" (Figure 3 layout): the target
+    features and the anchor sit at local position 0, the placeholders follow
+    at 1, 2, 3, ...  Slot order: [features 0..m-1, anchor, placeholders 1..K].
+    """
+    return np.concatenate([np.zeros(m + 1, dtype=np.int64),
+                           np.arange(1, K + 1, dtype=np.int64)])
+
+
+def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotary embedding, rotate-half pairing (i, i + d/2).
+
+    READING: frequency of pair i is theta^(-2i/d), theta = 1e6, as in the
+    Qwen3 targets the pages use.  x: [..., S, heads, d]; pos: [S].
+    """
+    d = x.shape[-1]
+    half = d // 2
+    inv = theta ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = pos.astype(np.float64)[:, None] * inv[None, :]          # [S, half]
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x1 * sin + x2 * cos], axis=-1)
+
+
+def block_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Non-causal attention of the local queries over every slot of the block.
+
+    [W] "锚点是已经确定、尚待目标前向处理的输入": inside the short block the
+    drafter attends non-causally, so all placeholders are computed at once.
+    [W] "本轮临时 K/V 仍然需要计算": Q for the anchor and placeholders, K and V
+    for the context features and the local inputs; nothing persists.
+    Grouped heads: query head h reads key/value head floor(h / G).
+    q: [Lq, n_q, d]; k, v: [S, n_kv, d]  ->  [Lq, n_q, d].
+    """
+    n_q, d = q.shape[1], q.shape[2]
+    G = n_q // k.shape[1]
+    out = np.empty_like(q)
+    for h in range(n_q):
+        kh, vh = k[:, h // G, :], v[:, h // G, :]
+        sc = (q[:, h, :] @ kh.T) / np.sqrt(d)                      # [Lq, S]
+        sc = sc - sc.max(axis=1, keepdims=True)
+        p = np.exp(sc)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ vh
+    return out
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def swiglu_ffn(n: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """W_down (silu(W_gate n) * W_up n); w_gate_up holds gate rows then up rows.
+
+    READING: the backbone layer form is not printed; a pre-norm Qwen3-style
+    block (grouped attention + SwiGLU, no biases) is taken.
+    """
+    F = w_gate_up.shape[0] // 2
+    g = n @ w_gate_up[:F].T
+    u = n @ w_gate_up[F:].T
+    return (silu(g) * u) @ w_down.T
+
+
+# --------------------------------------------------------------- backbone ---
+
+
+def backbone_layer(ctx: np.ndarray, x: np.ndarray, pos: np.ndarray, lw: dict,
+                   dims) -> np.ndarray:
+    """One history-free backbone layer for one request.
+
+    ctx: [m, D] context slots (fixed across layers, READING of [W] "本轮临时
+    K/V 仍然需要计算": context features only supply K and V);
+    x: [1 + K, D] residual stream of the anchor and placeholders.
+    Returns the updated local residual stream.
+    """
+    n_q, n_kv, d_h, eps = dims.n_q, dims.n_kv, dims.d_h, dims.rms_eps
+    m = ctx.shape[0]
+    slots = np.concatenate([ctx, x], axis=0)                         # [S, D]
+    n_slots = rms_norm(slots, lw["attn_norm"], eps)
+    wq = lw["wqkv"][: n_q * d_h]
+    wk = lw["wqkv"][n_q * d_h: (n_q + n_kv) * d_h]
+    wv = lw["wqkv"][(n_q + n_kv) * d_h:]
+    q = (n_slots[m:] @ wq.T).reshape(-1, n_q, d_h)
+    k = (n_slots @ wk.T).reshape(-1, n_kv, d_h)
+    v = (n_slots @ wv.T).reshape(-1, n_kv, d_h)
+    q = rope(q, pos[m:], dims.rope_theta)
+    k = rope(k, pos, dims.rope_theta)
+    o = block_attention(q, k, v).reshape(x.shape[0], n_q * d_h)
+    x = x + o @ lw["wo"].T
+    n2 = rms_norm(x, lw["ffn_norm"], eps)
+    return x + swiglu_ffn(n2, lw["w_gate_up"], lw["w_down"])
+
+
+# ---------------------------------------------------------- sequential head ---
+
+
+def sequential_head(h: np.ndarray, w_down: np.ndarray, w_up: np.ndarray) -> np.ndarray:
+    """Low-rank recurrent state over the K block positions.
+
+    [W] "把条件分布拆成历史与本块前缀": a narrow state s_i in R^R, R << D, restores
+    the in-block dependency; it is reset at block start ("官方顺序头具体算了什么").
+    READING (the recurrence is fixed by the build's statement, because the
+    pages print only a different, token-fed gated head):
+        s_0 = 0,  s_k = s_{k-1} + W_up silu(W_down [h_k ; s_{k-1}]).
+    h: [K, D]; w_down: [r, D + r]; w_up: [r, r]  ->  s: [K, r] (s_1..s_K).
+    """
+    K = h.shape[0]
+    r = w_up.shape[0]
+    s = np.zeros(r)
+    out = np.empty((K, r))
+    for k in range(K):
+        t = w_down @ np.concatenate([h[k], s])
+        s = s + w_up @ silu(t)
+        out[k] = s
+    return out
+
+
+def lm_head_argmax(s: np.ndarray, lm_head: np.ndarray):
+    """Vocabulary projection applied once, after the head, then greedy choice.
+
+    [W] "避免的是昂贵的中间词表投影" and [S] "设计": the R -> V projection is done
+    once after the in-block dependencies are integrated.  [W] "贪心模式与随机模式
+    要分别说明": at temperature 0 the token with the largest logit is chosen.
+    READING: ties go to the lowest vocabulary index.
+    s: [..., r]; lm_head: [V, r]  ->  logits [..., V], tokens [...], margin [...]
+    (margin = largest minus second-largest logit).
+    """
+    logits = s @ lm_head.T
+    tok = np.argmax(logits, axis=-1)          # first index of the maximum
+    top2 = np.partition(logits, -2, axis=-1)[..., -2:]
+    margin = top2[..., 1] - top2[..., 0]
+    return logits, tok.astype(np.int64), margin
+
+
+# ------------------------------------------------------------------- step ---
+
+
+def draft_block(dims, weights: dict, H: np.ndarray, anchor_rows: np.ndarray) -> dict:
+    """The whole draft step for a batch: K greedy candidates per request.
+
+    dims: object with B, m, D, n_layers, n_q, n_kv, d_h, K, rms_eps, rope_theta.
+    weights: fp64 arrays keyed as in the library's weight layout (layers list).
+    H: [B, m, D] boundary features; anchor_rows: [B, D] = tok_emb[anchor].
+    Returns dict with z [B,m,D], x_layers (list of [B,1+K,D]), h [B,K,D],
+    s [B,K,r], logits [B,K,V], cand [B,K], margin [B,K].
+
+    [W] "从目标隐藏状态到并行草稿表示" (Figure 3) and the generation loop in
+    "一轮执行后，缓存、锚点与隐藏状态怎样对齐": features + anchor + placeholders
+    -> parallel backbone -> sequential head -> proposals.
+    """
+    B, m, K = dims.B, dims.m, dims.K
+    z = feature_slots(H, weights["depth_emb"], weights["feat_norm"], dims.rms_eps)
+    pos = local_positions(m, K)
+    # [W] "锚点是已经确定…": the anchor enters through its embedding;
+    # READING: one shared learned placeholder vector for all K slots.
+    x = np.empty((B, 1 + K, dims.D))
+    x[:, 0] = anchor_rows
+    x[:, 1:] = weights["ph_emb"][None, None, :]
+    x_layers = []
+    for lw in weights["layers"]:
+        x = np.stack([backbone_layer(z[b], x[b], pos, lw, dims) for b in range(B)])
+        x_layers.append(x.copy())
+    # READING: a final RMSNorm before the head; only placeholder rows are drafted.
+    h = rms_norm(x[:, 1:], weights["final_norm"], dims.rms_eps)
+    s = np.stack([sequential_head(h[b], weights["seq_w_down"], weights["seq_w_up"])
+                  for b in range(B)])
+    logits, cand, margin = lm_head_argmax(s, weights["lm_head"])
+    return dict(z=z, x_layers=x_layers, h=h, s=s, logits=logits, cand=cand,
+                margin=margin)
+
+
+# ----------------------------------------------------------------- accept ---
+
+
+def accept_prefix(cand: np.ndarray, target: np.ndarray):
+    """Greedy verification: longest accepted prefix and the next anchor.
+
+    [W] "一次因果前向评估整条候选": only the leading run of passes is committed;
+    the official code takes a cumulative product of the boolean matches.
+    [W] "先拆开一次投机轮次的时间": 0 <= A <= K and a round commits A + 1 tokens.
+    [W] "一轮执行后…": the next anchor is the target token at verify index A
+    (index 0 is the anchor's own output when nothing passed).
+    cand: [B, K] draft tokens d_1..d_K; target: [B, K + 1] target tokens at
+    the verify inputs [a, d_1..d_K].  Returns A [B], next_anchor [B].
+    """
+    cand = np.asarray(cand)
+    target = np.asarray(target)
+    K = cand.shape[1]
+    passed = (cand == target[:, :K]).astype(np.int64)
+    A = np.cumprod(passed, axis=1).sum(axis=1)
+    nxt = target[np.arange(target.shape[0]), A]
+    return A.astype(np.int64), nxt.astype(np.int64)
+
+
+def prefix_survival(c: np.ndarray) -> np.ndarray:
+    """P(A >= k) = prod_{i<=k} c_i for k = 1..K ([F] "为什么验证仍然只接受最长前缀")."""
+    return np.cumprod(np.asarray(c, dtype=np.float64), axis=-1)
+
+
+def expected_commit(c: np.ndarray) -> np.ndarray:
+    """tau = E[A + 1] = 1 + sum_j P(A >= j) ([W] "分布重叠怎样影响平均推进量")."""
+    return 1.0 + prefix_survival(c).sum(axis=-1)
