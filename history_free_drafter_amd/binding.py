@@ -1,0 +1,160 @@
+"""ctypes binding of libdlite.so: the C ABI declared in include/dlite.h.
+
+Argument marshalling only.  Every step of the draft and accept computations
+runs in the library's HIP kernels; torch is used for device memory and for the
+current stream.  If the library is missing the import fails loudly: there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_char_p, c_float, c_int, c_int32, c_size_t, c_void_p
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdlite.so")
+
+DLITE_F32, DLITE_BF16 = 0, 1
+ERRORS = {-1: "DLITE_ERR_NULL", -2: "DLITE_ERR_SHAPE", -3: "DLITE_ERR_DTYPE",
+          -4: "DLITE_ERR_WORKSPACE", -5: "DLITE_ERR_UNSUPPORTED", -6: "DLITE_ERR_HIP"}
+EXPORTS = ["dlite_workspace_bytes", "dlite_draft_block", "dlite_accept_prefix",
+           "dlite_last_error", "dlite_version"]
+
+
+class DliteDims(Structure):
+    _fields_ = [(n, c_int32) for n in
+                ("B", "m", "D", "n_layers", "n_q", "n_kv", "d_h", "ffn", "K", "rank",
+                 "vocab", "dtype")] + [("rms_eps", c_float), ("rope_theta", c_float)]
+
+
+class DliteLayerWeights(Structure):
+    _fields_ = [(n, c_void_p) for n in
+                ("attn_norm", "wqkv", "wo", "ffn_norm", "w_gate_up", "w_down")]
+
+
+class DliteWeights(Structure):
+    _fields_ = [("depth_emb", c_void_p), ("feat_norm", c_void_p), ("tok_emb", c_void_p),
+                ("ph_emb", c_void_p), ("layers", POINTER(DliteLayerWeights)),
+                ("final_norm", c_void_p), ("seq_w_down", c_void_p), ("seq_w_up", c_void_p),
+                ("lm_head", c_void_p)]
+
+
+class DliteTaps(Structure):
+    _fields_ = [(n, c_void_p) for n in ("z", "x", "hidden", "state", "logits")]
+
+
+class DliteError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libdlite.so once and declare the prototypes of its exports."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it first (python -m history_free_drafter_amd.build)")
+    lib = ctypes.CDLL(path)
+    lib.dlite_workspace_bytes.argtypes = [POINTER(DliteDims)]
+    lib.dlite_workspace_bytes.restype = c_size_t
+    lib.dlite_draft_block.argtypes = [POINTER(DliteDims), POINTER(DliteWeights), c_void_p,
+                                      c_void_p, c_void_p, c_void_p, POINTER(DliteTaps),
+                                      c_void_p, c_size_t, c_void_p]
+    lib.dlite_draft_block.restype = c_int
+    lib.dlite_accept_prefix.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                        c_void_p, c_void_p]
+    lib.dlite_accept_prefix.restype = c_int
+    lib.dlite_last_error.argtypes = []
+    lib.dlite_last_error.restype = c_char_p
+    lib.dlite_version.argtypes = []
+    lib.dlite_version.restype = c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    """Device address of a torch tensor (or None / int passthrough)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc):
+    if rc != 0:
+        raise DliteError(rc, load_library().dlite_last_error().decode())
+
+
+def make_dims(B, m, D, n_layers, n_q, n_kv, d_h, ffn, K, rank, vocab, dtype,
+              rms_eps=1e-6, rope_theta=1e6) -> DliteDims:
+    return DliteDims(B, m, D, n_layers, n_q, n_kv, d_h, ffn, K, rank, vocab, dtype,
+                     rms_eps, rope_theta)
+
+
+def make_weights(w: dict):
+    """dlite_weights from a dict of device tensors (keys as in include/dlite.h).
+
+    Returns (struct, keepalive): keep `keepalive` referenced while the struct
+    is in use (it owns the host array of layer structs).
+    """
+    layers = (DliteLayerWeights * len(w["layers"]))(
+        *[DliteLayerWeights(*[_ptr(lw[k]) for k in
+                              ("attn_norm", "wqkv", "wo", "ffn_norm", "w_gate_up", "w_down")])
+          for lw in w["layers"]])
+    s = DliteWeights(_ptr(w["depth_emb"]), _ptr(w["feat_norm"]), _ptr(w["tok_emb"]),
+                     _ptr(w["ph_emb"]), ctypes.cast(layers, POINTER(DliteLayerWeights)),
+                     _ptr(w["final_norm"]), _ptr(w["seq_w_down"]), _ptr(w["seq_w_up"]),
+                     _ptr(w["lm_head"]))
+    return s, layers
+
+
+def make_taps(z=None, x=None, hidden=None, state=None, logits=None) -> DliteTaps:
+    return DliteTaps(_ptr(z), _ptr(x), _ptr(hidden), _ptr(state), _ptr(logits))
+
+
+def dlite_workspace_bytes(dims: DliteDims) -> int:
+    n = load_library().dlite_workspace_bytes(ctypes.byref(dims))
+    if n == 0:
+        raise DliteError(-2, load_library().dlite_last_error().decode())
+    return n
+
+
+def dlite_draft_block(dims, weights, features, anchor_ids, candidates, max_logit=None,
+                      taps=None, workspace=None, workspace_bytes=None, stream=None):
+    """Enqueue one draft step; see include/dlite.h for the contract."""
+    ws_bytes = workspace_bytes
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load_library().dlite_draft_block(
+        ctypes.byref(dims), ctypes.byref(weights), _ptr(features), _ptr(anchor_ids),
+        _ptr(candidates), _ptr(max_logit), ctypes.byref(taps) if taps is not None else None,
+        _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc)
+
+
+def dlite_accept_prefix(candidates, target_tokens, B, K, accept_len, next_anchor=None,
+                        stream=None):
+    """Enqueue greedy prefix acceptance; see include/dlite.h."""
+    rc = load_library().dlite_accept_prefix(_ptr(candidates), _ptr(target_tokens), B, K,
+                                            _ptr(accept_len), _ptr(next_anchor),
+                                            _stream(stream))
+    _check(rc)
+
+
+def dlite_version() -> str:
+    return load_library().dlite_version().decode()

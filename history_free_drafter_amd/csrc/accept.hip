@@ -1,0 +1,36 @@
+// Greedy prefix accept: one lane per request.
+//
+// A = number of leading positions where the draft equals the target's greedy
+// token (DLite walkthrough, section "一次因果前向评估整条候选": only the first
+// unbroken run of matches is committed); the next anchor is the target token at
+// verify index A ("一轮执行后，缓存、锚点与隐藏状态怎样对齐").  Integer only.
+#include "kernels.hpp"
+
+namespace dlite {
+
+namespace {
+
+__global__ __launch_bounds__(256) void accept_kernel(const int32_t* __restrict__ cand,
+                                                     const int32_t* __restrict__ tgt,
+                                                     int B, int K, int32_t* __restrict__ A,
+                                                     int32_t* __restrict__ next) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int32_t* c = cand + static_cast<long>(b) * K;
+  const int32_t* t = tgt + static_cast<long>(b) * (K + 1);
+  int n = 0;
+  while (n < K && c[n] == t[n]) ++n;
+  A[b] = n;
+  if (next) next[b] = t[n];
+}
+
+}  // namespace
+
+hipError_t launch_accept(const int32_t* cand, const int32_t* tgt, int B, int K,
+                         int32_t* A, int32_t* next, hipStream_t st) {
+  const dim3 block(256), grid((B + 255) / 256);
+  hipLaunchKernelGGL(accept_kernel, grid, block, 0, st, cand, tgt, B, K, A, next);
+  return hipGetLastError();
+}
+
+}  // namespace dlite

@@ -1,0 +1,57 @@
+"""Device buffers for the draft step: weights, workspace and outputs.
+
+torch is used only to allocate device memory and to name the stream; every
+computation is a call into libdlite.so through `binding`.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as _b
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """Upload a stored array: uint16 bf16 bit patterns -> bfloat16, else as is."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+class DraftModel:
+    """Weights resident on the GPU plus a workspace sized for the dimensions."""
+
+    def __init__(self, dims: dict, weights: dict, device="cuda"):
+        dt = _b.DLITE_BF16 if dims["dtype"] == "bf16" else _b.DLITE_F32
+        self.shape = dict(dims)
+        self.dims = _b.make_dims(dims["B"], dims["m"], dims["D"], dims["n_layers"],
+                                 dims["n_q"], dims["n_kv"], dims["d_h"], dims["ffn"],
+                                 dims["K"], dims["rank"], dims["vocab"], dt,
+                                 dims.get("rms_eps", 1e-6), dims.get("rope_theta", 1e6))
+        self.device = device
+        self.w = {k: (to_device(v, device) if v is not None and k != "layers" else None)
+                  for k, v in weights.items() if k != "layers"}
+        self.w["layers"] = [{k: to_device(v, device) for k, v in lw.items()}
+                            for lw in weights["layers"]]
+        self.wstruct, self._keep = _b.make_weights(self.w)
+        self.ws_bytes = _b.dlite_workspace_bytes(self.dims)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        B, K = dims["B"], dims["K"]
+        self.candidates = torch.empty((B, K), dtype=torch.int32, device=device)
+        self.max_logit = torch.empty((B, K), dtype=torch.float32, device=device)
+        self.accept_len = torch.empty((B,), dtype=torch.int32, device=device)
+        self.next_anchor = torch.empty((B,), dtype=torch.int32, device=device)
+
+    def draft(self, features: torch.Tensor, anchors: torch.Tensor, taps=None, stream=None,
+              weights=None):
+        _b.dlite_draft_block(self.dims, weights if weights is not None else self.wstruct,
+                             features, anchors, self.candidates, self.max_logit, taps,
+                             self.workspace, self.ws_bytes, stream)
+        return self.candidates
+
+    def accept(self, target_tokens: torch.Tensor, stream=None):
+        B, K = self.shape["B"], self.shape["K"]
+        _b.dlite_accept_prefix(self.candidates, target_tokens, B, K, self.accept_len,
+                               self.next_anchor, stream)
+        return self.accept_len, self.next_anchor

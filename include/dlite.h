@@ -1,0 +1,191 @@
+/*
+ * dlite.h — C ABI of the DLite draft step on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, following the statement of the problem on the DLite pages:
+ *
+ *   dlite_draft_block   boundary features [B, m, D] + anchor ids [B] + drafter
+ *                       weights  ->  K greedy candidates per request [B, K].
+ *   dlite_accept_prefix candidates [B, K] + target greedy tokens [B, K + 1]
+ *                       ->  accepted prefix length A [B] and next anchor [B].
+ *
+ * Sources (page title and section; no code is printed on them):
+ *   [W] "DLite 完全拆解" walkthrough (pinghaoyang.com.cn);
+ *   [S] DLite paper summary (yomxxx.com);
+ *   [F] DFlash article (charlestar.github.io), shared verification math.
+ *
+ * Conventions for every entry point.
+ *   Ownership   All tensor pointers are DEVICE pointers owned by the caller,
+ *               except the dlite_dims / dlite_weights / dlite_taps structs and
+ *               the dlite_weights.layers array, which are host memory and are
+ *               read only during the call.  The library allocates no device
+ *               memory and keeps no state between calls; all scratch lives in
+ *               the caller's workspace.
+ *   Layout      Row-major, densest axis last.  Matrices are
+ *               [out_features, in_features].
+ *   Streams     Work is enqueued on `stream` and the call returns without
+ *               synchronising; outputs are valid once the stream has
+ *               completed.  Buffers must stay alive until then.  Two calls
+ *               that share a workspace must be ordered on one stream.
+ *   Errors      0 on success, else a negative DLITE_ERR_* code; arguments are
+ *               validated before anything is enqueued, so a failed call
+ *               launches nothing.  dlite_last_error() returns a message for
+ *               the calling thread's last failure.  No exception crosses the
+ *               ABI.
+ *   Determinism Outputs are bitwise reproducible for identical inputs: no
+ *               floating-point atomics, fixed reduction orders.
+ */
+#ifndef DLITE_H
+#define DLITE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of weights, features and norm gains. */
+enum { DLITE_F32 = 0, DLITE_BF16 = 1 };
+
+enum {
+  DLITE_OK = 0,
+  DLITE_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  DLITE_ERR_SHAPE = -2,       /* a dimension is out of range or inconsistent   */
+  DLITE_ERR_DTYPE = -3,       /* unknown storage type                          */
+  DLITE_ERR_WORKSPACE = -4,   /* workspace smaller than dlite_workspace_bytes  */
+  DLITE_ERR_UNSUPPORTED = -5, /* valid but unsupported configuration           */
+  DLITE_ERR_HIP = -6          /* the HIP runtime reported a launch error       */
+};
+
+/*
+ * Problem dimensions.
+ *   B        requests in the batch (1 .. 4096)
+ *   m        selected target layers = context slots per request ([W] section
+ *            "历史并没有消失，而是由目标模型编码"; 1 .. 64)
+ *   D        target hidden width = drafter width (multiple of 64, <= 16384)
+ *   n_layers drafter backbone layers (1 .. 16)
+ *   n_q,n_kv query / key-value heads, n_q % n_kv == 0, n_q / n_kv <= 16
+ *   d_h      head width, 64 or 128
+ *   ffn      SwiGLU inner width F (multiple of 32)
+ *   K        placeholders = drafted tokens per request (1 .. 16); the paper's
+ *            block of 8 is the anchor plus K = 7 ([W] "草稿块长与验证块长不是一个参数")
+ *   rank     sequential-head state width r (multiple of 32, <= 1024)
+ *   vocab    vocabulary size V (1 .. 2^30)
+ *   dtype    DLITE_BF16 or DLITE_F32 for all weights and the features
+ *   rms_eps  RMSNorm epsilon (e.g. 1e-6)
+ *   rope_theta RoPE base (e.g. 1e6)
+ */
+typedef struct dlite_dims {
+  int32_t B, m, D, n_layers, n_q, n_kv, d_h, ffn, K, rank, vocab;
+  int32_t dtype;
+  float rms_eps, rope_theta;
+} dlite_dims;
+
+/* One backbone layer (pre-norm grouped attention + SwiGLU, no biases). */
+typedef struct dlite_layer_weights {
+  const void *attn_norm;  /* [D] RMSNorm gain before attention                 */
+  const void *wqkv;       /* [(n_q + 2 n_kv) d_h, D]: q heads, k heads, v heads */
+  const void *wo;         /* [D, n_q d_h]                                       */
+  const void *ffn_norm;   /* [D] RMSNorm gain before the FFN                    */
+  const void *w_gate_up;  /* [2F, D]: F gate rows, then F up rows               */
+  const void *w_down;     /* [D, F]                                             */
+} dlite_layer_weights;
+
+typedef struct dlite_weights {
+  const void *depth_emb;  /* [m, D] depth embedding e_depth ([W] eq. for z_t^(l)) */
+  const void *feat_norm;  /* [D] gain of the feature RMSNorm                       */
+  const void *tok_emb;    /* [V, D] anchor token embedding (only B rows are read)  */
+  const void *ph_emb;     /* [D] shared placeholder input                          */
+  const dlite_layer_weights *layers; /* HOST array of n_layers entries             */
+  const void *final_norm; /* [D] gain of the RMSNorm before the sequential head    */
+  const void *seq_w_down; /* [r, D + r]: columns 0..D-1 act on h_k, D.. on s_{k-1} */
+  const void *seq_w_up;   /* [r, r]                                                */
+  const void *lm_head;    /* [V, r] vocabulary projection of the state             */
+} dlite_weights;
+
+/*
+ * Optional fp32 copies of intermediate tensors, for checking.  Any member may
+ * be NULL; the same kernels run either way (the copy is a predicated store).
+ *   z       [B, m, D]               normalised, depth-embedded feature slots
+ *   x       [n_layers, B, 1 + K, D] anchor + placeholder residual stream after
+ *                                   each layer (the anchor row of the last
+ *                                   layer is not computed and is left as is)
+ *   hidden  [B, K, D]               h_k after the final RMSNorm
+ *   state   [B, K, r]               sequential-head states s_1..s_K
+ *   logits  [B, K, V]               vocabulary logits
+ */
+typedef struct dlite_taps {
+  float *z, *x, *hidden, *state, *logits;
+} dlite_taps;
+
+/*
+ * Workspace bytes dlite_draft_block needs for these dimensions; 0 if the
+ * dimensions are invalid (see dlite_last_error).  It depends on B, m, K and the
+ * model widths only: there is no history-length argument, because the drafter
+ * keeps no history KV ([W] "本轮临时 K/V 仍然需要计算").
+ */
+size_t dlite_workspace_bytes(const dlite_dims *dims);
+
+/*
+ * dlite_draft_block — one DLite draft step for a batch of requests.
+ *
+ * Computes, per request b ([W] Figure 3 data flow, sections
+ * "从目标隐藏状态到并行草稿表示" and "轻量顺序头：只补块内依赖"; [S] "设计"):
+ *   z_l   = RMSNorm(H[b,l] + depth_emb[l]; feat_norm), l < m: m sequence slots
+ *   x_0   = tok_emb[anchor_ids[b]],  x_k = ph_emb (k = 1..K); local positions
+ *           0 for every z_l and the anchor, k for placeholder k
+ *   n_layers pre-norm layers: non-causal grouped attention of the 1 + K local
+ *           rows over all m + 1 + K slots with RoPE (rotate-half), then SwiGLU;
+ *           context slots only provide keys and values
+ *   h_k   = RMSNorm(x_k; final_norm)
+ *   s_0 = 0, s_k = s_{k-1} + seq_w_up silu(seq_w_down [h_k; s_{k-1}])
+ *   candidates[b, k-1] = argmax_v (lm_head s_k)_v, lowest index on ties
+ *
+ * features    [B, m, D] (dtype)       target hidden states at the pivot position
+ * anchor_ids  [B] int32                ids in [0, V); an out-of-range id gives a
+ *                                      zero anchor embedding and candidates -1
+ * candidates  [B, K] int32 (out)
+ * max_logit   [B, K] fp32 (out, may be NULL): the winning logit
+ * taps        may be NULL
+ * workspace   device buffer of at least dlite_workspace_bytes(dims) bytes,
+ *             256-byte aligned; contents on entry are ignored
+ * stream      HIP stream (0 = default stream)
+ */
+int dlite_draft_block(const dlite_dims *dims, const dlite_weights *weights,
+                      const void *features, const int32_t *anchor_ids,
+                      int32_t *candidates, float *max_logit,
+                      const dlite_taps *taps, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dlite_accept_prefix — greedy verification of one round.
+ *
+ * [W] "一次因果前向评估整条候选": only the leading run of matches is committed.
+ * [W] "一轮执行后，缓存、锚点与隐藏状态怎样对齐": the next anchor (the
+ * correction, or the bonus token when all K pass) is the target token at verify
+ * index A.  A round commits A + 1 tokens ([W] "先拆开一次投机轮次的时间").
+ *
+ * candidates    [B, K] int32    draft tokens d_1..d_K
+ * target_tokens [B, K + 1] int32 target greedy token at each verify input
+ *                               [a, d_1, .., d_K]
+ * accept_len    [B] int32 (out)  A = number of leading i with
+ *                               candidates[b, i] == target_tokens[b, i], 0..K
+ * next_anchor   [B] int32 (out, may be NULL)  target_tokens[b, A]
+ * Integer only; bit-exact.  B in 1 .. 2^24, K in 1 .. 64.
+ */
+int dlite_accept_prefix(const int32_t *candidates, const int32_t *target_tokens,
+                        int32_t B, int32_t K, int32_t *accept_len,
+                        int32_t *next_anchor, hipStream_t stream);
+
+/* Message describing the calling thread's last error ("" if none). */
+const char *dlite_last_error(void);
+
+/* Library version string. */
+const char *dlite_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLITE_H */

