@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of the DLite draft step + greedy prefix accept on one MI355X.
+
+One step = dlite_draft_block (feature slots -> backbone -> sequential head ->
+vocabulary GEMM + argmax) followed by dlite_accept_prefix, for one batch of
+synthetic, seeded inputs already resident in HBM.  The value is drafted tokens
+per second (B*K per step).  Weights are rotated over several device copies so
+that no step finds its weights in the 256 MB last-level cache (MALL) left
+behind by the previous step.
+
+Prints one JSON line.  Also reports, for the dominant kernel, the achieved
+bandwidth (or MFMA rate) from HIP events recorded around it on the library's
+stream during the timed steps, and the fp64 CPU oracle's throughput on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16
+METRIC = "drafted tokens/s (B·K) for drafter+accept at Qwen3-8B shapes; % HBM/MFMA peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="qwen3_8b_b1")
+    p.add_argument("--copies", type=int, default=3, help="weight copies rotated over steps")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="time budget of the CPU oracle baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--stages", action="store_true", help="also time every stage separately")
+    return p.parse_args()
+
+
+# ------------------------------------------------------- algorithmic costs ---
+
+def stage_costs(w):
+    """Algorithmic HBM bytes and flops per stage (each weight read once; token
+    table: B rows; activations counted once in and once out)."""
+    e = 2 if w.dtype == "bf16" else 4
+    B, m, K, D, F, r, V = w.B, w.m, w.K, w.D, w.ffn, w.rank, w.vocab
+    S, L = m + 1 + K, 1 + K
+    Hq, Hkv = w.n_q * w.d_h, w.n_kv * w.d_h
+    c = {k: [0.0, 0.0] for k in ("features", "qkv", "attention", "oproj", "gate_up", "down",
+                                  "final_norm", "seq_proj", "scan", "lm_head")}
+    c["features"] = [B * m * D * e + m * D * e + D * e + B * D * e + D * e + B * S * D * 4, 0.0]
+    for l in range(w.n_layers):
+        Lr = L - 1 if l == w.n_layers - 1 else L
+        c["qkv"][0] += (Hq + 2 * Hkv) * D * e + D * e + B * S * D * 4 + B * (Lr * Hq + S * 2 * Hkv) * 4
+        c["qkv"][1] += 2.0 * D * (B * Lr * Hq + B * S * 2 * Hkv)
+        c["attention"][0] += B * (Lr * Hq + S * 2 * Hkv) * 4 + B * Lr * Hq * e
+        c["attention"][1] += 4.0 * B * Lr * S * Hq
+        c["oproj"][0] += D * Hq * e + B * Lr * Hq * e + 2 * B * Lr * D * 4
+        c["oproj"][1] += 2.0 * B * Lr * Hq * D
+        c["gate_up"][0] += 2 * F * D * e + D * e + B * Lr * D * 4 + B * Lr * F * e
+        c["gate_up"][1] += 2.0 * B * Lr * D * 2 * F
+        c["down"][0] += D * F * e + B * Lr * F * e + 2 * B * Lr * D * 4
+        c["down"][1] += 2.0 * B * Lr * F * D
+    c["final_norm"] = [B * K * D * 4 + D * e + B * K * D * e, 0.0]
+    c["seq_proj"] = [r * D * e + B * K * D * e + B * K * r * 4, 2.0 * B * K * D * r]
+    c["scan"] = [2 * r * r * e + B * K * r * (4 + 4 + e), 4.0 * B * K * r * r]
+    c["lm_head"] = [V * r * e + B * K * r * e + B * K * 8, 2.0 * B * K * r * V]
+    return c
+
+
+def step_costs(w):
+    c = stage_costs(w)
+    by = sum(v[0] for v in c.values()) + w.B * (w.K + (w.K + 1) + 2) * 4  # + accept
+    fl = sum(v[1] for v in c.values())
+    return by, fl
+
+
+# ----------------------------------------------------------------- HIP events ---
+
+class HipEvents:
+    """Raw HIP events (recorded by the library on its own stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+# ------------------------------------------------------------- CPU baseline ---
+
+def cpu_baseline(w, weights, H, anchors, budget_s):
+    """The fp64 oracle timed on the host cores on a bounded sample."""
+    import oracle
+    from synth import as_f64, make_target_tokens
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    Wf = {k: as_f64(v) for k, v in weights.items() if k not in ("layers", "tok_emb")}
+    Wf["layers"] = [{k: as_f64(v) for k, v in lw.items()} for lw in weights["layers"]]
+    Hf, rows = as_f64(H), as_f64(weights["tok_emb"][anchors])
+    ref, tgt = None, None
+    n, t0 = 0, time.perf_counter()
+    while True:
+        ref = oracle.draft_block(w, Wf, Hf, rows)
+        if tgt is None:
+            tgt = make_target_tokens(w, ref["cand"])
+        oracle.accept_prefix(ref["cand"], tgt)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 50:
+            break
+    value = n * w.B * w.K / el
+    res = {"value": value, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{n} full draft+accept step(s) of {w.name} (B={w.B}), fp64 numpy, "
+                     f"{el:.1f} s"}
+    return res, ref, tgt
+
+
+# --------------------------------------------------------------------- main ---
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the draft step "
+              f"shards by request across GPUs with no collective, which is not built here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from history_free_drafter_amd import binding as B
+    from history_free_drafter_amd.runtime import DraftModel, to_device
+    from synth import (WORKLOADS, make_anchors, make_features, make_target_tokens,
+                       make_weights)
+
+    w = WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    weights = make_weights(w)
+    H, anchors = make_features(w), make_anchors(w)
+
+    cpu, ref, tgt = None, None, None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        cpu, ref, tgt = cpu_baseline(w, weights, H, anchors, args.cpu_seconds)
+    else:
+        rng = np.random.default_rng(0)
+        tgt = make_target_tokens(w, rng.integers(0, w.vocab, size=(w.B, w.K)))
+
+    dims = dict(B=w.B, m=w.m, D=w.D, n_layers=w.n_layers, n_q=w.n_q, n_kv=w.n_kv,
+                d_h=w.d_h, ffn=w.ffn, K=w.K, rank=w.rank, vocab=w.vocab, dtype=w.dtype,
+                rms_eps=w.rms_eps, rope_theta=w.rope_theta)
+    print("[bench] uploading", file=sys.stderr, flush=True)
+    model = DraftModel(dims, weights, "cuda")
+    del weights
+    # extra weight copies (token table shared: only B rows of it are read)
+    copies = [model.wstruct]
+    keep = []
+    for _ in range(max(0, args.copies - 1)):
+        wc = {k: (v.clone() if isinstance(v, torch.Tensor) and k != "tok_emb" else v)
+              for k, v in model.w.items() if k != "layers"}
+        wc["layers"] = [{k: v.clone() for k, v in lw.items()} for lw in model.w["layers"]]
+        s, k = B.make_weights(wc)
+        copies.append(s)
+        keep.append((wc, k))
+    Hd = to_device(H, "cuda")
+    ad = torch.from_numpy(anchors).cuda()
+    td = torch.from_numpy(tgt).cuda()
+    torch.cuda.synchronize()
+
+    costs = stage_costs(w)
+    # dominant kernel: the stage with the largest algorithmic time at peak
+    def t_roof(s):
+        return max(costs[s][0] / HBM_PEAK, costs[s][1] / MFMA_BF16_PEAK)
+    dom = max(costs, key=t_roof)
+    ev = HipEvents()
+
+    def step(i):
+        model.draft(Hd, ad, weights=copies[i % len(copies)])
+        model.accept(td)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0.record()
+    for i in range(args.steps):
+        B.dlite_set_stage_events(dom, pairs[i][0], pairs[i][1])
+        step(i)
+    g1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.dlite_set_stage_events(0, None, None)
+    wall_s = t1 - t0
+    gpu_ms = g0.elapsed_time(g1)
+    kern_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    ms_per_step = 1e3 * wall_s / args.steps
+    value = w.B * w.K / (wall_s / args.steps)
+    k_avg = float(np.mean(kern_ms)) * 1e-3
+    bound = "hbm" if costs[dom][0] / HBM_PEAK >= costs[dom][1] / MFMA_BF16_PEAK else "mfma"
+    if bound == "hbm":
+        achieved, peak, unit = costs[dom][0] / k_avg / 1e9, HBM_PEAK / 1e9, "GB/s"
+    else:
+        achieved, peak, unit = costs[dom][1] / k_avg / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
+    sb, sf = step_costs(w)
+    step_s = wall_s / args.steps
+
+    stages = None
+    if args.stages:
+        stages = {}
+        for si, name in enumerate(B.STAGES):
+            ps = [(ev.create(), ev.create()) for _ in range(20)]
+            for i, (a, b) in enumerate(ps):
+                B.dlite_set_stage_events(si, a, b)
+                step(i)
+            torch.cuda.synchronize()
+            B.dlite_set_stage_events(0, None, None)
+            stages[name] = round(1e3 * float(np.mean([ev.elapsed_ms(a, b) for a, b in ps])), 2)
+            for a, b in ps:
+                ev.destroy(a)
+                ev.destroy(b)
+
+    # tau-hat of the accepted prefixes and spot parity of the last step's tokens
+    A = model.accept_len.cpu().numpy()
+    cand = model.candidates.cpu().numpy()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) features, N(0,0.02) weights)",
+        "config": {"workload": w.name, "B": w.B, "m": w.m, "D": w.D, "n_layers": w.n_layers,
+                   "heads": f"{w.n_q}q/{w.n_kv}kv x{w.d_h}", "ffn": w.ffn, "K": w.K,
+                   "rank": w.rank, "vocab": w.vocab, "weight_copies": len(copies),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": bound, "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": None, "avg_launch_us": round(k_avg * 1e6, 2),
+                     "algorithmic_bytes": int(costs[dom][0]),
+                     "algorithmic_flops": int(costs[dom][1])},
+        "cpu_baseline": cpu,
+        "step": {"algorithmic_bytes": int(sb), "algorithmic_flops": int(sf),
+                 "hbm_frac": round(sb / step_s / HBM_PEAK, 4),
+                 "mfma_frac": round(sf / step_s / MFMA_BF16_PEAK, 4),
+                 "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4)},
+        "tau_hat_last_step": float(np.mean(A + 1)),
+    }
+    if ref is not None:
+        clear = ref["margin"] >= 1e-2
+        out["parity_tokens_clear_margin"] = float((cand == ref["cand"])[clear].mean()) if clear.any() else None
+    if stages is not None:
+        out["stages_us"] = stages
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

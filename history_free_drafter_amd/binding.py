@@ -18,7 +18,9 @@ DLITE_F32, DLITE_BF16 = 0, 1
 ERRORS = {-1: "DLITE_ERR_NULL", -2: "DLITE_ERR_SHAPE", -3: "DLITE_ERR_DTYPE",
           -4: "DLITE_ERR_WORKSPACE", -5: "DLITE_ERR_UNSUPPORTED", -6: "DLITE_ERR_HIP"}
 EXPORTS = ["dlite_workspace_bytes", "dlite_draft_block", "dlite_accept_prefix",
-           "dlite_last_error", "dlite_version"]
+           "dlite_set_stage_events", "dlite_last_error", "dlite_version"]
+STAGES = ["features", "qkv", "attention", "oproj", "gate_up", "down", "final_norm",
+          "seq_proj", "scan", "lm_head"]
 
 
 class DliteDims(Structure):
@@ -69,6 +71,8 @@ def load_library(path: str = LIB_PATH):
     lib.dlite_accept_prefix.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                         c_void_p, c_void_p]
     lib.dlite_accept_prefix.restype = c_int
+    lib.dlite_set_stage_events.argtypes = [c_int, c_void_p, c_void_p]
+    lib.dlite_set_stage_events.restype = c_int
     lib.dlite_last_error.argtypes = []
     lib.dlite_last_error.restype = c_char_p
     lib.dlite_version.argtypes = []
@@ -154,6 +158,13 @@ def dlite_accept_prefix(candidates, target_tokens, B, K, accept_len, next_anchor
                                             _ptr(accept_len), _ptr(next_anchor),
                                             _stream(stream))
     _check(rc)
+
+
+def dlite_set_stage_events(stage, before, after):
+    """Record HIP events around one stage of later draft calls (None, None: off)."""
+    if isinstance(stage, str):
+        stage = STAGES.index(stage)
+    _check(load_library().dlite_set_stage_events(stage, before, after))
 
 
 def dlite_version() -> str:

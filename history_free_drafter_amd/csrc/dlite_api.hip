@@ -15,6 +15,18 @@ namespace {
 
 thread_local std::string g_err;
 
+struct StageEvents {
+  int stage = -1;
+  hipEvent_t before = nullptr, after = nullptr;
+};
+thread_local StageEvents g_ev;
+
+// Records the instrumentation event for `stage` (layer 0 for per-layer stages).
+hipError_t mark(int stage, bool begin, hipStream_t st, int layer = 0) {
+  if (g_ev.stage != stage || layer != 0) return hipSuccess;
+  return hipEventRecord(begin ? g_ev.before : g_ev.after, st);
+}
+
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -35,7 +47,7 @@ size_t esize(const dlite_dims& d) { return d.dtype == DLITE_BF16 ? 2 : 4; }
 
 // Workspace regions, each 256-byte aligned.
 struct Plan {
-  size_t counters, X, Q, KV, AO, ACT, Hn, P, U, Sf, Sb, pmax, pidx, total;
+  size_t counters, X, XB, XF, SSQ, Q, KV, AO, ACT, P, U, Sf, Sb, pmax, pidx, total;
   int G;
 };
 
@@ -49,15 +61,17 @@ Plan make_plan(const dlite_dims& d) {
   p.G = lmhead_groups(d.vocab);
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
-  p.counters = take(CNT_COUNT * sizeof(unsigned));
+  p.counters = take(counter_words() * sizeof(unsigned));
   p.X = take(B * S * D * 4);
+  p.XB = take((d.n_layers + 1) * B * S * D * es);
+  p.XF = take(B * L * D * es);
+  p.SSQ = take(B * S * kSsqParts * 4);
   p.Q = take(B * L * Hq * 4);
   p.KV = take(B * S * 2 * Hkv * 4);
   p.AO = take(B * L * Hq * es);
   p.ACT = take(B * L * F * es);
-  p.Hn = take(B * K * D * es);
   p.P = take(B * K * r * 4);
-  p.U = take(B * r * 4);
+  p.U = take(scan_scratch_floats(d.B, d.rank) * 4);
   p.Sf = take(B * K * r * 4);
   p.Sb = take(B * K * r * es);
   p.pmax = take(B * K * static_cast<size_t>(p.G) * 4);
@@ -90,6 +104,15 @@ int check_dims(const dlite_dims* dp) {
   if (d.rank < 32 || d.rank % 32 || d.rank > rmax)
     return fail(DLITE_ERR_SHAPE, "rank=%d must be a multiple of 32 in [32, %d]", d.rank, rmax);
   if (d.vocab < 1 || d.vocab > (1 << 30)) return fail(DLITE_ERR_SHAPE, "vocab=%d not in [1, 2^30]", d.vocab);
+  if (d.D > 8 * 256 * (d.dtype == DLITE_BF16 ? 8 : 4))
+    return fail(DLITE_ERR_UNSUPPORTED, "D=%d too large for the feature kernel", d.D);
+  {
+    AttnArgs aa{};
+    aa.n_q = d.n_q; aa.n_kv = d.n_kv; aa.m = d.m; aa.K = d.K; aa.d_h = d.d_h;
+    if (attention_smem(aa) > 160 * 1024)
+      return fail(DLITE_ERR_UNSUPPORTED, "attention block too large for LDS (m=%d, K=%d, n_q/n_kv=%d)",
+                  d.m, d.K, d.n_q / d.n_kv);
+  }
   if (!(d.rms_eps >= 0.f) || !std::isfinite(d.rms_eps))
     return fail(DLITE_ERR_SHAPE, "rms_eps must be finite and >= 0");
   if (!(d.rope_theta > 0.f) || !std::isfinite(d.rope_theta))
@@ -125,6 +148,19 @@ const char* at(const void* base, size_t bytes) { return static_cast<const char*>
 extern "C" {
 
 const char* dlite_last_error(void) { return g_err.c_str(); }
+
+int dlite_set_stage_events(int stage, hipEvent_t before, hipEvent_t after) {
+  if (!before && !after) {
+    g_ev = StageEvents{};
+    return ok();
+  }
+  if (!before || !after) return fail(DLITE_ERR_NULL, "both events are needed");
+  if (stage < 0 || stage >= DLITE_NUM_STAGES) return fail(DLITE_ERR_SHAPE, "unknown stage %d", stage);
+  g_ev.stage = stage;
+  g_ev.before = before;
+  g_ev.after = after;
+  return ok();
+}
 
 const char* dlite_version(void) { return "dlite-mi355x 0.1 (gfx950)"; }
 
@@ -173,26 +209,40 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   const size_t es = esize(d);
   const int B = d.B, m = d.m, K = d.K, D = d.D, S = m + 1 + K, L = 1 + K;
   const int Hq = d.n_q * d.d_h, Hkv = d.n_kv * d.d_h, F = d.ffn, r = d.rank;
-  unsigned* counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + p.counters);
-  float* X = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.X);
-  float* Qb = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.Q);
-  float* KVb = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.KV);
-  void* AO = static_cast<char*>(workspace) + p.AO;
-  void* ACT = static_cast<char*>(workspace) + p.ACT;
-  void* Hn = static_cast<char*>(workspace) + p.Hn;
-  float* P = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.P);
-  float* U = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.U);
-  float* Sf = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.Sf);
-  void* Sb = static_cast<char*>(workspace) + p.Sb;
-  float* pmax = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.pmax);
-  int* pidx = reinterpret_cast<int*>(static_cast<char*>(workspace) + p.pidx);
+  char* ws = static_cast<char*>(workspace);
+  unsigned* counters = reinterpret_cast<unsigned*>(ws + p.counters);
+  float* X = reinterpret_cast<float*>(ws + p.X);
+  char* XB = ws + p.XB;                      // [n_layers + 1][B S, D] GEMM inputs
+  void* XF = ws + p.XF;                      // [B L, D] FFN inputs
+  float* SSQ = reinterpret_cast<float*>(ws + p.SSQ);
+  float* Qb = reinterpret_cast<float*>(ws + p.Q);
+  float* KVb = reinterpret_cast<float*>(ws + p.KV);
+  void* AO = ws + p.AO;
+  void* ACT = ws + p.ACT;
+  float* P = reinterpret_cast<float*>(ws + p.P);
+  float* U = reinterpret_cast<float*>(ws + p.U);
+  float* Sf = reinterpret_cast<float*>(ws + p.Sf);
+  void* Sb = ws + p.Sb;
+  float* pmax = reinterpret_cast<float*>(ws + p.pmax);
+  int* pidx = reinterpret_cast<int*>(ws + p.pidx);
   const dlite_taps no_taps{};
   const dlite_taps& tp = taps ? *taps : no_taps;
+  const size_t xb_layer = static_cast<size_t>(B) * S * D * es;
+  const int G_rows = D < kSsqParts ? D : kSsqParts;   // workgroups of a D-row GEMM
 
-  // 1. feature slots, anchor and placeholder rows (also clears the counters)
-  FeatureArgs fa{features, w->depth_emb, w->feat_norm, w->tok_emb, w->ph_emb, anchor_ids,
-                 X, tp.z, counters, B, m, K, D, d.vocab, d.rms_eps};
+  // 1. feature slots, anchor and placeholder rows, first GEMM inputs
+  //    (also clears the counters)
+  FeatureArgs fa{};
+  fa.H = features; fa.depth_emb = w->depth_emb; fa.feat_norm = w->feat_norm;
+  fa.tok_emb = w->tok_emb; fa.ph_emb = w->ph_emb;
+  for (int l = 0; l < d.n_layers; ++l) fa.attn_norm[l] = w->layers[l].attn_norm;
+  fa.anchors = anchor_ids; fa.X = X; fa.XB = XB; fa.ssq = SSQ; fa.tap_z = tp.z;
+  fa.counters = counters; fa.n_counters = counter_words();
+  fa.B = B; fa.m = m; fa.K = K; fa.D = D; fa.V = d.vocab; fa.n_layers = d.n_layers;
+  fa.eps = d.rms_eps;
+  DLITE_LAUNCH(mark(DLITE_STAGE_FEATURES, true, st));
   DLITE_LAUNCH(launch_feature(fa, bf16, st));
+  DLITE_LAUNCH(mark(DLITE_STAGE_FEATURES, false, st));
 
   // 2. backbone layers
   for (int l = 0; l < d.n_layers; ++l) {
@@ -201,62 +251,92 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
     const int q0 = (l == d.n_layers - 1) ? 1 : 0;
     const int Lr = L - q0;
     const RowMap slot_rows{Lr, S, m + q0}, local_rows{Lr, L, q0}, all_slots{S, S, 0};
+    const void* xb = XB + l * xb_layer;
+    // local rows of layer 0 come from the feature kernel (one part), later
+    // layers from the previous down projection (G_rows parts)
+    const int np_local = l == 0 ? 1 : G_rows;
 
     GemmArgs q{};
     q.W = lw.wqkv; q.ldw = D; q.N = Hq; q.K = D;
-    q.src = X; q.src_f32 = 1; q.ld_src = D; q.smap = slot_rows; q.M = B * Lr;
-    q.gain = lw.attn_norm; q.eps = d.rms_eps;
+    q.src = xb; q.ld_src = D; q.smap = slot_rows; q.M = B * Lr;
+    q.ssq = SSQ; q.qmap = slot_rows; q.ssq_group = S; q.ssq_split = m; q.np_lo = 1;
+    q.np_hi = np_local; q.norm_len = D; q.eps = d.rms_eps;
     q.out = Qb; q.ld_out = Hq; q.omap = local_rows;
+    DLITE_LAUNCH(mark(DLITE_STAGE_QKV, true, st, l));
     DLITE_LAUNCH(launch_gemm(q, EPI_STORE_F32, bf16, st));
 
-    GemmArgs kv{};
-    kv.W = at(lw.wqkv, static_cast<size_t>(Hq) * D * es); kv.ldw = D; kv.N = 2 * Hkv; kv.K = D;
-    kv.src = X; kv.src_f32 = 1; kv.ld_src = D; kv.smap = all_slots; kv.M = B * S;
-    kv.gain = lw.attn_norm; kv.eps = d.rms_eps;
+    GemmArgs kv = q;
+    kv.W = at(lw.wqkv, static_cast<size_t>(Hq) * D * es); kv.N = 2 * Hkv;
+    kv.smap = all_slots; kv.qmap = all_slots; kv.M = B * S;
     kv.out = KVb; kv.ld_out = 2 * Hkv; kv.omap = all_slots;
     DLITE_LAUNCH(launch_gemm(kv, EPI_STORE_F32, bf16, st));
+    DLITE_LAUNCH(mark(DLITE_STAGE_QKV, false, st, l));
 
     AttnArgs aa{Qb, KVb, AO, B, m, K, d.n_q, d.n_kv, d.d_h, q0, d.rope_theta};
+    DLITE_LAUNCH(mark(DLITE_STAGE_ATTENTION, true, st, l));
     DLITE_LAUNCH(launch_attention(aa, bf16, st));
+    DLITE_LAUNCH(mark(DLITE_STAGE_ATTENTION, false, st, l));
 
     GemmArgs o{};
     o.W = lw.wo; o.ldw = Hq; o.N = D; o.K = Hq;
-    o.src = AO; o.src_f32 = 0; o.ld_src = Hq; o.smap = local_rows; o.M = B * Lr;
+    o.src = AO; o.ld_src = Hq; o.smap = local_rows; o.M = B * Lr;
     o.out = X; o.ld_out = D; o.omap = slot_rows;
+    o.next_gain = lw.ffn_norm; o.xb_out = XF; o.ld_xb = D; o.xmap = local_rows; o.ssq_out = SSQ;
+    DLITE_LAUNCH(mark(DLITE_STAGE_OPROJ, true, st, l));
     DLITE_LAUNCH(launch_gemm(o, EPI_RESID, bf16, st));
+    DLITE_LAUNCH(mark(DLITE_STAGE_OPROJ, false, st, l));
 
     GemmArgs gu{};
     gu.W = lw.w_gate_up; gu.ldw = D; gu.N = F; gu.K = D; gu.pair_off = F;
-    gu.src = X; gu.src_f32 = 1; gu.ld_src = D; gu.smap = slot_rows; gu.M = B * Lr;
-    gu.gain = lw.ffn_norm; gu.eps = d.rms_eps;
+    gu.src = XF; gu.ld_src = D; gu.smap = local_rows; gu.M = B * Lr;
+    gu.ssq = SSQ; gu.qmap = slot_rows; gu.ssq_group = S; gu.ssq_split = 0; gu.np_lo = G_rows;
+    gu.np_hi = G_rows; gu.norm_len = D; gu.eps = d.rms_eps;
     gu.out = ACT; gu.ld_out = F; gu.omap = local_rows;
+    DLITE_LAUNCH(mark(DLITE_STAGE_GATE_UP, true, st, l));
     DLITE_LAUNCH(launch_gemm(gu, EPI_SWIGLU, bf16, st));
+    DLITE_LAUNCH(mark(DLITE_STAGE_GATE_UP, false, st, l));
 
     GemmArgs dn{};
     dn.W = lw.w_down; dn.ldw = F; dn.N = D; dn.K = F;
-    dn.src = ACT; dn.src_f32 = 0; dn.ld_src = F; dn.smap = local_rows; dn.M = B * Lr;
+    dn.src = ACT; dn.ld_src = F; dn.smap = local_rows; dn.M = B * Lr;
     dn.out = X; dn.ld_out = D; dn.omap = slot_rows;
+    dn.next_gain = (l + 1 < d.n_layers) ? w->layers[l + 1].attn_norm : w->final_norm;
+    dn.xb_out = XB + (l + 1) * xb_layer; dn.ld_xb = D; dn.xmap = slot_rows; dn.ssq_out = SSQ;
     if (tp.x) {
       dn.tap = tp.x + static_cast<size_t>(l) * B * L * D;
       dn.ld_tap = D; dn.tmap = local_rows;
     }
+    DLITE_LAUNCH(mark(DLITE_STAGE_DOWN, true, st, l));
     DLITE_LAUNCH(launch_gemm(dn, EPI_RESID, bf16, st));
+    DLITE_LAUNCH(mark(DLITE_STAGE_DOWN, false, st, l));
   }
 
-  // 3. final norm of the placeholder rows
-  NormArgs na{X, w->final_norm, Hn, tp.hidden, B, m, K, D, d.rms_eps};
-  DLITE_LAUNCH(launch_final_norm(na, bf16, st));
+  // 3. final RMSNorm: folded into the down projection (pre-gained rows and
+  //    partial sums of squares) and the next GEMM's epilogue; fp32 copy on request
+  DLITE_LAUNCH(mark(DLITE_STAGE_FINAL_NORM, true, st));
+  if (tp.hidden) {
+    NormArgs na{X, w->final_norm, tp.hidden, B, m, K, D, d.rms_eps};
+    DLITE_LAUNCH(launch_hidden_tap(na, bf16, st));
+  }
+  DLITE_LAUNCH(mark(DLITE_STAGE_FINAL_NORM, false, st));
 
   // 4. hidden part of the sequential head's input projection, all B*K rows at once
+  const RowMap ph_rows{K, S, m + 1};
   GemmArgs ph{};
   ph.W = w->seq_w_down; ph.ldw = static_cast<long>(D) + r; ph.N = r; ph.K = D;
-  ph.src = Hn; ph.src_f32 = 0; ph.ld_src = D; ph.smap = RowMap{K, K, 0}; ph.M = B * K;
+  ph.src = XB + d.n_layers * xb_layer; ph.ld_src = D; ph.smap = ph_rows; ph.M = B * K;
+  ph.ssq = SSQ; ph.qmap = ph_rows; ph.ssq_group = S; ph.ssq_split = 0; ph.np_lo = G_rows;
+  ph.np_hi = G_rows; ph.norm_len = D; ph.eps = d.rms_eps;
   ph.out = P; ph.ld_out = r; ph.omap = RowMap{K, K, 0};
+  DLITE_LAUNCH(mark(DLITE_STAGE_SEQ_PROJ, true, st));
   DLITE_LAUNCH(launch_gemm(ph, EPI_STORE_F32, bf16, st));
+  DLITE_LAUNCH(mark(DLITE_STAGE_SEQ_PROJ, false, st));
 
   // 5. the K-step recurrence
-  ScanArgs sa{P, w->seq_w_down, w->seq_w_up, U, Sf, Sb, tp.state, counters, B, K, D, r};
+  ScanArgs sa{P, w->seq_w_down, w->seq_w_up, U, Sf, Sb, tp.state, counters, B, K, D, r, 0u, 0};
+  DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
   DLITE_LAUNCH(launch_scan(sa, bf16, st));
+  DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st));
 
   // 6. vocabulary projection + argmax
   LmArgs la{};
@@ -264,7 +344,9 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   la.part_max = pmax; la.part_idx = pidx; la.G = p.G;
   la.cand = candidates; la.max_logit = max_logit; la.tap = tp.logits;
   la.anchors = anchor_ids; la.K = K; la.counters = counters;
+  DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, true, st));
   DLITE_LAUNCH(launch_lmhead(la, bf16, st));
+  DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, false, st));
   return ok();
 }
 

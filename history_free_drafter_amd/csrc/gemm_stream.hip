@@ -1,35 +1,43 @@
 // Weight-streaming GEMM for few activation rows (M <= 32 per launch).
 //
 // In the small-batch draft step every linear map is read-bound: each weight
-// byte is used by at most 32 token rows.  The kernel therefore streams each
-// weight row exactly once from HBM straight into registers (16 bytes per lane,
-// no LDS staging) and feeds it to 16x16 MFMA tiles whose other operand is the
-// token block, built in registers from the activation rows (L2-resident).
+// byte meets at most 32 token rows.  Each weight row is therefore streamed
+// once from HBM straight into registers (16 bytes per lane, non-temporal) and
+// fed to 16x16 MFMA tiles; the other operand, the token block, is read from
+// the (L2-resident) activation rows alongside.  Workgroup g owns logical output
+// rows [g N / G, (g+1) N / G) in 16-row tiles; its waves split K.  Each wave
+// walks (tile, k-chunk) units through a two-stage register pipeline, so the
+// loads of the next unit are in flight while the current one is multiplied.
+// Partial tiles are summed through LDS in a fixed order (deterministic).
 //
-// Work split: workgroup g owns logical output rows [g N / G, (g+1) N / G) in
-// 16-row tiles; its waves split the K dimension, and partial tiles are summed
-// through LDS in a fixed order (deterministic).  An optional RMSNorm prologue
-// multiplies inputs by the gain while the waves accumulate each row's sum of
-// squares; the 1/rms factor is applied to the finished dot products, which is
-// exact algebra (the factor is constant along k).
+// Inputs are pre-gained rows bf16(gamma * x) written by the producing kernel;
+// when the map is preceded by an RMSNorm, each token's 1/rms is rebuilt from
+// the producer's partial sums of squares and applied to the finished dot
+// products (the factor is constant along k, so this is exact algebra).
 #include "kernels.hpp"
 
 namespace dlite {
 
 namespace {
 
-constexpr int kMaxWaves = 8;
-constexpr int kMaxTiles = 4;    // 16-row tiles per workgroup
-constexpr int kChunk = 8;       // k-steps held in registers at once
+template <typename T, int NP, int MT, int NS>
+struct Stage {
+  uint4 a[NP][NS];
+  uint4 b[MT][NS];
+};
 
-template <typename T, int MT, int EPI, bool NORM>
+// BL: the token rows are staged once in LDS (row stride K + 8 elements keeps
+// 16-byte alignment and spreads banks) and every wave reads its fragments
+// from there; otherwise fragments are loaded per unit from global memory.
+template <typename T, int MT, int NS, int EPI, bool BL>
 __global__ __launch_bounds__(512) void gemm_stream_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) unsigned char bsm[];
   constexpr int PER = Elem<T>::kPerLane;
   constexpr int KS = PER * 4;                        // k per MFMA step
   constexpr int NP = (EPI == EPI_SWIGLU) ? 2 : 1;    // gate/up pairs
 
-  __shared__ float red[2][kMaxWaves * NP * MT * 256];
-  __shared__ float ssq_part[kMaxWaves][32];
+  // per tile: nwaves * NP * MT * 256 partials, nwaves <= 8
+  __shared__ float red[2][8 * NP * MT * 256];
   __shared__ float inv_rms[32];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -43,143 +51,142 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GemmArgs a) {
 
   const int nsteps = a.K / KS;
   const int s0 = (wave * nsteps) / nwaves, s1 = ((wave + 1) * nsteps) / nwaves;
+  const int per_max = (nsteps + nwaves - 1) / nwaves;
+  const int nchunk = (per_max + NS - 1) / NS;        // same for every wave
+  const int nunit = ntile * nchunk;
 
   const T* W = static_cast<const T*>(a.W);
-  const T* gain = static_cast<const T*>(a.gain);
+  const T* X = static_cast<const T*>(a.src);
 
-  floatx4 acc[kMaxTiles][NP][MT];
-#pragma unroll
-  for (int t = 0; t < kMaxTiles; ++t)
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int u = 0; u < MT; ++u) acc[t][p][u] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float ssq[MT];
-#pragma unroll
-  for (int u = 0; u < MT; ++u) ssq[u] = 0.f;
-
-  // physical source rows of this lane's tokens
+  // token rows of this lane (invalid tokens read token 0's row, masked later)
   long srow[MT];
   bool tok_ok[MT];
 #pragma unroll
   for (int u = 0; u < MT; ++u) {
     const int tok = u * 16 + c16;
     tok_ok[u] = tok < a.M;
-    srow[u] = tok_ok[u] ? a.smap.row(a.tok0 + tok) : 0;
+    srow[u] = a.smap.row(a.tok0 + (tok_ok[u] ? tok : 0));
   }
 
-  for (int c0 = s0; c0 < s1; c0 += kChunk) {
-    // token block for this chunk of k-steps
-    uint4 b[MT][kChunk];
+  const int ldb = a.K + 8;
+  const T* Bs = reinterpret_cast<const T*>(bsm);
+  if (BL) {
+    // stage the M real token rows: 16-byte loads, all issued before the stores
+    T* bw = reinterpret_cast<T*>(bsm);
+    const int vk = a.K / PER, nv = a.M * vk;
+    for (int base = threadIdx.x; base < nv; base += 8 * blockDim.x) {
+      uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      const int s = c0 + i;
-      const int k = s * KS + grp * PER;
-      float gv[PER];
-      if (NORM && s < s1) {
-        load16_f32(gain + k, gv);
+      for (int q = 0; q < 8; ++q) {
+        int idx = base + q * blockDim.x;
+        idx = idx < nv ? idx : nv - 1;   // clamped: every load is issued unconditionally
+        v[q] = *reinterpret_cast<const uint4*>(X + a.smap.row(a.tok0 + idx / vk) * a.ld_src +
+                                               (idx % vk) * PER);
       }
 #pragma unroll
-      for (int u = 0; u < MT; ++u) {
-        float v[PER];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) v[e] = 0.f;
-        if (s < s1 && tok_ok[u]) {
-          if (a.src_f32) {
-            const float* sp = static_cast<const float*>(a.src) + srow[u] * a.ld_src + k;
-            if constexpr (PER == 8) {
-              load16_f32(sp, v);
-              load16_f32(sp + 4, v + 4);
-            } else {
-              load16_f32(sp, v);
-            }
-          } else {
-            load16_f32(static_cast<const T*>(a.src) + srow[u] * a.ld_src + k, v);
-          }
-          if (NORM) {
-#pragma unroll
-            for (int e = 0; e < PER; ++e) {
-              ssq[u] += v[e] * v[e];
-              v[e] *= gv[e];
-            }
-          }
-        }
-        b[u][i] = pack16(v, T());
+      for (int q = 0; q < 8; ++q) {
+        const int idx = base + q * blockDim.x;
+        if (idx < nv) *reinterpret_cast<uint4*>(bw + (idx / vk) * ldb + (idx % vk) * PER) = v[q];
       }
-    }
-    // stream the weight tiles of this workgroup through the MFMAs
-#pragma unroll
-    for (int t = 0; t < kMaxTiles; ++t) {
-      if (t < ntile) {
-        const int row = r0 + t * 16 + c16;
-        const bool rok = row < r1;
-        uint4 av[NP][kChunk];
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-          const int s = c0 + i;
-#pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            if (s < s1 && rok)
-              av[p][i] = ld_stream(W + (row + p * a.pair_off) * a.ldw + s * KS + grp * PER);
-            else
-              av[p][i] = make_uint4(0, 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i)
-#pragma unroll
-          for (int p = 0; p < NP; ++p)
-#pragma unroll
-            for (int u = 0; u < MT; ++u)
-              acc[t][p][u] = mma_step(av[p][i], b[u][i], acc[t][p][u], T());
-      }
-    }
-  }
-
-  if (NORM) {
-#pragma unroll
-    for (int u = 0; u < MT; ++u) {
-      float v = ssq[u];
-      v += __shfl_xor(v, 16, kWave);
-      v += __shfl_xor(v, 32, kWave);
-      if (grp == 0) ssq_part[wave][u * 16 + c16] = v;
     }
     __syncthreads();
-    if (threadIdx.x < MT * 16) {
-      float s = 0.f;
-      for (int w = 0; w < nwaves; ++w) s += ssq_part[w][threadIdx.x];
-      inv_rms[threadIdx.x] = 1.0f / sqrtf(s / static_cast<float>(a.K) + a.eps);
+  }
+
+  auto issue = [&](int p, Stage<T, NP, MT, NS>& st) {
+    const int t = p / nchunk, c = p % nchunk;
+    int row = r0 + t * 16 + c16;
+    row = row < r1 ? row : r1 - 1;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      int s = s0 + c * NS + i;
+      const int slast = s1 > 0 ? s1 - 1 : 0;
+      s = s < s1 ? s : slast;
+      const long k = static_cast<long>(s) * KS + grp * PER;
+#pragma unroll
+      for (int q = 0; q < NP; ++q) st.a[q][i] = ld_stream(W + (row + q * a.pair_off) * a.ldw + k);
+      if (!BL) {
+#pragma unroll
+        for (int u = 0; u < MT; ++u)
+          if (tok_ok[u]) st.b[u][i] = *reinterpret_cast<const uint4*>(X + srow[u] * a.ld_src + k);
+      }
+    }
+  };
+
+  floatx4 acc[NP][MT];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int u = 0; u < MT; ++u) acc[q][u] = floatx4{0.f, 0.f, 0.f, 0.f};
+  };
+  zero_acc();
+
+  auto compute = [&](int p, const Stage<T, NP, MT, NS>& st) {
+    const int c = p % nchunk;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const bool ok = s0 + c * NS + i < s1;
+#pragma unroll
+      for (int u = 0; u < MT; ++u) {
+        uint4 bv;
+        if (BL) {
+          const int s = s0 + c * NS + i;
+          const int sc = s < s1 ? s : (s1 > 0 ? s1 - 1 : 0);
+          const int tok = tok_ok[u] ? u * 16 + c16 : 0;
+          bv = *reinterpret_cast<const uint4*>(Bs + tok * ldb + sc * KS + grp * PER);
+        } else {
+          bv = st.b[u][i];
+        }
+        bv = (ok && tok_ok[u]) ? bv : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < NP; ++q) acc[q][u] = mma_step(st.a[q][i], bv, acc[q][u], T());
+      }
+    }
+  };
+
+  // 1/rms of each token from the producer's partial sums of squares
+  if (a.ssq) {
+    for (int tl = wave; tl < MT * 16; tl += nwaves) {
+      float v = 0.f;
+      if (tl < a.M) {
+        const long prow = a.qmap.row(a.tok0 + tl);
+        const int np = (prow % a.ssq_group) < a.ssq_split ? a.np_lo : a.np_hi;
+        const float* sp = a.ssq + prow * kSsqParts;
+        for (int j = lane; j < np; j += 64) v += sp[j];
+      }
+      v = wave_sum(v);
+      if (lane == 0) inv_rms[tl] = 1.0f / sqrtf(v / static_cast<float>(a.norm_len) + a.eps);
     }
   }
 
-  // cross-wave reduction and epilogue, one 16-row tile at a time
+  // per-thread running sum of squares of the updated residual rows
+  float ssq_loc = 0.f;
   const int per_wave = NP * MT * 256;
+
+  auto finish_tile = [&](int t) {
+    float* buf = red[t & 1];
 #pragma unroll
-  for (int t = 0; t < kMaxTiles; ++t) {
-    if (t < ntile) {
-      float* buf = red[t & 1];
+    for (int q = 0; q < NP; ++q)
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
+      for (int u = 0; u < MT; ++u)
 #pragma unroll
-        for (int u = 0; u < MT; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            buf[wave * per_wave + ((p * MT + u) * 4 + i) * 64 + lane] = acc[t][p][u][i];
-      __syncthreads();
-      for (int e = threadIdx.x; e < MT * 256; e += blockDim.x) {
-        // e = (token, row16) with row16 fastest so stores run along n
-        const int row16 = e & 15, tokl = e >> 4;
-        const int u = tokl >> 4, c = tokl & 15;
-        const int i = row16 & 3, gq = row16 >> 2;
-        const int ln = gq * 16 + c;
-        const int row = r0 + t * 16 + row16;
-        if (row >= r1 || tokl >= a.M) continue;
+        for (int i = 0; i < 4; ++i)
+          buf[wave * per_wave + ((q * MT + u) * 4 + i) * 64 + lane] = acc[q][u][i];
+    __syncthreads();
+    const int e = threadIdx.x;   // one (token, row) element per thread
+    if (e < MT * 256) {
+      const int row16 = e & 15, tokl = e >> 4;
+      const int u = tokl >> 4, cc = tokl & 15;
+      const int i = row16 & 3, gq = row16 >> 2;
+      const int ln = gq * 16 + cc;
+      const int row = r0 + t * 16 + row16;
+      if (row < r1 && tokl < a.M) {
         float v0 = 0.f, v1 = 0.f;
         for (int w = 0; w < nwaves; ++w) {
           v0 += buf[w * per_wave + ((0 * MT + u) * 4 + i) * 64 + ln];
           if (NP == 2) v1 += buf[w * per_wave + ((1 * MT + u) * 4 + i) * 64 + ln];
         }
-        if (NORM) {
+        if (a.ssq) {
           v0 *= inv_rms[tokl];
           v1 *= inv_rms[tokl];
         }
@@ -192,6 +199,10 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GemmArgs a) {
           float* x = static_cast<float*>(a.out) + orow * a.ld_out + row;
           const float nv = *x + v0;
           *x = nv;
+          ssq_loc += nv * nv;
+          const T* ng = static_cast<const T*>(a.next_gain);
+          static_cast<T*>(a.xb_out)[a.xmap.row(a.tok0 + tokl) * a.ld_xb + row] =
+              Elem<T>::from_f32(Elem<T>::to_f32(ng[row]) * nv);
           if (a.tap) a.tap[a.tmap.row(a.tok0 + tokl) * a.ld_tap + row] = nv;
         } else {  // SwiGLU: silu(gate) * up
           const float act = v0 / (1.0f + expf(-v0)) * v1;
@@ -199,23 +210,76 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GemmArgs a) {
         }
       }
     }
+  };
+
+  // two-stage pipeline over (tile, chunk) units
+  Stage<T, NP, MT, NS> st0, st1;
+  if (nunit > 0) issue(0, st0);
+  for (int p = 0; p < nunit; p += 2) {
+    if (p + 1 < nunit) issue(p + 1, st1);
+    compute(p, st0);
+    if (p % nchunk == nchunk - 1) { finish_tile(p / nchunk); zero_acc(); }
+    if (p + 1 < nunit) {
+      if (p + 2 < nunit) issue(p + 2, st0);
+      compute(p + 1, st1);
+      if ((p + 1) % nchunk == nchunk - 1) { finish_tile((p + 1) / nchunk); zero_acc(); }
+    }
+  }
+
+  if (EPI == EPI_RESID && a.ssq_out) {
+    // combine the 16 rows of each token (consecutive lanes), one partial per workgroup
+    float v = ssq_loc;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, kWave);
+    const int e = threadIdx.x;
+    if (e < MT * 256 && (e & 15) == 0 && (e >> 4) < a.M)
+      a.ssq_out[a.omap.row(a.tok0 + (e >> 4)) * kSsqParts + g] = v;
   }
 }
 
-template <typename T, int MT>
-hipError_t dispatch_epi(const GemmArgs& a, int epi, dim3 grid, dim3 block, hipStream_t st) {
-  const bool norm = a.gain != nullptr;
-#define DLITE_GS(E, NRM) \
-  hipLaunchKernelGGL((gemm_stream_kernel<T, MT, E, NRM>), grid, block, 0, st, a)
+template <typename T, int MT, int NS, bool BL>
+hipError_t dispatch_epi(const GemmArgs& a, int epi, dim3 grid, dim3 block, size_t sm, hipStream_t st) {
+  // the gate/up pair at 32 tokens keeps a 4-step stage (register budget)
+  constexpr int NSG = (MT == 2 && NS == 8) ? 4 : NS;
+  const void* fn = nullptr;
   switch (epi) {
-    case EPI_STORE_F32: if (norm) DLITE_GS(EPI_STORE_F32, true); else DLITE_GS(EPI_STORE_F32, false); break;
-    case EPI_STORE_ACT: if (norm) DLITE_GS(EPI_STORE_ACT, true); else DLITE_GS(EPI_STORE_ACT, false); break;
-    case EPI_RESID:     if (norm) DLITE_GS(EPI_RESID, true);     else DLITE_GS(EPI_RESID, false); break;
-    case EPI_SWIGLU:    if (norm) DLITE_GS(EPI_SWIGLU, true);    else DLITE_GS(EPI_SWIGLU, false); break;
+    case EPI_STORE_F32: fn = reinterpret_cast<const void*>(&gemm_stream_kernel<T, MT, NS, EPI_STORE_F32, BL>); break;
+    case EPI_STORE_ACT: fn = reinterpret_cast<const void*>(&gemm_stream_kernel<T, MT, NS, EPI_STORE_ACT, BL>); break;
+    case EPI_RESID:     fn = reinterpret_cast<const void*>(&gemm_stream_kernel<T, MT, NS, EPI_RESID, BL>); break;
+    case EPI_SWIGLU:    fn = reinterpret_cast<const void*>(&gemm_stream_kernel<T, MT, NSG, EPI_SWIGLU, BL>); break;
     default: return hipErrorInvalidValue;
   }
-#undef DLITE_GS
+  if (BL) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
+    if (e != hipSuccess) return e;
+  }
+  switch (epi) {
+    case EPI_STORE_F32: hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NS, EPI_STORE_F32, BL>), grid, block, sm, st, a); break;
+    case EPI_STORE_ACT: hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NS, EPI_STORE_ACT, BL>), grid, block, sm, st, a); break;
+    case EPI_RESID:     hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NS, EPI_RESID, BL>), grid, block, sm, st, a); break;
+    case EPI_SWIGLU:    hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NSG, EPI_SWIGLU, BL>), grid, block, sm, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+template <typename T, int MT, int NS>
+hipError_t dispatch_bl(const GemmArgs& a, int epi, dim3 grid, dim3 block, hipStream_t st) {
+  // stage the token rows in LDS when they fit beside the reduction buffers
+  const size_t es = sizeof(T);
+  const size_t red = 2ull * 8 * (epi == EPI_SWIGLU ? 2 : 1) * MT * 256 * 4;
+  const size_t sm = static_cast<size_t>(a.M) * (a.K + 8) * es;
+  if (sm + red + 1024 <= 160 * 1024) return dispatch_epi<T, MT, NS, true>(a, epi, grid, block, sm, st);
+  return dispatch_epi<T, MT, NS, false>(a, epi, grid, block, 0, st);
+}
+
+// Waves per workgroup: the first count in {8, 4, 2, 1} that splits the k-steps
+// into equal whole chunks, else 8 with a masked tail.
+int pick_waves(int nsteps, int ns) {
+  const int cand[] = {8, 4, 2, 1};
+  for (int w : cand)
+    if (nsteps % w == 0 && (nsteps / w) % ns == 0) return w;
+  return 8;
 }
 
 }  // namespace
@@ -223,23 +287,34 @@ hipError_t dispatch_epi(const GemmArgs& a, int epi, dim3 grid, dim3 block, hipSt
 hipError_t launch_gemm(const GemmArgs& a0, int epi, bool bf16, hipStream_t st) {
   const int KS = bf16 ? 32 : 16;
   const int nsteps = a0.K / KS;
-  const int nwaves = nsteps < kMaxWaves ? nsteps : kMaxWaves;
-  // rows per workgroup <= 16 * kMaxTiles; about 256 workgroups when possible
-  long G = a0.N < 256 ? a0.N : 256;
-  const long min_g = (a0.N + 16 * kMaxTiles - 1) / (16 * kMaxTiles);
-  if (G < min_g) G = min_g;
-  const dim3 grid(static_cast<unsigned>(G)), block(nwaves * 64);
+  // pipeline depth: 8 k-steps per stage when the split allows it, else 4
+  int ns = 8;
+  int nw8 = pick_waves(nsteps, 8);
+  if (!(nsteps % nw8 == 0 && (nsteps / nw8) % 8 == 0)) ns = 4;
+  long G = a0.N < kSsqParts ? a0.N : kSsqParts;
+  const dim3 grid(static_cast<unsigned>(G));
   for (int t0 = 0; t0 < a0.M; t0 += 32) {
     GemmArgs a = a0;
     a.tok0 = a0.tok0 + t0;
     a.M = (a0.M - t0) < 32 ? (a0.M - t0) : 32;
+    // one epilogue element per thread: at least 4 waves per 16-token tile
+    int nwaves = pick_waves(nsteps, ns);
+    const int minw = a.M <= 16 ? 4 : 8;
+    if (nwaves < minw) nwaves = minw;
+    const dim3 block(nwaves * 64);
     hipError_t e;
-    if (bf16)
-      e = a.M <= 16 ? dispatch_epi<uint16_t, 1>(a, epi, grid, block, st)
-                    : dispatch_epi<uint16_t, 2>(a, epi, grid, block, st);
-    else
-      e = a.M <= 16 ? dispatch_epi<float, 1>(a, epi, grid, block, st)
-                    : dispatch_epi<float, 2>(a, epi, grid, block, st);
+    const bool one = a.M <= 16;
+    if (bf16) {
+      if (ns == 8) e = one ? dispatch_bl<uint16_t, 1, 8>(a, epi, grid, block, st)
+                           : dispatch_bl<uint16_t, 2, 8>(a, epi, grid, block, st);
+      else e = one ? dispatch_bl<uint16_t, 1, 4>(a, epi, grid, block, st)
+                   : dispatch_bl<uint16_t, 2, 4>(a, epi, grid, block, st);
+    } else {
+      if (ns == 8) e = one ? dispatch_bl<float, 1, 8>(a, epi, grid, block, st)
+                           : dispatch_bl<float, 2, 8>(a, epi, grid, block, st);
+      else e = one ? dispatch_bl<float, 1, 4>(a, epi, grid, block, st)
+                   : dispatch_bl<float, 2, 4>(a, epi, grid, block, st);
+    }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -10,8 +10,17 @@
 namespace dlite {
 
 // Workspace counters, zeroed by the first kernel of every draft step.
-enum Counter { CNT_LM_DONE = 0, CNT_SCAN_BAR = 1, CNT_STATUS = 2, CNT_COUNT = 16 };
+// Words 0..15 are fixed counters; the scan's team barriers follow.
+enum Counter { CNT_LM_DONE = 0, CNT_STATUS = 2, CNT_TEAM0 = 16 };
+int scan_counters();                        // team-barrier words after CNT_TEAM0
+size_t scan_scratch_floats(int B, int r);   // size of ScanArgs::U
+inline int counter_words() { return CNT_TEAM0 + scan_counters(); }
 enum Status { STATUS_BARRIER_TIMEOUT = 1 };
+
+// Partial sums of squares per activation row: one slot per producing
+// workgroup (at most kSsqParts), summed in fixed order by the consumer.
+constexpr int kSsqParts = 256;
+constexpr int kMaxLayers = 16;
 
 // ------------------------------------------------------------ feature build --
 struct FeatureArgs {
@@ -20,27 +29,37 @@ struct FeatureArgs {
   const void* feat_norm;  // [D]
   const void* tok_emb;    // [V, D]
   const void* ph_emb;     // [D]
+  const void* attn_norm[kMaxLayers];  // [D] per layer
   const int32_t* anchors; // [B]
   float* X;               // [B, S, D] slot buffer (fp32)
+  void* XB;               // [n_layers + 1][B, S, D] pre-gained GEMM inputs
+  float* ssq;             // [B S, kSsqParts] row sums of squares (slot 0)
   float* tap_z;           // [B, m, D] or null
-  unsigned* counters;     // CNT_COUNT words, zeroed here
-  int B, m, K, D, V;
+  unsigned* counters;     // counter_words() words, zeroed here
+  int n_counters;
+  int B, m, K, D, V, n_layers;
   float eps;
 };
 hipError_t launch_feature(const FeatureArgs& a, bool bf16, hipStream_t st);
 
 // ---------------------------------------------------------------- GEMMs ----
-// out[token, n] = epilogue( sum_k W[n, k] * in[token, k] ), tokens 0..M-1
-// (offset tok0), logical output rows n in [0, N).
+// out[token, n] = epilogue( s_tok * sum_k W[n, k] * in[token, k] ), tokens
+// 0..M-1 (offset tok0), logical output rows n in [0, N); s_tok = 1/rms of
+// the token when `ssq` is given, else 1.
 enum Epi { EPI_STORE_F32 = 0, EPI_STORE_ACT = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
 
 struct GemmArgs {
   const void* W; long ldw; int N; int K;
   long pair_off;                 // SwiGLU: up rows start pair_off rows after gate rows
-  const void* src; int src_f32; long ld_src; RowMap smap;
+  const void* src; long ld_src; RowMap smap;   // pre-gained input rows (storage type)
   int M; int tok0;
-  const void* gain; float eps;   // RMSNorm prologue over the K inputs (null: none)
+  // RMSNorm scale: partial sums at ssq[qmap.row(tok) * kSsqParts + j]; rows
+  // with (row % ssq_group) < ssq_split have np_lo parts, the others np_hi
+  const float* ssq; RowMap qmap; int ssq_group, ssq_split, np_lo, np_hi; int norm_len; float eps;
   void* out; long ld_out; RowMap omap;
+  // EPI_RESID: x += y, then xb_out = bf16(next_gain * x) and one partial
+  // sum of squares of x per workgroup into ssq_out (rows of omap)
+  const void* next_gain; void* xb_out; long ld_xb; RowMap xmap; float* ssq_out;
   float* tap; long ld_tap; RowMap tmap;   // RESID: copy of the updated row
 };
 hipError_t launch_gemm(const GemmArgs& a, int epi, bool bf16, hipStream_t st);
@@ -54,29 +73,33 @@ struct AttnArgs {
   float theta;
 };
 hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t st);
+size_t attention_smem(const AttnArgs& a);   // dynamic LDS bytes of one workgroup
 
-// ----------------------------------------------------------- final norm ----
+// ------------------------------------------------------------ hidden tap ----
+// fp32 copy of h_k = RMSNorm(x_k; gain) for the placeholder rows (checking only).
 struct NormArgs {
   const float* X;     // [B, S, D]
   const void* gain;   // [D]
-  void* out;          // [B, K, D] storage type
-  float* tap;         // [B, K, D] or null
+  float* tap;         // [B, K, D]
   int B, m, K, D; float eps;
 };
-hipError_t launch_final_norm(const NormArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_hidden_tap(const NormArgs& a, bool bf16, hipStream_t st);
 
 // ------------------------------------------------------ sequential head ----
 struct ScanArgs {
   const float* P;        // [B, K, r]  seq_w_down[:, :D] h_k
   const void* w_down;    // [r, D + r] (state columns used)
   const void* w_up;      // [r, r]
-  float* U;              // [B, r] scratch
+  float* U;              // scan_scratch_floats(B, r) floats of scratch
   float* Sf;             // [B, K, r] states (fp32)
   void* Sb;              // [B, K, r] states (storage type) for the vocabulary GEMM
   float* tap;            // [B, K, r] or null
   unsigned* counters;
   int B, K, D, r;
+  unsigned cnt_base;     // barrier counts already accumulated by earlier launches
+  int rpt;               // requests per team (set by launch_scan)
 };
+size_t scan_lds_bytes(int r, bool bf16, int K);
 hipError_t launch_scan(const ScanArgs& a, bool bf16, hipStream_t st);
 
 // ------------------------------------------- vocabulary GEMM + argmax ----

@@ -5,9 +5,9 @@
 // Pass 1: workgroup g streams vocabulary rows [g V / G, (g+1) V / G) through
 // 16x16 MFMA tiles against the token block held in registers and keeps a
 // running (max, index) per token; the full logits are never written (unless
-// the logits tap is requested).  Pass 2 runs in whichever workgroup finishes
-// last: it reduces the G partials of every token in a fixed order, so the
-// result does not depend on scheduling.
+// the logits tap is requested).  Pass 2, a second small kernel, reduces the G
+// partials of every token in a fixed order, so the result does not depend on
+// scheduling.
 #include "kernels.hpp"
 
 namespace dlite {
@@ -17,13 +17,42 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kMaxSteps = 16;   // r <= 512 (bf16) / 256 (fp32)
 
+// Pass 2: one wave per token reduces the G partials in fixed order.  A
+// separate launch: the kernel boundary orders it after every partial.
+__global__ __launch_bounds__(256) void lmhead_reduce_kernel(LmArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= a.M) return;
+  const long G = a.G;
+  const long base = static_cast<long>(a.tok0 + tok) * G;
+  float v = -INFINITY;
+  int i = 0x7fffffff;
+  for (long j = lane; j < G; j += 64) {
+    const float pv = a.part_max[base + j];
+    const int pi = a.part_idx[base + j];
+    if (better(pv, pi, v, i)) { v = pv; i = pi; }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(i, o, kWave);
+    if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  }
+  if (lane == 0) {
+    const int gt = a.tok0 + tok;
+    const int anchor = a.anchors[gt / a.K];
+    const bool ok = anchor >= 0 && anchor < a.V;
+    a.cand[gt] = ok ? i : -1;
+    if (a.max_logit) a.max_logit[gt] = ok ? v : 0.f;
+  }
+}
+
 template <typename T, int MT>
 __global__ __launch_bounds__(kWaves * 64) void lmhead_kernel(LmArgs a) {
   constexpr int PER = Elem<T>::kPerLane;
   constexpr int KS = PER * 4;
   __shared__ float sv[kWaves][32];
   __shared__ int si[kWaves][32];
-  __shared__ int is_last;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, grp = lane >> 4;
@@ -40,11 +69,9 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_kernel(LmArgs a) {
     const int tok = u * 16 + c16;
 #pragma unroll
     for (int s = 0; s < kMaxSteps; ++s) {
-      if (s < nsteps && tok < a.M)
-        b[u][s] = *reinterpret_cast<const uint4*>(
-            X + static_cast<long>(a.tok0 + tok) * a.r + s * KS + grp * PER);
-      else
-        b[u][s] = make_uint4(0, 0, 0, 0);
+      const int sc = s < nsteps ? s : nsteps - 1;
+      b[u][s] = *reinterpret_cast<const uint4*>(
+          X + static_cast<long>(a.tok0 + (tok < a.M ? tok : 0)) * a.r + sc * KS + grp * PER);
     }
   }
 
@@ -57,12 +84,11 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_kernel(LmArgs a) {
     const int row = r0 + t * 16 + c16;
     const bool rok = row < r1;
     uint4 av[kMaxSteps];
+    const int rowc = rok ? row : r1 - 1;
 #pragma unroll
     for (int s = 0; s < kMaxSteps; ++s) {
-      if (s < nsteps && rok)
-        av[s] = ld_stream(W + static_cast<long>(row) * a.r + s * KS + grp * PER);
-      else
-        av[s] = make_uint4(0, 0, 0, 0);
+      const int sc = s < nsteps ? s : nsteps - 1;
+      av[s] = ld_stream(W + static_cast<long>(rowc) * a.r + sc * KS + grp * PER);
     }
     floatx4 acc[MT];
 #pragma unroll
@@ -71,7 +97,8 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_kernel(LmArgs a) {
     for (int s = 0; s < kMaxSteps; ++s)
       if (s < nsteps)
 #pragma unroll
-        for (int u = 0; u < MT; ++u) acc[u] = mma_step(av[s], b[u][s], acc[u], T());
+        for (int u = 0; u < MT; ++u)
+          acc[u] = mma_step(av[s], (u * 16 + c16 < a.M) ? b[u][s] : make_uint4(0, 0, 0, 0), acc[u], T());
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
       const int tok = u * 16 + c16;
@@ -109,40 +136,98 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_kernel(LmArgs a) {
     a.part_idx[o] = i;
   }
 
-  // pass 2 in the last workgroup to finish
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(a.counters + CNT_LM_DONE, 1u);
-    is_last = (prev == static_cast<unsigned>(G - 1));
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int tok = wave; tok < a.M; tok += kWaves) {
-    const long base = static_cast<long>(a.tok0 + tok) * G;
-    float v = -INFINITY;
-    int i = 0x7fffffff;
-    for (long j = lane; j < G; j += 64) {
-      const float pv = a.part_max[base + j];
-      const int pi = a.part_idx[base + j];
-      if (better(pv, pi, v, i)) { v = pv; i = pi; }
-    }
+}
+
+// Pipelined variant for at most 16 tokens: each wave streams its tiles
+// (16 vocabulary rows, all r columns) through a two-stage register pipeline
+// so that the next tile's 16 KB is in flight while the current one is
+// multiplied and reduced.
+template <typename T>
+__global__ __launch_bounds__(kWaves * 64) void lmhead_pipe_kernel(LmArgs a) {
+  constexpr int PER = Elem<T>::kPerLane;
+  constexpr int KS = PER * 4;
+  __shared__ float sv[kWaves][16];
+  __shared__ int si[kWaves][16];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, grp = lane >> 4;
+  const long G = gridDim.x, g = blockIdx.x;
+  const int r0 = static_cast<int>((g * a.V) / G), r1 = static_cast<int>(((g + 1) * a.V) / G);
+  const int ntile = (r1 - r0 + 15) >> 4;
+  const int nsteps = a.r / KS;
+  const T* W = static_cast<const T*>(a.W);
+  const T* X = static_cast<const T*>(a.src);
+
+  // token block: all loads issued unconditionally (clamped addresses); the
+  // mask for missing tokens is applied where the values are used
+  const bool tok_ok = c16 < a.M;
+  const long xrow = static_cast<long>(a.tok0 + (tok_ok ? c16 : 0)) * a.r;
+  uint4 b[kMaxSteps];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float ov = __shfl_xor(v, o, kWave);
-      const int oi = __shfl_xor(i, o, kWave);
-      if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  for (int s = 0; s < kMaxSteps; ++s) {
+    const int sc = s < nsteps ? s : nsteps - 1;
+    b[s] = *reinterpret_cast<const uint4*>(X + xrow + sc * KS + grp * PER);
+  }
+
+  auto issue = [&](int t, uint4 (&st)[kMaxSteps]) {
+    int row = r0 + t * 16 + c16;
+    row = row < r1 ? row : r1 - 1;
+    const T* wr = W + static_cast<long>(row) * a.r + grp * PER;
+#pragma unroll
+    for (int s = 0; s < kMaxSteps; ++s) {
+      const int sc = s < nsteps ? s : nsteps - 1;
+      st[s] = ld_stream(wr + sc * KS);
     }
-    if (lane == 0) {
-      const int gt = a.tok0 + tok;
-      const int anchor = a.anchors[gt / a.K];
-      const bool ok = anchor >= 0 && anchor < a.V;
-      a.cand[gt] = ok ? i : -1;
-      if (a.max_logit) a.max_logit[gt] = ok ? v : 0.f;
+  };
+
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  auto consume = [&](int t, const uint4 (&st)[kMaxSteps]) {
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kMaxSteps; ++s)
+      if (s < nsteps) acc = mma_step(st[s], tok_ok ? b[s] : make_uint4(0, 0, 0, 0), acc, T());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int vr = r0 + t * 16 + grp * 4 + i;
+      if (vr < r1 && tok_ok) {
+        const float v = acc[i];
+        if (better(v, vr, bv, bi)) { bv = v; bi = vr; }
+        if (a.tap) a.tap[static_cast<long>(a.tok0 + c16) * a.V + vr] = v;
+      }
+    }
+  };
+
+  uint4 st0[kMaxSteps], st1[kMaxSteps];
+  int t = wave;
+  if (t < ntile) issue(t, st0);
+  for (; t < ntile; t += 2 * kWaves) {
+    if (t + kWaves < ntile) issue(t + kWaves, st1);
+    consume(t, st0);
+    if (t + kWaves < ntile) {
+      if (t + 2 * kWaves < ntile) issue(t + 2 * kWaves, st0);
+      consume(t + kWaves, st1);
     }
   }
-  if (threadIdx.x == 0) a.counters[CNT_LM_DONE] = 0u;
+
+  // combine the four row groups of each token column, then the waves
+#pragma unroll
+  for (int o = 16; o < 64; o <<= 1) {
+    const float ov = __shfl_xor(bv, o, kWave);
+    const int oi = __shfl_xor(bi, o, kWave);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if (grp == 0) { sv[wave][c16] = bv; si[wave][c16] = bi; }
+  __syncthreads();
+  if (threadIdx.x < 16 && static_cast<int>(threadIdx.x) < a.M) {
+    float v = sv[0][threadIdx.x];
+    int i = si[0][threadIdx.x];
+    for (int w = 1; w < kWaves; ++w)
+      if (better(sv[w][threadIdx.x], si[w][threadIdx.x], v, i)) { v = sv[w][threadIdx.x]; i = si[w][threadIdx.x]; }
+    const long o = static_cast<long>(a.tok0 + threadIdx.x) * G + g;
+    a.part_max[o] = v;
+    a.part_idx[o] = i;
+  }
 }
 
 }  // namespace
@@ -159,13 +244,16 @@ hipError_t launch_lmhead(const LmArgs& a0, bool bf16, hipStream_t st) {
     a.tok0 = a0.tok0 + t0;
     a.M = (a0.M - t0) < 32 ? (a0.M - t0) : 32;
     if (bf16) {
-      if (a.M <= 16) hipLaunchKernelGGL((lmhead_kernel<uint16_t, 1>), grid, block, 0, st, a);
+      if (a.M <= 16) hipLaunchKernelGGL((lmhead_pipe_kernel<uint16_t>), grid, block, 0, st, a);
       else hipLaunchKernelGGL((lmhead_kernel<uint16_t, 2>), grid, block, 0, st, a);
     } else {
-      if (a.M <= 16) hipLaunchKernelGGL((lmhead_kernel<float, 1>), grid, block, 0, st, a);
+      if (a.M <= 16) hipLaunchKernelGGL((lmhead_pipe_kernel<float>), grid, block, 0, st, a);
       else hipLaunchKernelGGL((lmhead_kernel<float, 2>), grid, block, 0, st, a);
     }
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3((a.M + 3) / 4), dim3(256), 0, st, a);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -1,6 +1,6 @@
 // Row-wise kernels of the draft step: building the slot buffer (depth-embedded,
-// RMS-normalised context features, anchor embedding, placeholders) and the
-// final RMSNorm in front of the sequential head.
+// RMS-normalised context features, anchor embedding, placeholders) with the
+// first GEMM inputs, and the optional fp32 copy of the final-normed hidden rows.
 //
 // Feature slots follow the DLite walkthrough, section "历史并没有消失，而是由目标
 // 模型编码" (z = Norm(h^(l) + e_depth^(l))), kept as m separate sequence slots
@@ -30,41 +30,118 @@ __device__ __forceinline__ float ld(const void* p, long i) {
   return Elem<T>::to_f32(static_cast<const T*>(p)[i]);
 }
 
-// One workgroup per slot (b, s).
+// One workgroup per slot (b, s).  Writes the fp32 slot row, its sum of
+// squares (slot 0 of the row's partials) and the pre-gained GEMM input rows:
+// context slots for every layer (they do not change between layers), anchor
+// and placeholder rows for the first layer.  Each thread holds its share of
+// the row in registers (16-byte loads, all issued before the reduction).
+constexpr int kMaxVec = 8;   // 16-byte vectors per thread: D <= 8 * 256 * 8
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& v, float* out) {
+  load16_f32(reinterpret_cast<const T*>(&v), out);
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
+  constexpr int PER = Elem<T>::kPerLane;
   __shared__ float sh[kThreads / 64];
   const int S = a.m + 1 + a.K;
   const int b = blockIdx.x / S, s = blockIdx.x % S;
-  float* x = a.X + static_cast<long>(blockIdx.x) * a.D;
-  if (blockIdx.x == 0 && threadIdx.x < CNT_COUNT) a.counters[threadIdx.x] = 0u;
+  const long row = blockIdx.x;
+  float* x = a.X + row * a.D;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < a.n_counters; i += blockDim.x) a.counters[i] = 0u;
+  const int nvec = a.D / PER;
+
+  const T* src;
+  const T* add = nullptr;
   if (s < a.m) {
-    const long hrow = (static_cast<long>(b) * a.m + s) * a.D;
-    float ss = 0.f;
-    for (int e = threadIdx.x; e < a.D; e += blockDim.x) {
-      const float y = ld<T>(a.H, hrow + e) + ld<T>(a.depth_emb, static_cast<long>(s) * a.D + e);
-      ss += y * y;
-    }
-    const float inv = 1.0f / sqrtf(block_sum(ss, sh) / static_cast<float>(a.D) + a.eps);
-    for (int e = threadIdx.x; e < a.D; e += blockDim.x) {
-      const float y = ld<T>(a.H, hrow + e) + ld<T>(a.depth_emb, static_cast<long>(s) * a.D + e);
-      const float z = ld<T>(a.feat_norm, e) * (y * inv);
-      x[e] = z;
-      if (a.tap_z) a.tap_z[hrow + e] = z;
-    }
+    src = static_cast<const T*>(a.H) + (static_cast<long>(b) * a.m + s) * a.D;
+    add = static_cast<const T*>(a.depth_emb) + static_cast<long>(s) * a.D;
   } else if (s == a.m) {
     const int tok = a.anchors[b];
-    const bool ok = tok >= 0 && tok < a.V;   // out of range: zero input row
-    for (int e = threadIdx.x; e < a.D; e += blockDim.x)
-      x[e] = ok ? ld<T>(a.tok_emb, static_cast<long>(tok) * a.D + e) : 0.f;
+    src = (tok >= 0 && tok < a.V) ? static_cast<const T*>(a.tok_emb) + static_cast<long>(tok) * a.D
+                                  : nullptr;   // out of range: zero input row
   } else {
-    for (int e = threadIdx.x; e < a.D; e += blockDim.x) x[e] = ld<T>(a.ph_emb, e);
+    src = static_cast<const T*>(a.ph_emb);
   }
+  const T* g0 = static_cast<const T*>(a.attn_norm[0]);
+  const T* gf = static_cast<const T*>(a.feat_norm);
+  uint4 hv[kMaxVec], dv[kMaxVec], gv[kMaxVec];
+#pragma unroll
+  for (int q = 0; q < kMaxVec; ++q) {
+    const int idx = threadIdx.x + q * kThreads;
+    hv[q] = dv[q] = gv[q] = make_uint4(0, 0, 0, 0);
+    if (idx < nvec) {
+      if (src) hv[q] = *reinterpret_cast<const uint4*>(src + idx * PER);
+      if (add) {
+        dv[q] = *reinterpret_cast<const uint4*>(add + idx * PER);
+        gv[q] = *reinterpret_cast<const uint4*>(gf + idx * PER);
+      }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < kMaxVec; ++q) {
+    float h[PER], e[PER];
+    unpack16<T>(hv[q], h);
+    unpack16<T>(dv[q], e);
+#pragma unroll
+    for (int t = 0; t < PER; ++t) ss += (h[t] + e[t]) * (h[t] + e[t]);
+  }
+  float inv = 1.f;
+  if (add) inv = 1.0f / sqrtf(block_sum(ss, sh) / static_cast<float>(a.D) + a.eps);
+  ss = 0.f;
+  // final slot values (fp32), their sum of squares, the first layer's inputs
+#pragma unroll
+  for (int q = 0; q < kMaxVec; ++q) {
+    const int idx = threadIdx.x + q * kThreads;
+    if (idx < nvec) {
+      float h[PER], e[PER], gz[PER], v[PER], g[PER];
+      unpack16<T>(hv[q], h);
+      unpack16<T>(dv[q], e);
+      unpack16<T>(gv[q], gz);
+#pragma unroll
+      for (int t = 0; t < PER; ++t) {
+        v[t] = add ? gz[t] * ((h[t] + e[t]) * inv) : h[t];
+        ss += v[t] * v[t];
+      }
+      float* xo = x + idx * PER;
+#pragma unroll
+      for (int t = 0; t < PER; t += 4)
+        *reinterpret_cast<float4*>(xo + t) = make_float4(v[t], v[t + 1], v[t + 2], v[t + 3]);
+      if (add && a.tap_z) {
+        float* tz = a.tap_z + (static_cast<long>(b) * a.m + s) * a.D + idx * PER;
+#pragma unroll
+        for (int t = 0; t < PER; t += 4)
+          *reinterpret_cast<float4*>(tz + t) = make_float4(v[t], v[t + 1], v[t + 2], v[t + 3]);
+      }
+      load16_f32(g0 + idx * PER, g);
+      float o[PER];
+#pragma unroll
+      for (int t = 0; t < PER; ++t) o[t] = g[t] * v[t];
+      *reinterpret_cast<uint4*>(static_cast<T*>(a.XB) + row * a.D + idx * PER) = pack16(o, T());
+      // context slots feed every layer's keys and values with that layer's gain
+      if (add) {
+        for (int l = 1; l < a.n_layers; ++l) {
+          load16_f32(static_cast<const T*>(a.attn_norm[l]) + idx * PER, g);
+#pragma unroll
+          for (int t = 0; t < PER; ++t) o[t] = g[t] * v[t];
+          *reinterpret_cast<uint4*>(static_cast<T*>(a.XB) +
+                                    (l * static_cast<long>(a.B) * S + row) * a.D + idx * PER) =
+              pack16(o, T());
+        }
+      }
+    }
+  }
+  ss = block_sum(ss, sh);
+  if (threadIdx.x == 0) a.ssq[row * kSsqParts] = ss;
 }
 
-// h_k = RMSNorm(x_k; gain) for the placeholder rows; one workgroup per row.
+// fp32 h_k = RMSNorm(x_k; gain) of the placeholder rows; one workgroup per row.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void final_norm_kernel(NormArgs a) {
+__global__ __launch_bounds__(kThreads) void hidden_tap_kernel(NormArgs a) {
   __shared__ float sh[kThreads / 64];
   const int S = a.m + 1 + a.K;
   const int b = blockIdx.x / a.K, k = blockIdx.x % a.K;
@@ -73,11 +150,7 @@ __global__ __launch_bounds__(kThreads) void final_norm_kernel(NormArgs a) {
   for (int e = threadIdx.x; e < a.D; e += blockDim.x) ss += x[e] * x[e];
   const float inv = 1.0f / sqrtf(block_sum(ss, sh) / static_cast<float>(a.D) + a.eps);
   const long orow = static_cast<long>(blockIdx.x) * a.D;
-  for (int e = threadIdx.x; e < a.D; e += blockDim.x) {
-    const float h = ld<T>(a.gain, e) * (x[e] * inv);
-    static_cast<T*>(a.out)[orow + e] = Elem<T>::from_f32(h);
-    if (a.tap) a.tap[orow + e] = h;
-  }
+  for (int e = threadIdx.x; e < a.D; e += blockDim.x) a.tap[orow + e] = ld<T>(a.gain, e) * (x[e] * inv);
 }
 
 }  // namespace
@@ -91,12 +164,12 @@ hipError_t launch_feature(const FeatureArgs& a, bool bf16, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_final_norm(const NormArgs& a, bool bf16, hipStream_t st) {
+hipError_t launch_hidden_tap(const NormArgs& a, bool bf16, hipStream_t st) {
   const dim3 grid(a.B * a.K), block(kThreads);
   if (bf16)
-    hipLaunchKernelGGL(final_norm_kernel<uint16_t>, grid, block, 0, st, a);
+    hipLaunchKernelGGL(hidden_tap_kernel<uint16_t>, grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL(final_norm_kernel<float>, grid, block, 0, st, a);
+    hipLaunchKernelGGL(hidden_tap_kernel<float>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -70,7 +70,8 @@ enum {
  *   ffn      SwiGLU inner width F (multiple of 32)
  *   K        placeholders = drafted tokens per request (1 .. 16); the paper's
  *            block of 8 is the anchor plus K = 7 ([W] "草稿块长与验证块长不是一个参数")
- *   rank     sequential-head state width r (multiple of 32, <= 1024)
+ *   rank     sequential-head state width r (multiple of 32; <= 512 for bf16,
+ *            <= 256 for fp32)
  *   vocab    vocabulary size V (1 .. 2^30)
  *   dtype    DLITE_BF16 or DLITE_F32 for all weights and the features
  *   rms_eps  RMSNorm epsilon (e.g. 1e-6)
@@ -177,6 +178,31 @@ int dlite_draft_block(const dlite_dims *dims, const dlite_weights *weights,
 int dlite_accept_prefix(const int32_t *candidates, const int32_t *target_tokens,
                         int32_t B, int32_t K, int32_t *accept_len,
                         int32_t *next_anchor, hipStream_t stream);
+
+/*
+ * Instrumentation for timing one stage of the draft step with HIP events.
+ * After this call, every dlite_draft_block call made from the same thread
+ * records `before` on its stream immediately before the first kernel of
+ * `stage` and `after` immediately after the stage's last kernel (for
+ * per-layer stages: in the first backbone layer).  The events are owned by the
+ * caller; pass NULL for both to switch recording off.  Returns
+ * DLITE_ERR_SHAPE for an unknown stage, DLITE_ERR_NULL if exactly one event is
+ * NULL.
+ */
+enum {
+  DLITE_STAGE_FEATURES = 0,   /* feature slots, anchor and placeholder rows     */
+  DLITE_STAGE_QKV = 1,        /* RMSNorm + q, k, v projections                   */
+  DLITE_STAGE_ATTENTION = 2,  /* non-causal block attention                      */
+  DLITE_STAGE_OPROJ = 3,      /* output projection + residual                    */
+  DLITE_STAGE_GATE_UP = 4,    /* RMSNorm + gate/up projection + SwiGLU           */
+  DLITE_STAGE_DOWN = 5,       /* down projection + residual                      */
+  DLITE_STAGE_FINAL_NORM = 6, /* RMSNorm of the placeholder rows                 */
+  DLITE_STAGE_SEQ_PROJ = 7,   /* hidden part of the sequential head's input      */
+  DLITE_STAGE_SCAN = 8,       /* the K-step recurrence                           */
+  DLITE_STAGE_LM_HEAD = 9,    /* vocabulary projection + argmax                  */
+  DLITE_NUM_STAGES = 10
+};
+int dlite_set_stage_events(int stage, hipEvent_t before, hipEvent_t after);
 
 /* Message describing the calling thread's last error ("" if none). */
 const char *dlite_last_error(void);
