@@ -43,6 +43,12 @@ def parse():
                    help="time budget of the CPU oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stages", action="store_true", help="also time every stage separately")
+    p.add_argument("--kernel", default=None,
+                   help="stage whose roofline is reported (default: the one with the "
+                        "largest algorithmic time at peak)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB (5 times); "
+                        "its HBM counters calibrate the kernel traffic figures")
     return p.parse_args()
 
 
@@ -137,7 +143,7 @@ def cpu_baseline(w, weights, H, anchors, budget_s):
         oracle.accept_prefix(ref["cand"], tgt)
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
+        if el >= budget_s:
             break
     value = n * w.B * w.K / el
     res = {"value": value, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
@@ -157,6 +163,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}))
+        return
     from history_free_drafter_amd import binding as B
     from history_free_drafter_amd.runtime import DraftModel, to_device
     from synth import (WORKLOADS, make_anchors, make_features, make_target_tokens,
@@ -200,7 +215,9 @@ def main():
     # dominant kernel: the stage with the largest algorithmic time at peak
     def t_roof(s):
         return max(costs[s][0] / HBM_PEAK, costs[s][1] / MFMA_BF16_PEAK)
-    dom = max(costs, key=t_roof)
+    dom = args.kernel or max(costs, key=t_roof)
+    if dom not in costs:
+        raise SystemExit(f"unknown stage {dom}; stages: {sorted(costs)}")
     ev = HipEvents()
 
     def step(i):

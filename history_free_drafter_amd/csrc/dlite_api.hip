@@ -47,11 +47,37 @@ size_t esize(const dlite_dims& d) { return d.dtype == DLITE_BF16 ? 2 : 4; }
 
 // Workspace regions, each 256-byte aligned.
 struct Plan {
-  size_t counters, X, XB, XF, SSQ, Q, KV, AO, ACT, P, U, Sf, Sb, pmax, pidx, total;
+  size_t counters, X, XB, XF, SSQ, Q, KV, AO, ACT, P, U, Sf, Sb, pmax, pidx, TP, total;
   int G;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+// Partial-tile scratch of the tiled GEMMs: the largest need of any launch of
+// the step (the same tile plan the launches use).
+size_t tile_scratch_bytes(const dlite_dims& d) {
+  if (d.dtype != DLITE_BF16) return 0;
+  const int B = d.B, S = d.m + 1 + d.K, L = 1 + d.K, K = d.K, D = d.D, F = d.ffn, r = d.rank;
+  const int Hq = d.n_q * d.d_h, Hkv2 = 2 * d.n_kv * d.d_h;
+  auto one = [&](int M0, int M1, int N0, int N1, int Kd, int epi) -> size_t {
+    const int mx = M0 > M1 ? M0 : M1;
+    if (mx < kTileMinRows || Kd % 64) return 0;
+    return gemm_tile_scratch(M0, M1, N0, N1, Kd, epi);
+  };
+  size_t need = 0;
+  auto keep = [&](size_t v) { need = v > need ? v : need; };
+  for (int Lr : {L, K}) {
+    const int Mq = B * Lr, Mkv = B * S;
+    if (Mq >= kTileMinRows) keep(one(Mq, Mkv, Hq, Hkv2, D, EPI_STORE_F32));
+    else keep(one(Mkv, 0, Hkv2, 0, D, EPI_STORE_F32));
+    keep(one(Mq, 0, D, 0, Hq, EPI_RESID));
+    keep(one(Mq, 0, F, 0, D, EPI_SWIGLU));
+    keep(one(Mq, 0, D, 0, F, EPI_RESID));
+  }
+  keep(one(B * K, 0, r, 0, D, EPI_STORE_F32));
+  keep(one(B * K, 0, d.vocab, 0, r, EPI_ARGMAX));
+  return need;
+}
 
 Plan make_plan(const dlite_dims& d) {
   const size_t B = d.B, S = d.m + 1 + d.K, L = 1 + d.K, D = d.D;
@@ -59,6 +85,8 @@ Plan make_plan(const dlite_dims& d) {
   const size_t F = d.ffn, K = d.K, r = d.rank, es = esize(d);
   Plan p{};
   p.G = lmhead_groups(d.vocab);
+  const int Gt = gemm_tile_groups(d.vocab);
+  const size_t Gmax = p.G > Gt ? p.G : Gt;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
   p.counters = take(counter_words() * sizeof(unsigned));
@@ -74,8 +102,9 @@ Plan make_plan(const dlite_dims& d) {
   p.U = take(scan_scratch_floats(d.B, d.rank) * 4);
   p.Sf = take(B * K * r * 4);
   p.Sb = take(B * K * r * es);
-  p.pmax = take(B * K * static_cast<size_t>(p.G) * 4);
-  p.pidx = take(B * K * static_cast<size_t>(p.G) * 4);
+  p.pmax = take(B * K * Gmax * 4);
+  p.pidx = take(B * K * Gmax * 4);
+  p.TP = take(tile_scratch_bytes(d));
   p.total = off;
   return p;
 }
@@ -225,10 +254,13 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   void* Sb = ws + p.Sb;
   float* pmax = reinterpret_cast<float*>(ws + p.pmax);
   int* pidx = reinterpret_cast<int*>(ws + p.pidx);
+  float* TPs = p.TP != p.total ? reinterpret_cast<float*>(ws + p.TP) : nullptr;
   const dlite_taps no_taps{};
   const dlite_taps& tp = taps ? *taps : no_taps;
   const size_t xb_layer = static_cast<size_t>(B) * S * D * es;
-  const int G_rows = D < kSsqParts ? D : kSsqParts;   // workgroups of a D-row GEMM
+  // partial sums of squares per local row left by the last residual update
+  // (the feature kernel writes one)
+  int local_parts = 1;
 
   // 1. feature slots, anchor and placeholder rows, first GEMM inputs
   //    (also clears the counters)
@@ -252,24 +284,25 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
     const int Lr = L - q0;
     const RowMap slot_rows{Lr, S, m + q0}, local_rows{Lr, L, q0}, all_slots{S, S, 0};
     const void* xb = XB + l * xb_layer;
-    // local rows of layer 0 come from the feature kernel (one part), later
-    // layers from the previous down projection (G_rows parts)
-    const int np_local = l == 0 ? 1 : G_rows;
 
     GemmArgs q{};
     q.W = lw.wqkv; q.ldw = D; q.N = Hq; q.K = D;
     q.src = xb; q.ld_src = D; q.smap = slot_rows; q.M = B * Lr;
     q.ssq = SSQ; q.qmap = slot_rows; q.ssq_group = S; q.ssq_split = m; q.np_lo = 1;
-    q.np_hi = np_local; q.norm_len = D; q.eps = d.rms_eps;
+    q.np_hi = local_parts; q.norm_len = D; q.eps = d.rms_eps;
     q.out = Qb; q.ld_out = Hq; q.omap = local_rows;
     DLITE_LAUNCH(mark(DLITE_STAGE_QKV, true, st, l));
-    DLITE_LAUNCH(launch_gemm(q, EPI_STORE_F32, bf16, st));
-
     GemmArgs kv = q;
     kv.W = at(lw.wqkv, static_cast<size_t>(Hq) * D * es); kv.N = 2 * Hkv;
     kv.smap = all_slots; kv.qmap = all_slots; kv.M = B * S;
     kv.out = KVb; kv.ld_out = 2 * Hkv; kv.omap = all_slots;
-    DLITE_LAUNCH(launch_gemm(kv, EPI_STORE_F32, bf16, st));
+    if (gemm_tiled(q, bf16) && gemm_tiled(kv, bf16)) {
+      const GemmArgs qkv[2] = {q, kv};   // one launch for both row sets
+      DLITE_LAUNCH(launch_gemm_tiled(qkv, 2, EPI_STORE_F32, TPs, st));
+    } else {
+      DLITE_LAUNCH(launch_gemm(q, EPI_STORE_F32, bf16, TPs, st));
+      DLITE_LAUNCH(launch_gemm(kv, EPI_STORE_F32, bf16, TPs, st));
+    }
     DLITE_LAUNCH(mark(DLITE_STAGE_QKV, false, st, l));
 
     AttnArgs aa{Qb, KVb, AO, B, m, K, d.n_q, d.n_kv, d.d_h, q0, d.rope_theta};
@@ -283,17 +316,17 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
     o.out = X; o.ld_out = D; o.omap = slot_rows;
     o.next_gain = lw.ffn_norm; o.xb_out = XF; o.ld_xb = D; o.xmap = local_rows; o.ssq_out = SSQ;
     DLITE_LAUNCH(mark(DLITE_STAGE_OPROJ, true, st, l));
-    DLITE_LAUNCH(launch_gemm(o, EPI_RESID, bf16, st));
+    DLITE_LAUNCH(launch_gemm(o, EPI_RESID, bf16, TPs, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_OPROJ, false, st, l));
 
     GemmArgs gu{};
     gu.W = lw.w_gate_up; gu.ldw = D; gu.N = F; gu.K = D; gu.pair_off = F;
     gu.src = XF; gu.ld_src = D; gu.smap = local_rows; gu.M = B * Lr;
-    gu.ssq = SSQ; gu.qmap = slot_rows; gu.ssq_group = S; gu.ssq_split = 0; gu.np_lo = G_rows;
-    gu.np_hi = G_rows; gu.norm_len = D; gu.eps = d.rms_eps;
+    gu.ssq = SSQ; gu.qmap = slot_rows; gu.ssq_group = S; gu.ssq_split = 0; gu.np_lo = gemm_resid_parts(o, bf16);
+    gu.np_hi = gu.np_lo; gu.norm_len = D; gu.eps = d.rms_eps;
     gu.out = ACT; gu.ld_out = F; gu.omap = local_rows;
     DLITE_LAUNCH(mark(DLITE_STAGE_GATE_UP, true, st, l));
-    DLITE_LAUNCH(launch_gemm(gu, EPI_SWIGLU, bf16, st));
+    DLITE_LAUNCH(launch_gemm(gu, EPI_SWIGLU, bf16, TPs, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_GATE_UP, false, st, l));
 
     GemmArgs dn{};
@@ -307,7 +340,8 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
       dn.ld_tap = D; dn.tmap = local_rows;
     }
     DLITE_LAUNCH(mark(DLITE_STAGE_DOWN, true, st, l));
-    DLITE_LAUNCH(launch_gemm(dn, EPI_RESID, bf16, st));
+    DLITE_LAUNCH(launch_gemm(dn, EPI_RESID, bf16, TPs, st));
+    local_parts = gemm_resid_parts(dn, bf16);
     DLITE_LAUNCH(mark(DLITE_STAGE_DOWN, false, st, l));
   }
 
@@ -325,11 +359,11 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   GemmArgs ph{};
   ph.W = w->seq_w_down; ph.ldw = static_cast<long>(D) + r; ph.N = r; ph.K = D;
   ph.src = XB + d.n_layers * xb_layer; ph.ld_src = D; ph.smap = ph_rows; ph.M = B * K;
-  ph.ssq = SSQ; ph.qmap = ph_rows; ph.ssq_group = S; ph.ssq_split = 0; ph.np_lo = G_rows;
-  ph.np_hi = G_rows; ph.norm_len = D; ph.eps = d.rms_eps;
+  ph.ssq = SSQ; ph.qmap = ph_rows; ph.ssq_group = S; ph.ssq_split = 0; ph.np_lo = local_parts;
+  ph.np_hi = local_parts; ph.norm_len = D; ph.eps = d.rms_eps;
   ph.out = P; ph.ld_out = r; ph.omap = RowMap{K, K, 0};
   DLITE_LAUNCH(mark(DLITE_STAGE_SEQ_PROJ, true, st));
-  DLITE_LAUNCH(launch_gemm(ph, EPI_STORE_F32, bf16, st));
+  DLITE_LAUNCH(launch_gemm(ph, EPI_STORE_F32, bf16, TPs, st));
   DLITE_LAUNCH(mark(DLITE_STAGE_SEQ_PROJ, false, st));
 
   // 5. the K-step recurrence
@@ -343,7 +377,7 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   la.W = w->lm_head; la.src = Sb; la.V = d.vocab; la.r = r; la.M = B * K; la.tok0 = 0;
   la.part_max = pmax; la.part_idx = pidx; la.G = p.G;
   la.cand = candidates; la.max_logit = max_logit; la.tap = tp.logits;
-  la.anchors = anchor_ids; la.K = K; la.counters = counters;
+  la.anchors = anchor_ids; la.K = K; la.counters = counters; la.part = TPs;
   DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, true, st));
   DLITE_LAUNCH(launch_lmhead(la, bf16, st));
   DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, false, st));

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GemmArgs a) {
 
   const int ldb = a.K + 8;
   const T* Bs = reinterpret_cast<const T*>(bsm);
-  if (BL) {
+  auto stage_tokens = [&]() {
     // stage the M real token rows: 16-byte loads, all issued before the stores
     T* bw = reinterpret_cast<T*>(bsm);
     const int vk = a.K / PER, nv = a.M * vk;
@@ -90,10 +90,13 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GemmArgs a) {
       }
     }
     __syncthreads();
-  }
+  };
 
+  // chunk order rotated by workgroup so that workgroups read different
+  // activation lines at any moment
+  const int crot = static_cast<int>(g % nchunk);
   auto issue = [&](int p, Stage<T, NP, MT, NS>& st) {
-    const int t = p / nchunk, c = p % nchunk;
+    const int t = p / nchunk, c = (p % nchunk + crot) % nchunk;
     int row = r0 + t * 16 + c16;
     row = row < r1 ? row : r1 - 1;
 #pragma unroll
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GemmArgs a) {
   zero_acc();
 
   auto compute = [&](int p, const Stage<T, NP, MT, NS>& st) {
-    const int c = p % nchunk;
+    const int c = (p % nchunk + crot) % nchunk;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const bool ok = s0 + c * NS + i < s1;
@@ -213,10 +216,14 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GemmArgs a) {
   };
 
   // two-stage pipeline over (tile, chunk) units
+  // the first two stages of weights are requested before the token rows are
+  // staged, so both round trips overlap
   Stage<T, NP, MT, NS> st0, st1;
   if (nunit > 0) issue(0, st0);
+  if (nunit > 1) issue(1, st1);
+  if (BL) stage_tokens();
   for (int p = 0; p < nunit; p += 2) {
-    if (p + 1 < nunit) issue(p + 1, st1);
+    if (p + 1 < nunit && p > 0) issue(p + 1, st1);
     compute(p, st0);
     if (p % nchunk == nchunk - 1) { finish_tile(p / nchunk); zero_acc(); }
     if (p + 1 < nunit) {
@@ -284,7 +291,14 @@ int pick_waves(int nsteps, int ns) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& a0, int epi, bool bf16, hipStream_t st) {
+int gemm_resid_parts(const GemmArgs& a, bool bf16) {
+  if (gemm_tiled(a, bf16)) return (a.N + 127) / 128;
+  return a.N < kSsqParts ? a.N : kSsqParts;
+}
+
+hipError_t launch_gemm(const GemmArgs& a0, int epi, bool bf16, float* part, hipStream_t st) {
+  if (gemm_tiled(a0, bf16)) return launch_gemm_tiled(&a0, 1, epi, part, st);
+  if (epi == EPI_ARGMAX) return hipErrorInvalidValue;
   const int KS = bf16 ? 32 : 16;
   const int nsteps = a0.K / KS;
   // pipeline depth: 8 k-steps per stage when the split allows it, else 4

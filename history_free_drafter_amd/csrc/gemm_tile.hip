@@ -1,0 +1,479 @@
+// LDS-tiled bf16 MFMA GEMM for many activation rows (batched draft steps).
+//
+// Once a linear map meets hundreds of token rows, each weight byte carries
+// hundreds of multiply-adds and the maps become MFMA-bound, so the weights are
+// no longer streamed past a tiny token block.  The output is cut into tiles of
+// 256 weight rows x 128 tokens; four waves each own a 128 x 64 block of one
+// tile and compute it with 32x32x16 MFMAs whose fragments come from LDS.  K is
+// walked in 64-wide stages: the next stage's weight and token rows are
+// fetched with 16-byte loads into registers while the current stage (one LDS
+// buffer of 48 KB) is multiplied.  Two workgroups share a CU (LDS and
+// registers are sized for it), so one's loads, barriers and epilogue overlap
+// the other's MFMAs.  LDS rows are 128 bytes with the 16-byte chunks of row R
+// stored at position (chunk ^ ((R >> 1) & 7)), so each 16-lane group of a
+// fragment load (16 consecutive rows) hits distinct banks without padding.
+//
+// Launches with fewer output tiles than CUs split K: work item (tile, slice)
+// stores its fp32 accumulators as a partial tile, and a second launch of the
+// same kernel adds the slices of each tile in slice order (deterministic) and
+// runs the epilogue.
+//
+// Tiles are numbered with the token tile fastest and handed out per XCD in
+// contiguous ranges, so the token tiles that share a weight tile run side by
+// side on one XCD and read the weight tile through one L2.  Up to two
+// independent problems with the same K (e.g. query rows of the local tokens
+// and key/value rows of every slot) share one launch.
+//
+// Epilogues match the weight-streaming kernel (same argument block): plain
+// stores, residual update with pre-gained copy and partial sums of squares,
+// SwiGLU pairs, and for the vocabulary projection a per-tile (max, index)
+// partial with ties to the lower index.
+#include <type_traits>
+
+#include "kernels.hpp"
+
+namespace dlite {
+
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBN = 256;        // weight rows per workgroup tile
+constexpr int kBK = 64;         // k per stage
+constexpr int kRowB = kBK * 2;  // bytes of one LDS row
+constexpr int kBM = 128;        // tokens per workgroup tile
+constexpr int kTileFloats = kBN * kBM;   // one fp32 partial tile
+constexpr int kSplitTarget = 256;        // work items wanted per launch
+constexpr int kMinSlice = 4;             // stages per k slice, at least
+
+enum Mode { MODE_FULL = 0, MODE_SLICE = 1, MODE_REDUCE = 2 };
+
+__device__ __forceinline__ floatx16 mma32(uint4 a, uint4 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 16-byte chunk c of LDS row r sits at position c ^ ((r >> 1) & 7): the 16
+// rows read by each 16-lane group of a fragment load cover all 64 banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
+
+// Weight row behind LDS row l of output tile nb (SwiGLU: 64-row blocks
+// alternate gate and up rows of the same 64 outputs).
+template <int EPI>
+__device__ __forceinline__ long weight_row(const GemmArgs& a, int nb, int l) {
+  if (EPI == EPI_SWIGLU) {
+    const int q = l >> 6;
+    int n = nb * (kBN / 2) + (q >> 1) * 64 + (l & 63);
+    n = n < a.N ? n : a.N - 1;
+    return n + ((q & 1) ? a.pair_off : 0);
+  }
+  int n = nb * kBN + l;
+  return n < a.N ? n : a.N - 1;
+}
+
+template <int EPI, int MODE>
+__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
+  constexpr int WTM = 2;                      // 32-token blocks per wave
+  constexpr int NT = 256;                     // four waves, 2 x 2 over the tile
+  constexpr int BM = kBM;
+  constexpr int ROWS = kBN + BM;              // LDS rows per stage
+  constexpr int NLD = ROWS * 8 / NT;          // 16-byte loads per thread per stage
+  constexpr int NLA = kBN * 8 / NT;           // of which weight loads
+  constexpr int TPT = NT / BM;                // threads per token for the norm sums
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint4* lds = reinterpret_cast<uint4*>(smem);                      // [ROWS * 8] chunks
+  float* red = reinterpret_cast<float*>(smem + ROWS * kRowB);       // [TPT][BM]
+  float* bv_s = red + TPT * BM;                                     // [2][BM] argmax values
+  int* bi_s = reinterpret_cast<int*>(bv_s + 2 * BM);                // [2][BM] argmax indices
+
+  // ---- work item: XCD x (workgroups x, x + 8, ...) owns items
+  //      [x per_xcd, (x+1) per_xcd); within a problem the token tile is
+  //      fastest, then the k slice, then the weight tile, so the token tiles
+  //      of one weight slice run side by side on one XCD
+  const int S = MODE == MODE_SLICE ? ta.ksplit : 1;
+  const int bid = blockIdx.x;
+  int t = (bid & 7) * ta.per_xcd + (bid >> 3);
+  if (t >= ta.total * S) return;
+  const int sg = t < ta.tiles0 * S ? 0 : 1;
+  if (sg) t -= ta.tiles0 * S;
+  const GemmArgs& a = ta.seg[sg];
+  const int nbm = ta.nbm[sg];
+  const int mb = t % nbm, rest = t / nbm;
+  const int slice = rest % S, nb = rest / S;
+  const int m0 = mb * BM;
+  const int tile = (sg ? ta.tiles0 : 0) + nb * nbm + mb;   // index of the output tile
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int fr = lane & 31, fk = lane >> 5;
+
+  floatx16 acc[4][WTM];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int u = 0; u < WTM; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][u][e] = 0.f;
+
+  // partial tile layout: float4 j of thread tid at (j * 256 + tid) * 4
+  auto part_at = [&](int sl) { return ta.part + (static_cast<long>(tile) * ta.ksplit + sl) * kTileFloats; };
+
+  if (MODE != MODE_REDUCE) {
+    const uint16_t* W = static_cast<const uint16_t*>(a.W);
+    const uint16_t* X = static_cast<const uint16_t*>(a.src);
+    // ---- stage loads: thread covers rows (tid / 8) + 32 i, 16-byte chunk tid % 8
+    const int kc = tid & 7;
+    const uint16_t* gp[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int row = (tid >> 3) + i * (NT / 8);
+      if (i < NLA) {
+        gp[i] = W + weight_row<EPI>(a, nb, row) * a.ldw + kc * 8;
+      } else {
+        int tk = m0 + row - kBN;
+        tk = tk < a.M ? tk : a.M - 1;
+        gp[i] = X + a.smap.row(a.tok0 + tk) * a.ld_src + kc * 8;
+      }
+    }
+    const int nk = a.K / kBK;
+    const int k0 = (slice * nk) / S, k1 = ((slice + 1) * nk) / S;
+    uint4 pre[NLD];
+    auto load_stage = [&](int kt) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const uint16_t* q = gp[i] + static_cast<long>(kt) * kBK;
+        pre[i] = i < NLA ? ld_stream(q) : *reinterpret_cast<const uint4*>(q);
+      }
+    };
+    auto store_stage = [&]() {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) lds[swz((tid >> 3) + i * (NT / 8), kc)] = pre[i];
+    };
+    auto compute = [&]() {
+#pragma unroll
+      for (int ks = 0; ks < kBK / 16; ++ks) {
+        const int ch = 2 * ks + fk;
+        uint4 af[4], bf[WTM];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = lds[swz(wn * 128 + i * 32 + fr, ch)];
+#pragma unroll
+        for (int u = 0; u < WTM; ++u) bf[u] = lds[swz(kBN + wm * (BM / 2) + u * 32 + fr, ch)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int u = 0; u < WTM; ++u) acc[i][u] = mma32(af[i], bf[u], acc[i][u]);
+      }
+    };
+
+    load_stage(k0);
+    store_stage();
+    __syncthreads();
+    for (int kt = k0; kt < k1; ++kt) {
+      if (kt + 1 < k1) load_stage(kt + 1);
+      compute();
+      __syncthreads();
+      if (kt + 1 < k1) {
+        store_stage();
+        __syncthreads();
+      }
+    }
+    if (MODE == MODE_SLICE) {
+      float4* pp = reinterpret_cast<float4*>(part_at(slice));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int u = 0; u < WTM; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            pp[((i * WTM + u) * 4 + q) * NT + tid] =
+                make_float4(acc[i][u][4 * q], acc[i][u][4 * q + 1], acc[i][u][4 * q + 2], acc[i][u][4 * q + 3]);
+      return;
+    }
+  } else {
+    // ---- add the k slices of this tile in slice order
+    for (int sl = 0; sl < ta.ksplit; ++sl) {
+      const float4* pp = reinterpret_cast<const float4*>(part_at(sl));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int u = 0; u < WTM; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v = pp[((i * WTM + u) * 4 + q) * NT + tid];
+            acc[i][u][4 * q] += v.x;
+            acc[i][u][4 * q + 1] += v.y;
+            acc[i][u][4 * q + 2] += v.z;
+            acc[i][u][4 * q + 3] += v.w;
+          }
+    }
+  }
+
+  // ---- partial sums of squares of this tile's tokens (TPT threads per token)
+  if (a.ssq) {
+    const int tl = tid % BM, part = tid / BM;
+    float v = 0.f;
+    const int tk = m0 + tl;
+    if (tk < a.M) {
+      const long prow = a.qmap.row(a.tok0 + tk);
+      const int np = (prow % a.ssq_group) < a.ssq_split ? a.np_lo : a.np_hi;
+      const float* sp = a.ssq + prow * kSsqParts;
+      for (int j = part; j < np; j += TPT) v += sp[j];
+    }
+    red[part * BM + tl] = v;
+  }
+  __syncthreads();
+
+  // ---- epilogue: lane holds token column fr of each 32x32 block and rows
+  //      8 q + 4 fk + (0..3) of it
+  float inv[WTM];
+  int tk[WTM];
+  bool tok_ok[WTM];
+#pragma unroll
+  for (int u = 0; u < WTM; ++u) {
+    const int tloc = wm * (BM / 2) + u * 32 + fr;
+    tk[u] = m0 + tloc;
+    tok_ok[u] = tk[u] < a.M;
+    inv[u] = 1.f;
+    if (a.ssq) {
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < TPT; ++q) v += red[q * BM + tloc];
+      inv[u] = 1.0f / sqrtf(v / static_cast<float>(a.norm_len) + a.eps);
+    }
+  }
+
+  if (EPI == EPI_ARGMAX) {
+    // a lane's values come in increasing row order, so "strictly greater"
+    // keeps the lowest index among equal maxima; rows past N only exist in
+    // the last weight tile
+    const int nbase = nb * kBN + wn * 128 + 4 * fk;
+    const bool full = nb * kBN + kBN <= a.N;
+#pragma unroll
+    for (int u = 0; u < WTM; ++u) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      if (full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float v = acc[i][u][4 * q + e];
+              const bool gt = v > bv;
+              bv = gt ? v : bv;
+              bi = gt ? nbase + i * 32 + 8 * q + e : bi;
+            }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int n = nbase + i * 32 + 8 * q + e;
+              const float v = acc[i][u][4 * q + e];
+              const bool gt = v > bv && n < a.N;
+              bv = gt ? v : bv;
+              bi = gt ? n : bi;
+            }
+      }
+      const float ov = __shfl_xor(bv, 32, kWave);
+      const int oi = __shfl_xor(bi, 32, kWave);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      if (fk == 0) {
+        const int tloc = wm * (BM / 2) + u * 32 + fr;
+        bv_s[wn * BM + tloc] = bv;
+        bi_s[wn * BM + tloc] = bi;
+      }
+    }
+    if (a.tap) {   // logits copy (checking only)
+#pragma unroll
+      for (int u = 0; u < WTM; ++u) {
+        float* trow = a.tap + a.tmap.row(a.tok0 + (tok_ok[u] ? tk[u] : 0)) * a.ld_tap;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int n = nbase + i * 32 + 8 * q + e;
+              if (tok_ok[u] && n < a.N) trow[n] = acc[i][u][4 * q + e];
+            }
+      }
+    }
+    __syncthreads();
+    if (tid < BM && m0 + tid < a.M) {
+      float v = bv_s[tid];
+      int ix = bi_s[tid];
+      if (better(bv_s[BM + tid], bi_s[BM + tid], v, ix)) { v = bv_s[BM + tid]; ix = bi_s[BM + tid]; }
+      const long o = static_cast<long>(a.tok0 + m0 + tid) * a.G_part + nb;
+      a.part_max[o] = v;
+      a.part_idx[o] = ix;
+    }
+    return;
+  }
+
+  // stores of token block u; CHK: rows past N possible (last weight tile)
+  auto store_u = [&](int u, auto chk) {
+    constexpr bool CHK = decltype(chk)::value;
+    const long orow = a.omap.row(a.tok0 + tk[u]);
+    if (EPI == EPI_SWIGLU) {
+      uint16_t* out = static_cast<uint16_t*>(a.out) + orow * a.ld_out;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nb * (kBN / 2) + wn * 64 + i * 32 + 8 * q + 4 * fk;
+          if (CHK && n >= a.N) continue;
+          uint32_t h[2];
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            float r2[2];
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+              const float gt = acc[i][u][4 * q + e + f] * inv[u];
+              const float up = acc[i + 2][u][4 * q + e + f] * inv[u];
+              r2[f] = gt / (1.0f + expf(-gt)) * up;
+            }
+            h[e / 2] = static_cast<uint32_t>(f32_to_bf16(r2[0])) |
+                       (static_cast<uint32_t>(f32_to_bf16(r2[1])) << 16);
+          }
+          *reinterpret_cast<uint2*>(out + n) = make_uint2(h[0], h[1]);
+        }
+    } else {
+      float ssq = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nb * kBN + wn * 128 + i * 32 + 8 * q + 4 * fk;
+          if (CHK && n >= a.N) continue;
+          const float4 y = make_float4(acc[i][u][4 * q] * inv[u], acc[i][u][4 * q + 1] * inv[u],
+                                       acc[i][u][4 * q + 2] * inv[u], acc[i][u][4 * q + 3] * inv[u]);
+          if (EPI == EPI_STORE_F32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * a.ld_out + n) = y;
+          } else if (EPI == EPI_STORE_ACT) {
+            const uint32_t h0 = static_cast<uint32_t>(f32_to_bf16(y.x)) | (static_cast<uint32_t>(f32_to_bf16(y.y)) << 16);
+            const uint32_t h1 = static_cast<uint32_t>(f32_to_bf16(y.z)) | (static_cast<uint32_t>(f32_to_bf16(y.w)) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow * a.ld_out + n) = make_uint2(h0, h1);
+          } else {  // residual
+            float4* xp = reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * a.ld_out + n);
+            float4 x = *xp;
+            x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+            *xp = x;
+            ssq += (x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w);
+            const uint2 gw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.next_gain) + n);
+            const float g0 = __uint_as_float(gw.x << 16), g1 = __uint_as_float(gw.x & 0xffff0000u);
+            const float g2 = __uint_as_float(gw.y << 16), g3 = __uint_as_float(gw.y & 0xffff0000u);
+            const uint32_t h0 = static_cast<uint32_t>(f32_to_bf16(g0 * x.x)) | (static_cast<uint32_t>(f32_to_bf16(g1 * x.y)) << 16);
+            const uint32_t h1 = static_cast<uint32_t>(f32_to_bf16(g2 * x.z)) | (static_cast<uint32_t>(f32_to_bf16(g3 * x.w)) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.xb_out) + a.xmap.row(a.tok0 + tk[u]) * a.ld_xb + n) =
+                make_uint2(h0, h1);
+            if (a.tap)
+              *reinterpret_cast<float4*>(a.tap + a.tmap.row(a.tok0 + tk[u]) * a.ld_tap + n) = x;
+          }
+        }
+      if (EPI == EPI_RESID && a.ssq_out) {
+        // the two row halves of this token's 128 rows sit in lanes fr, fr + 32
+        ssq += __shfl_xor(ssq, 32, kWave);
+        if (fk == 0) a.ssq_out[orow * kSsqParts + (nb * kBN + wn * 128) / 128] = ssq;
+      }
+    }
+  };
+  const int bno = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
+  const bool full = (nb + 1) * bno <= a.N;
+#pragma unroll
+  for (int u = 0; u < WTM; ++u) {
+    // the ssq shuffle pairs lanes fr and fr + 32, which share tok_ok
+    if (!tok_ok[u]) continue;
+    if (full) store_u(u, std::integral_constant<bool, false>());
+    else store_u(u, std::integral_constant<bool, true>());
+  }
+}
+
+template <int EPI, int MODE>
+hipError_t launch_tile_t(const TileArgs& ta, int items, hipStream_t st) {
+  const size_t sm = static_cast<size_t>(kBN + kBM) * kRowB + (256ull + 4ull * kBM) * 4;
+  const void* fn = reinterpret_cast<const void*>(&gemm_tile_kernel<EPI, MODE>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
+  if (e != hipSuccess) return e;
+  const int per_xcd = (items + 7) / 8;
+  TileArgs t = ta;
+  t.per_xcd = per_xcd;
+  hipLaunchKernelGGL((gemm_tile_kernel<EPI, MODE>), dim3(8 * per_xcd), dim3(256), sm, st, t);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_tile_e(const TileArgs& ta, hipStream_t st) {
+  if (ta.ksplit == 1) return launch_tile_t<EPI, MODE_FULL>(ta, ta.total, st);
+  hipError_t e = launch_tile_t<EPI, MODE_SLICE>(ta, ta.total * ta.ksplit, st);
+  if (e != hipSuccess) return e;
+  return launch_tile_t<EPI, MODE_REDUCE>(ta, ta.total, st);
+}
+
+// Output tiles of each problem and the k split of the launch.
+struct TilePlan {
+  int nbm[2], tiles[2], total, ksplit;
+};
+
+TilePlan plan_tiles(const int* M, const int* N, int nseg, int K, int epi) {
+  TilePlan p{};
+  const int bno = epi == EPI_SWIGLU ? kBN / 2 : kBN;
+  for (int s = 0; s < nseg; ++s) {
+    p.nbm[s] = (M[s] + kBM - 1) / kBM;
+    p.tiles[s] = M[s] > 0 ? ((N[s] + bno - 1) / bno) * p.nbm[s] : 0;
+    p.total += p.tiles[s];
+  }
+  // split K when the tiles leave CUs idle, keeping at least kMinSlice stages a slice
+  p.ksplit = 1;
+  const int nk = K / kBK;
+  if (p.total > 0 && p.total < kSplitTarget) {
+    int sp = (kSplitTarget + p.total - 1) / p.total;
+    const int smax = nk / kMinSlice;
+    sp = sp < smax ? sp : smax;
+    p.ksplit = sp > 1 ? sp : 1;
+  }
+  return p;
+}
+
+}  // namespace
+
+bool gemm_tiled(const GemmArgs& a, bool bf16) {
+  return bf16 && a.M >= kTileMinRows && a.K % kBK == 0;
+}
+
+int gemm_tile_groups(int N) { return (N + kBN - 1) / kBN; }
+
+size_t gemm_tile_scratch(int M0, int M1, int N0, int N1, int K, int epi) {
+  const int M[2] = {M0, M1}, N[2] = {N0, N1};
+  const TilePlan p = plan_tiles(M, N, M1 > 0 ? 2 : 1, K, epi);
+  return p.ksplit > 1 ? static_cast<size_t>(p.total) * p.ksplit * kTileFloats * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_tiled(const GemmArgs* segs, int nseg, int epi, float* part, hipStream_t st) {
+  if (nseg < 1 || nseg > 2) return hipErrorInvalidValue;
+  for (int s = 1; s < nseg; ++s)
+    if (segs[s].K != segs[0].K) return hipErrorInvalidValue;
+  int M[2] = {0, 0}, N[2] = {0, 0};
+  for (int s = 0; s < nseg; ++s) { M[s] = segs[s].M; N[s] = segs[s].N; }
+  const TilePlan p = plan_tiles(M, N, nseg, segs[0].K, epi);
+  if (p.total == 0) return hipSuccess;
+  TileArgs ta{};
+  for (int s = 0; s < nseg; ++s) { ta.seg[s] = segs[s]; ta.nbm[s] = p.nbm[s]; }
+  ta.tiles0 = p.tiles[0];
+  ta.total = p.total;
+  ta.ksplit = part ? p.ksplit : 1;
+  ta.part = part;
+  switch (epi) {
+    case EPI_STORE_F32: return launch_tile_e<EPI_STORE_F32>(ta, st);
+    case EPI_STORE_ACT: return launch_tile_e<EPI_STORE_ACT>(ta, st);
+    case EPI_RESID: return launch_tile_e<EPI_RESID>(ta, st);
+    case EPI_SWIGLU: return launch_tile_e<EPI_SWIGLU>(ta, st);
+    case EPI_ARGMAX: return launch_tile_e<EPI_ARGMAX>(ta, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dlite

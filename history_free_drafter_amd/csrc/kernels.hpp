@@ -46,7 +46,7 @@ hipError_t launch_feature(const FeatureArgs& a, bool bf16, hipStream_t st);
 // out[token, n] = epilogue( s_tok * sum_k W[n, k] * in[token, k] ), tokens
 // 0..M-1 (offset tok0), logical output rows n in [0, N); s_tok = 1/rms of
 // the token when `ssq` is given, else 1.
-enum Epi { EPI_STORE_F32 = 0, EPI_STORE_ACT = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
+enum Epi { EPI_STORE_F32 = 0, EPI_STORE_ACT = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_ARGMAX = 4 };
 
 struct GemmArgs {
   const void* W; long ldw; int N; int K;
@@ -60,9 +60,37 @@ struct GemmArgs {
   // EPI_RESID: x += y, then xb_out = bf16(next_gain * x) and one partial
   // sum of squares of x per workgroup into ssq_out (rows of omap)
   const void* next_gain; void* xb_out; long ld_xb; RowMap xmap; float* ssq_out;
-  float* tap; long ld_tap; RowMap tmap;   // RESID: copy of the updated row
+  float* tap; long ld_tap; RowMap tmap;   // RESID: copy of the updated row; ARGMAX: logits
+  // EPI_ARGMAX (tiled path only): per token and output tile a (max, index)
+  // partial at part_*[(tok0 + token) * G_part + tile]
+  float* part_max; int* part_idx; int G_part;
 };
-hipError_t launch_gemm(const GemmArgs& a, int epi, bool bf16, hipStream_t st);
+// Enqueues the GEMM; M > 32 is split into launches of 32 tokens on the
+// weight-streaming path, or handled in one launch by the tiled path.
+hipError_t launch_gemm(const GemmArgs& a, int epi, bool bf16, float* part, hipStream_t st);
+// Number of partial sums of squares per row that an EPI_RESID launch writes.
+int gemm_resid_parts(const GemmArgs& a, bool bf16);
+
+// Tiled MFMA path for many token rows: up to two independent problems with
+// the same epilogue in one launch.
+// Launches with few output tiles split K over several workgroups: each writes
+// an fp32 partial tile, and a second pass adds the partials in fixed order and
+// applies the epilogue.
+constexpr int kTileMinRows = 64;
+struct TileArgs {
+  GemmArgs seg[2];
+  int nbm[2];          // token tiles per problem
+  int tiles0, total;   // output tiles of problem 0, of the launch
+  int per_xcd;         // work items handed to each of the 8 XCDs
+  int ksplit;          // k slices per output tile
+  float* part;         // [total * ksplit][kTileFloats] partial tiles (ksplit > 1)
+};
+bool gemm_tiled(const GemmArgs& a, bool bf16);
+int gemm_tile_groups(int N);   // output tiles of an EPI_ARGMAX problem of N rows
+// Scratch bytes a tiled launch needs for its partial tiles (0 without split).
+size_t gemm_tile_scratch(int M0, int M1, int N0, int N1, int K, int epi);
+// `part` is the scratch area (at least gemm_tile_scratch bytes).
+hipError_t launch_gemm_tiled(const GemmArgs* segs, int nseg, int epi, float* part, hipStream_t st);
 
 // ------------------------------------------------------------- attention --
 struct AttnArgs {
@@ -116,6 +144,7 @@ struct LmArgs {
   const int32_t* anchors; // [B]: requests with an out-of-range anchor get -1
   int K;                 // tokens per request (token t belongs to request t / K)
   unsigned* counters;
+  float* part;           // partial-tile scratch of the tiled path (gemm_tile_scratch)
 };
 hipError_t launch_lmhead(const LmArgs& a, bool bf16, hipStream_t st);
 int lmhead_groups(int V);

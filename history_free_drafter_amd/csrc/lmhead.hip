@@ -238,6 +238,20 @@ int lmhead_groups(int V) {
 }
 
 hipError_t launch_lmhead(const LmArgs& a0, bool bf16, hipStream_t st) {
+  // many tokens: one tiled MFMA launch writes per-tile partials
+  GemmArgs g{};
+  g.W = a0.W; g.ldw = a0.r; g.N = a0.V; g.K = a0.r;
+  g.src = a0.src; g.ld_src = a0.r; g.smap = RowMap{1, 1, 0}; g.M = a0.M; g.tok0 = a0.tok0;
+  g.tap = a0.tap; g.ld_tap = a0.V; g.tmap = RowMap{1, 1, 0};
+  g.part_max = a0.part_max; g.part_idx = a0.part_idx; g.G_part = gemm_tile_groups(a0.V);
+  if (gemm_tiled(g, bf16)) {
+    hipError_t e = launch_gemm_tiled(&g, 1, EPI_ARGMAX, a0.part, st);
+    if (e != hipSuccess) return e;
+    LmArgs a = a0;
+    a.G = g.G_part;
+    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3((a.M + 3) / 4), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   const dim3 grid(a0.G), block(kWaves * 64);
   for (int t0 = 0; t0 < a0.M; t0 += 32) {
     LmArgs a = a0;

@@ -121,6 +121,18 @@ SMALL = [
            ffn=224, n_layers=3),
     _small("rank512_bf16", B=1, m=2, D=64, n_q=1, n_kv=1, ffn=32, K=2, rank=512,
            vocab=129, n_layers=1),
+    # many token rows (tiled MFMA path): ragged weight tiles (D = 320, vocab
+    # 1000), two token tiles with a ragged tail (288 local rows), fused
+    # query/key/value launch, SwiGLU and vocabulary tiles
+    _small("tiled_bf16", B=48, m=3, D=320, n_q=4, n_kv=2, ffn=384, K=5, rank=128,
+           vocab=1000, n_layers=2),
+    # few output tiles with long K: split-K partial tiles (2 and 4 k slices)
+    # added back in slice order by the reduce pass
+    _small("split_bf16", B=16, m=2, D=512, n_q=4, n_kv=2, d_h=128, ffn=1024, K=4,
+           rank=128, vocab=700, n_layers=2),
+    # one 64-wide k stage everywhere, token counts just above the tile threshold
+    _small("tiled_k64_bf16", B=70, m=1, D=64, n_q=1, n_kv=1, ffn=64, K=1, rank=64,
+           vocab=300, n_layers=1),
 ]
 
 
