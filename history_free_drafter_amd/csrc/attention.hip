@@ -1,190 +1,200 @@
 // Non-causal block attention over the m + 1 + K slots of one request.
 //
-// One workgroup per (request, key/value head); its G = n_q / n_kv waves are the
-// query heads that share that key/value head.  The block is tiny (at most 81
-// keys), so the rotated keys, the values and the rotated queries of all local
-// rows are staged once in LDS (every global load issued up front), and each
-// query head's rows are split over two waves: one lane per key for the scores
-// (query rows read as broadcasts), one lane per row for the fp32 softmax, and
-// one lane per output element for the weighted sums.  Local RoPE positions:
-// context slots and the anchor sit at 0, placeholder k at k (DLite walkthrough,
-// Figure 3 layout); nothing is kept after the call.
+// One workgroup per (request, group of HPW query heads of one key/value head):
+// the block is tiny (at most 81 keys and 17 query rows), so with few requests
+// the work is latency-bound and HPW = 1 spreads it over n_q * B workgroups;
+// with many requests HPW grows so that the heads sharing a key/value head
+// load and rotate it once.  A workgroup loads its key/value head and its query
+// rows once (all global loads issued up front), builds the rotation table for
+// local positions 0..K meanwhile, rotates keys and queries into LDS, then each
+// wave takes whole (head, query row) pairs: scores with one lane per key, the
+// softmax in registers (wave max and sum), and the weighted sum with one lane
+// per output element.  Local RoPE positions: context slots and the
+// anchor sit at 0, placeholder k at k (DLite walkthrough, Figure 3 layout);
+// nothing is kept after the call.
 #include "kernels.hpp"
 
 namespace dlite {
 
 namespace {
 
+constexpr int kThreads = 256;
 constexpr int kMaxD = 128;
-constexpr int kLd = kMaxD + 4;  // padded LDS row: 16-byte aligned, banks spread
-constexpr int kRows = 4;        // query rows per register block
+constexpr int kLd = kMaxD + 4;   // padded LDS row: 16-byte aligned, banks spread
+constexpr int kMaxS = 81;        // m <= 64, K <= 16
+constexpr int kLoads = 12;       // 16-byte global loads per thread and pass
 
-__device__ __forceinline__ float inv_freq(int i, int d, float theta) {
-  return powf(theta, -2.0f * static_cast<float>(i) / static_cast<float>(d));
-}
+__device__ __forceinline__ float rope_pos(int slot, int m) { return slot <= m ? 0.f : static_cast<float>(slot - m); }
 
 template <typename T>
-__global__ __launch_bounds__(1024) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   extern __shared__ __align__(16) float sm[];
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int G = a.n_q / a.n_kv;
-  const int d = a.d_h, half = d / 2;
+  const int hpw = a.n_q / gridDim.x;          // query heads of this workgroup
+  const int h0 = blockIdx.x * hpw, b = blockIdx.y;
+  const int G = a.n_q / a.n_kv, kvh = h0 / G;
+  const int d = a.d_h, half = d / 2, hq = half / 4;   // float4 groups per half row
   const int S = a.m + 1 + a.K, L = 1 + a.K;
   const int Hq = a.n_q * d, Hkv = a.n_kv * d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  const int RG = nw / G;                  // row groups per head
+  constexpr int nw = kThreads / 64;
 
-  float* Ks = sm;                         // [S][kLd]
-  float* Vs = Ks + S * kLd;               // [S][kLd]
-  float* Qs = Vs + S * kLd;               // [G][L][kLd]
-  float* Ps = Qs + G * L * kLd;           // [G][L][S + 1] scores, then probabilities
-  float* rc = Ps + G * L * (S + 1);       // [L][half] cos
-  float* rs = rc + L * half;              // [L][half] sin
+  float* Ks = sm;                    // [S][kLd] rotated keys
+  float* Vs = Ks + S * kLd;          // [S][kLd]
+  float* Qs = Vs + S * kLd;          // [hpw][L][kLd] rotated queries
+  float* Ps = Qs + hpw * L * kLd;    // [hpw][L][S + 1] probabilities
+  float* rc = Ps + hpw * L * (S + 1);   // [L][half] cos
+  float* rs = rc + L * half;         // [L][half] sin
 
-  // every global load up front: keys, values and the G heads' query rows
-  const int vd = d / 4;
-  const int nkv = 2 * S * vd, nq = G * L * vd, nv = nkv + nq;
-  constexpr int kBatch = 16;
-  for (int base = threadIdx.x; base < nv; base += kBatch * blockDim.x) {
-    float4 v[kBatch];
+  // ---- work items: (key row, pair group) | (query row, pair group) |
+  //      (value row, float4); every load issued before any is used
+  const int nk = S * hq, nq = hpw * L * hq, nv = S * (d / 4);
+  const int ntot = nk + nq + nv;
+  const float* Kg = a.KV + static_cast<long>(b) * S * 2 * Hkv + kvh * d;
+  const float* Vg = Kg + Hkv;
+  const float* Qg = a.Q + static_cast<long>(b) * L * Hq + h0 * d;
+  const int npass = (ntot + kLoads * kThreads - 1) / (kLoads * kThreads);   // same for all threads
+  for (int ps = 0; ps < npass; ++ps) {
+    const int base = ps * kLoads * kThreads + threadIdx.x;
+    float4 lo[kLoads], hi[kLoads];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      int idx = base + u * blockDim.x;
-      idx = idx < nv ? idx : nv - 1;   // clamped: every load is issued unconditionally
-      const float* src;
-      if (idx < nkv) {
-        const int which = idx / (S * vd), s = (idx / vd) % S, e = (idx % vd) * 4;
-        src = a.KV + (static_cast<long>(b) * S + s) * 2 * Hkv + which * Hkv + kvh * d + e;
+    for (int q = 0; q < kLoads; ++q) {
+      int it = base + q * kThreads;
+      it = it < ntot ? it : ntot - 1;   // clamped: unconditional loads
+      const float* p;
+      int off2 = 0;
+      if (it < nk) {
+        p = Kg + static_cast<long>(it / hq) * 2 * Hkv + (it % hq) * 4;
+        off2 = half;
+      } else if (it < nk + nq) {
+        const int t = it - nk, qrow = t / hq;   // qrow = head * L + row
+        p = Qg + static_cast<long>(qrow % L) * Hq + (qrow / L) * d + (t % hq) * 4;
+        off2 = half;
       } else {
-        const int t = idx - nkv, hq = t / (L * vd), j = (t / vd) % L, e = (t % vd) * 4;
-        src = a.Q + (static_cast<long>(b) * L + j) * Hq + (kvh * G + hq) * d + e;
+        const int t = it - nk - nq;
+        p = Vg + static_cast<long>(t / (d / 4)) * 2 * Hkv + (t % (d / 4)) * 4;
       }
-      v[u] = *reinterpret_cast<const float4*>(src);
+      lo[q] = *reinterpret_cast<const float4*>(p);
+      hi[q] = *reinterpret_cast<const float4*>(p + off2);
+    }
+    if (ps == 0) {
+      // rotation table for local positions 0..K while the loads are in flight:
+      // frequency i is theta^(-2 i / d)
+      const float l2t = log2f(a.theta);
+      for (int idx = threadIdx.x; idx < L * half; idx += kThreads) {
+        const int p = idx / half, i = idx % half;
+        const float f = exp2f(-2.0f * static_cast<float>(i) / static_cast<float>(d) * l2t);
+        float sn, cs;
+        sincosf(static_cast<float>(p) * f, &sn, &cs);
+        rc[idx] = cs;
+        rs[idx] = sn;
+      }
+      __syncthreads();
     }
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int idx = base + u * blockDim.x;
-      if (idx < nkv) {
-        const int which = idx / (S * vd), s = (idx / vd) % S, e = (idx % vd) * 4;
-        *reinterpret_cast<float4*>((which ? Vs : Ks) + s * kLd + e) = v[u];
-      } else if (idx < nv) {
-        const int t = idx - nkv, hq = t / (L * vd), j = (t / vd) % L, e = (t % vd) * 4;
-        *reinterpret_cast<float4*>(Qs + (hq * L + j) * kLd + e) = v[u];
+    for (int q = 0; q < kLoads; ++q) {
+      const int it = base + q * kThreads;
+      if (it >= ntot) continue;
+      if (it < nk + nq) {
+        // rotate pairs (i, i + half), i = 4 g .. 4 g + 3
+        const bool key = it < nk;
+        const int row = key ? it / hq : (it - nk) / hq, g = key ? it % hq : (it - nk) % hq;
+        const int pos = key ? static_cast<int>(rope_pos(row, a.m)) : row % L;
+        const float* c = rc + pos * half + 4 * g;
+        const float* sn = rs + pos * half + 4 * g;
+        float* dst = (key ? Ks : Qs) + row * kLd + 4 * g;
+        const float x1[4] = {lo[q].x, lo[q].y, lo[q].z, lo[q].w};
+        const float x2[4] = {hi[q].x, hi[q].y, hi[q].z, hi[q].w};
+        float y1[4], y2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y1[e] = x1[e] * c[e] - x2[e] * sn[e];
+          y2[e] = x1[e] * sn[e] + x2[e] * c[e];
+        }
+        *reinterpret_cast<float4*>(dst) = make_float4(y1[0], y1[1], y1[2], y1[3]);
+        *reinterpret_cast<float4*>(dst + half) = make_float4(y2[0], y2[1], y2[2], y2[3]);
+      } else {
+        const int t = it - nk - nq;
+        *reinterpret_cast<float4*>(Vs + (t / (d / 4)) * kLd + (t % (d / 4)) * 4) = lo[q];
       }
-    }
-  }
-  // rotation table for local positions 0..K
-  for (int idx = threadIdx.x; idx < L * half; idx += blockDim.x) {
-    const int p = idx / half, i = idx % half;
-    float sn, cs;
-    sincosf(static_cast<float>(p) * inv_freq(i, d, a.theta), &sn, &cs);
-    rc[idx] = cs;
-    rs[idx] = sn;
-  }
-  __syncthreads();
-  // rotate keys (slot positions) and queries (row j sits at position j) in
-  // place: one row per wave, lane = rotation pair
-  for (int row = wave; row < S + G * L; row += nw) {
-    const int pos = row < S ? (row <= a.m ? 0 : row - a.m) : (row - S) % L;
-    float* p = row < S ? Ks + row * kLd : Qs + (row - S) * kLd;
-    for (int i = lane; i < half; i += 64) {
-      const float cs = rc[pos * half + i], sn = rs[pos * half + i];
-      const float x1 = p[i], x2 = p[i + half];
-      p[i] = x1 * cs - x2 * sn;
-      p[i + half] = x1 * sn + x2 * cs;
     }
   }
   __syncthreads();
 
-  // this wave: head g, rows j = rg, rg + RG, ... in blocks of kRows
-  const int g = wave % G, rg = wave / G;
-  const int h = kvh * G + g;
   const float scale = 1.0f / sqrtf(static_cast<float>(d));
-  const float* Qh = Qs + g * L * kLd;
-  float* Ph = Ps + g * L * (S + 1);
-  const int nrow = (L - rg + RG - 1) / RG;   // rows of this wave
-
-  // scores: lane = key (passes of 64)
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    const int s = s0 + lane;
-    const bool ok = s < S;
-    const float* kr = Ks + (ok ? s : 0) * kLd;
-    for (int r0 = 0; r0 < nrow; r0 += kRows) {
-      float acc[kRows][2];
+  // ---- scores and softmax: wave w takes (head, row) pairs w, w + nw, ...
+  const int lr = L - a.q0;
+  for (int t = wave; t < hpw * lr; t += nw) {
+    const int hh = t / lr, j = a.q0 + t % lr;
+    const float* qr = Qs + (hh * L + j) * kLd;
+    float sc[2];
 #pragma unroll
-      for (int jj = 0; jj < kRows; ++jj) acc[jj][0] = acc[jj][1] = 0.f;
+    for (int ps = 0; ps < 2; ++ps) {
+      const int s = lane + 64 * ps;
+      const bool ok = s < S;
+      const float* kr = Ks + (ok ? s : 0) * kLd;
+      float a0 = 0.f, a1 = 0.f;
       for (int e = 0; e < d; e += 8) {
         const float4 k0 = *reinterpret_cast<const float4*>(kr + e);
         const float4 k1 = *reinterpret_cast<const float4*>(kr + e + 4);
-#pragma unroll
-        for (int jj = 0; jj < kRows; ++jj) {
-          const int ri = r0 + jj < nrow ? r0 + jj : nrow - 1;
-          const float* qr = Qh + (rg + ri * RG) * kLd + e;
-          const float4 q0 = *reinterpret_cast<const float4*>(qr);
-          const float4 q1 = *reinterpret_cast<const float4*>(qr + 4);
-          acc[jj][0] += (q0.x * k0.x + q0.y * k0.y) + (q0.z * k0.z + q0.w * k0.w);
-          acc[jj][1] += (q1.x * k1.x + q1.y * k1.y) + (q1.z * k1.z + q1.w * k1.w);
-        }
+        const float4 q0 = *reinterpret_cast<const float4*>(qr + e);
+        const float4 q1 = *reinterpret_cast<const float4*>(qr + e + 4);
+        a0 += (q0.x * k0.x + q0.y * k0.y) + (q0.z * k0.z + q0.w * k0.w);
+        a1 += (q1.x * k1.x + q1.y * k1.y) + (q1.z * k1.z + q1.w * k1.w);
       }
-#pragma unroll
-      for (int jj = 0; jj < kRows; ++jj)
-        if (r0 + jj < nrow && ok)
-          Ph[(rg + (r0 + jj) * RG) * (S + 1) + s] = (acc[jj][0] + acc[jj][1]) * scale;
+      sc[ps] = ok ? (a0 + a1) * scale : -INFINITY;
+      if (S <= 64) break;   // uniform
     }
+    if (S <= 64) sc[1] = -INFINITY;
+    const float mx = wave_max(fmaxf(sc[0], sc[1]));
+    const float p0 = lane < S ? expf(sc[0] - mx) : 0.f;
+    const float p1 = lane + 64 < S ? expf(sc[1] - mx) : 0.f;
+    const float inv = 1.0f / wave_sum(p0 + p1);
+    float* pr = Ps + (hh * L + j) * (S + 1);
+    if (lane < S) pr[lane] = p0 * inv;
+    if (lane + 64 < S) pr[lane + 64] = p1 * inv;
   }
   __syncthreads();
-  // softmax: one lane per row, serial over the S keys (no cross-lane traffic)
-  if (lane < nrow) {
-    float* pr = Ph + (rg + lane * RG) * (S + 1);
-    float mx = -INFINITY;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, pr[s]);
-    float sum = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float p = expf(pr[s] - mx);
-      pr[s] = p;
-      sum += p;
-    }
-    const float inv = 1.0f / sum;
-    for (int s = 0; s < S; ++s) pr[s] *= inv;
-  }
-  __syncthreads();
-  // outputs: lane = element e (two per lane at d = 128), rows in blocks of kRows
-  for (int e = lane; e < d; e += 64) {
-    for (int r0 = 0; r0 < nrow; r0 += kRows) {
-      float acc[kRows];
-#pragma unroll
-      for (int jj = 0; jj < kRows; ++jj) acc[jj] = 0.f;
-      for (int s = 0; s < S; ++s) {
-        const float vv = Vs[s * kLd + e];
-#pragma unroll
-        for (int jj = 0; jj < kRows; ++jj) {
-          const int ri = r0 + jj < nrow ? r0 + jj : nrow - 1;
-          acc[jj] += Ph[(rg + ri * RG) * (S + 1) + s] * vv;
-        }
+
+  // ---- outputs: wave w takes pairs as above; lane = output element(s)
+  for (int t = wave; t < hpw * lr; t += nw) {
+    const int hh = t / lr, j = a.q0 + t % lr;
+    const float* pr = Ps + (hh * L + j) * (S + 1);
+    T* out = static_cast<T*>(a.out) + (static_cast<long>(b) * L + j) * Hq + (h0 + hh) * d;
+    for (int e = lane; e < d; e += 64) {
+      float acc0 = 0.f, acc1 = 0.f;
+      int s = 0;
+      for (; s + 1 < S; s += 2) {
+        acc0 += pr[s] * Vs[s * kLd + e];
+        acc1 += pr[s + 1] * Vs[(s + 1) * kLd + e];
       }
-#pragma unroll
-      for (int jj = 0; jj < kRows; ++jj) {
-        const int j = rg + (r0 + jj) * RG;
-        if (r0 + jj < nrow && j >= a.q0)
-          static_cast<T*>(a.out)[(static_cast<long>(b) * L + j) * Hq + h * d + e] =
-              Elem<T>::from_f32(acc[jj]);
-      }
+      if (s < S) acc0 += pr[s] * Vs[s * kLd + e];
+      out[e] = Elem<T>::from_f32(acc0 + acc1);
     }
   }
+}
+
+size_t smem_hpw(const AttnArgs& a, int hpw) {
+  const int S = a.m + 1 + a.K, L = 1 + a.K;
+  return (static_cast<size_t>(2 * S * kLd) + hpw * L * kLd + hpw * L * (S + 1) + L * a.d_h) * 4;
+}
+
+// Query heads per workgroup: 1 while requests x key/value heads leave CUs
+// idle, else the largest divisor of the group size whose LDS fits.
+int pick_hpw(const AttnArgs& a) {
+  const int G = a.n_q / a.n_kv;
+  if (static_cast<long>(a.B) * a.n_kv < 256) return 1;
+  for (int h = G; h > 1; --h)
+    if (G % h == 0 && smem_hpw(a, h) <= 160 * 1024) return h;
+  return 1;
 }
 
 }  // namespace
 
-size_t attention_smem(const AttnArgs& a) {
-  const int G = a.n_q / a.n_kv, S = a.m + 1 + a.K, L = 1 + a.K;
-  return (static_cast<size_t>(2 * S * kLd) + G * L * kLd + G * L * (S + 1) + L * a.d_h) * 4;
-}
+size_t attention_smem(const AttnArgs& a) { return smem_hpw(a, pick_hpw(a)); }
 
 hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t st) {
-  const int G = a.n_q / a.n_kv;
-  const int RG = G <= 8 ? 2 : 1;          // split each head's rows over RG waves
-  const dim3 grid(a.n_kv, a.B), block(64 * G * RG);
+  if (a.m + 1 + a.K > kMaxS || a.d_h > kMaxD) return hipErrorInvalidValue;
+  const dim3 grid(a.n_q / pick_hpw(a), a.B), block(kThreads);
   const size_t sm = attention_smem(a);
   const void* fn = bf16 ? reinterpret_cast<const void*>(&attention_kernel<uint16_t>)
                         : reinterpret_cast<const void*>(&attention_kernel<float>);

@@ -130,6 +130,10 @@ SMALL = [
     # added back in slice order by the reduce pass
     _small("split_bf16", B=16, m=2, D=512, n_q=4, n_kv=2, d_h=128, ffn=1024, K=4,
            rank=128, vocab=700, n_layers=2),
+    # many requests x key/value heads: one attention workgroup per key/value
+    # head takes its whole group of 4 query heads
+    _small("grouped_heads_bf16", B=128, m=2, D=128, n_q=8, n_kv=2, ffn=96, K=3, rank=32,
+           vocab=500, n_layers=1),
     # one 64-wide k stage everywhere, token counts just above the tile threshold
     _small("tiled_k64_bf16", B=70, m=1, D=64, n_q=1, n_kv=1, ffn=64, K=1, rank=64,
            vocab=300, n_layers=1),
