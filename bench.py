@@ -28,6 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+CSRC = os.path.join(ROOT, "history_free_drafter_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16
 METRIC = "drafted tokens/s (B·K) for drafter+accept at Qwen3-8B shapes; % HBM/MFMA peak"
 
@@ -88,6 +90,43 @@ def step_costs(w):
     by = sum(v[0] for v in c.values()) + w.B * (w.K + (w.K + 1) + 2) * 4  # + accept
     fl = sum(v[1] for v in c.values())
     return by, fl
+
+
+# -------------------------------------------------------------- HBM traffic ---
+
+def kernel_source_hash():
+    """sha256 over the kernel sources (csrc/*.hip, *.hpp in name order)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def traffic_record(workload, stage):
+    """HBM bytes per launch of a stage's kernel(s) from the committed counter
+    summaries (profiles/*.md, lines 'traffic-record: {json}'), scaled by the
+    copy calibration.  None when no record matches or the kernel sources
+    changed since the counters were taken."""
+    if not os.path.isdir(PROFILES):
+        return None
+    cur = kernel_source_hash()
+    for f in sorted(os.listdir(PROFILES)):
+        if not f.endswith(".md"):
+            continue
+        with open(os.path.join(PROFILES, f)) as fh:
+            for line in fh:
+                if not line.startswith("traffic-record:"):
+                    continue
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("workload") != workload or rec.get("stage") != stage:
+                    continue
+                if rec.get("source_sha256") != cur:
+                    return None
+                return (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]) * 1024.0
+    return None
 
 
 # ----------------------------------------------------------------- HIP events ---
@@ -259,6 +298,7 @@ def main():
         achieved, peak, unit = costs[dom][1] / k_avg / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
     sb, sf = step_costs(w)
     step_s = wall_s / args.steps
+    traffic = traffic_record(w.name, dom)
 
     stages = None
     if args.stages:
@@ -297,7 +337,9 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": bound, "kernel": dom, "achieved": round(achieved, 1),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": None, "avg_launch_us": round(k_avg * 1e6, 2),
+                     "traffic": None if traffic is None else int(traffic),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "avg_launch_us": round(k_avg * 1e6, 2),
                      "algorithmic_bytes": int(costs[dom][0]),
                      "algorithmic_flops": int(costs[dom][1])},
         "cpu_baseline": cpu,

@@ -296,13 +296,7 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
     kv.W = at(lw.wqkv, static_cast<size_t>(Hq) * D * es); kv.N = 2 * Hkv;
     kv.smap = all_slots; kv.qmap = all_slots; kv.M = B * S;
     kv.out = KVb; kv.ld_out = 2 * Hkv; kv.omap = all_slots;
-    if (gemm_tiled(q, bf16) && gemm_tiled(kv, bf16)) {
-      const GemmArgs qkv[2] = {q, kv};   // one launch for both row sets
-      DLITE_LAUNCH(launch_gemm_tiled(qkv, 2, EPI_STORE_F32, TPs, st));
-    } else {
-      DLITE_LAUNCH(launch_gemm(q, EPI_STORE_F32, bf16, TPs, st));
-      DLITE_LAUNCH(launch_gemm(kv, EPI_STORE_F32, bf16, TPs, st));
-    }
+    DLITE_LAUNCH(launch_gemm_pair(q, kv, EPI_STORE_F32, bf16, TPs, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_QKV, false, st, l));
 
     AttnArgs aa{Qb, KVb, AO, B, m, K, d.n_q, d.n_kv, d.d_h, q0, d.rope_theta};

@@ -30,7 +30,10 @@ struct Stage {
 // 16-byte alignment and spreads banks) and every wave reads its fragments
 // from there; otherwise fragments are loaded per unit from global memory.
 template <typename T, int MT, int NS, int EPI, bool BL>
-__global__ __launch_bounds__(512) void gemm_stream_kernel(GemmArgs a) {
+__global__ __launch_bounds__(512) void gemm_stream_kernel(StreamArgs sa) {
+  // workgroups [0, g0) serve problem 0, the rest problem 1
+  const int seg = static_cast<int>(blockIdx.x) < sa.g0 ? 0 : 1;
+  const GemmArgs& a = sa.seg[seg];
   extern __shared__ __align__(16) unsigned char bsm[];
   constexpr int PER = Elem<T>::kPerLane;
   constexpr int KS = PER * 4;                        // k per MFMA step
@@ -44,7 +47,8 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GemmArgs a) {
   const int nwaves = blockDim.x >> 6;
   const int c16 = lane & 15, grp = lane >> 4;
 
-  const long G = gridDim.x, g = blockIdx.x;
+  const long G = seg ? static_cast<long>(gridDim.x) - sa.g0 : sa.g0;
+  const long g = static_cast<long>(blockIdx.x) - (seg ? sa.g0 : 0);
   const int r0 = static_cast<int>((g * a.N) / G);
   const int r1 = static_cast<int>(((g + 1) * a.N) / G);
   const int ntile = (r1 - r0 + 15) >> 4;
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GemmArgs a) {
 }
 
 template <typename T, int MT, int NS, bool BL>
-hipError_t dispatch_epi(const GemmArgs& a, int epi, dim3 grid, dim3 block, size_t sm, hipStream_t st) {
+hipError_t dispatch_epi(const StreamArgs& a, int epi, dim3 grid, dim3 block, size_t sm, hipStream_t st) {
   // the gate/up pair at 32 tokens keeps a 4-step stage (register budget)
   constexpr int NSG = (MT == 2 && NS == 8) ? 4 : NS;
   const void* fn = nullptr;
@@ -271,11 +275,13 @@ hipError_t dispatch_epi(const GemmArgs& a, int epi, dim3 grid, dim3 block, size_
 }
 
 template <typename T, int MT, int NS>
-hipError_t dispatch_bl(const GemmArgs& a, int epi, dim3 grid, dim3 block, hipStream_t st) {
+hipError_t dispatch_bl(const StreamArgs& a, int epi, dim3 grid, dim3 block, hipStream_t st) {
   // stage the token rows in LDS when they fit beside the reduction buffers
   const size_t es = sizeof(T);
   const size_t red = 2ull * 8 * (epi == EPI_SWIGLU ? 2 : 1) * MT * 256 * 4;
-  const size_t sm = static_cast<size_t>(a.M) * (a.K + 8) * es;
+  int mmax = a.seg[0].M;
+  if (grid.x > static_cast<unsigned>(a.g0) && a.seg[1].M > mmax) mmax = a.seg[1].M;
+  const size_t sm = static_cast<size_t>(mmax) * (a.seg[0].K + 8) * es;
   if (sm + red + 1024 <= 160 * 1024) return dispatch_epi<T, MT, NS, true>(a, epi, grid, block, sm, st);
   return dispatch_epi<T, MT, NS, false>(a, epi, grid, block, 0, st);
 }
@@ -296,42 +302,73 @@ int gemm_resid_parts(const GemmArgs& a, bool bf16) {
   return a.N < kSsqParts ? a.N : kSsqParts;
 }
 
-hipError_t launch_gemm(const GemmArgs& a0, int epi, bool bf16, float* part, hipStream_t st) {
-  if (gemm_tiled(a0, bf16)) return launch_gemm_tiled(&a0, 1, epi, part, st);
-  if (epi == EPI_ARGMAX) return hipErrorInvalidValue;
+namespace {
+
+// One launch for up to two problems with the same K and epilogue and at most
+// 32 tokens each; problem 1's workgroups follow problem 0's.
+hipError_t launch_stream(const GemmArgs* segs, int nseg, int epi, bool bf16, hipStream_t st) {
   const int KS = bf16 ? 32 : 16;
-  const int nsteps = a0.K / KS;
+  const int nsteps = segs[0].K / KS;
   // pipeline depth: 8 k-steps per stage when the split allows it, else 4
   int ns = 8;
   int nw8 = pick_waves(nsteps, 8);
   if (!(nsteps % nw8 == 0 && (nsteps / nw8) % 8 == 0)) ns = 4;
-  long G = a0.N < kSsqParts ? a0.N : kSsqParts;
-  const dim3 grid(static_cast<unsigned>(G));
+  StreamArgs sa{};
+  sa.seg[0] = segs[0];
+  sa.seg[1] = nseg > 1 ? segs[1] : segs[0];
+  const int g0 = segs[0].N < kSsqParts ? segs[0].N : kSsqParts;
+  const int g1 = nseg > 1 ? (segs[1].N < kSsqParts ? segs[1].N : kSsqParts) : 0;
+  sa.g0 = g0;
+  const dim3 grid(static_cast<unsigned>(g0 + g1));
+  int mmax = segs[0].M;
+  if (nseg > 1 && segs[1].M > mmax) mmax = segs[1].M;
+  // one epilogue element per thread: at least 4 waves per 16-token tile
+  int nwaves = pick_waves(nsteps, ns);
+  const int minw = mmax <= 16 ? 4 : 8;
+  if (nwaves < minw) nwaves = minw;
+  const dim3 block(nwaves * 64);
+  const bool one = mmax <= 16;
+  if (bf16) {
+    if (ns == 8) return one ? dispatch_bl<uint16_t, 1, 8>(sa, epi, grid, block, st)
+                            : dispatch_bl<uint16_t, 2, 8>(sa, epi, grid, block, st);
+    return one ? dispatch_bl<uint16_t, 1, 4>(sa, epi, grid, block, st)
+               : dispatch_bl<uint16_t, 2, 4>(sa, epi, grid, block, st);
+  }
+  if (ns == 8) return one ? dispatch_bl<float, 1, 8>(sa, epi, grid, block, st)
+                          : dispatch_bl<float, 2, 8>(sa, epi, grid, block, st);
+  return one ? dispatch_bl<float, 1, 4>(sa, epi, grid, block, st)
+             : dispatch_bl<float, 2, 4>(sa, epi, grid, block, st);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& a0, int epi, bool bf16, float* part, hipStream_t st) {
+  if (gemm_tiled(a0, bf16)) return launch_gemm_tiled(&a0, 1, epi, part, st);
+  if (epi == EPI_ARGMAX) return hipErrorInvalidValue;
   for (int t0 = 0; t0 < a0.M; t0 += 32) {
     GemmArgs a = a0;
     a.tok0 = a0.tok0 + t0;
     a.M = (a0.M - t0) < 32 ? (a0.M - t0) : 32;
-    // one epilogue element per thread: at least 4 waves per 16-token tile
-    int nwaves = pick_waves(nsteps, ns);
-    const int minw = a.M <= 16 ? 4 : 8;
-    if (nwaves < minw) nwaves = minw;
-    const dim3 block(nwaves * 64);
-    hipError_t e;
-    const bool one = a.M <= 16;
-    if (bf16) {
-      if (ns == 8) e = one ? dispatch_bl<uint16_t, 1, 8>(a, epi, grid, block, st)
-                           : dispatch_bl<uint16_t, 2, 8>(a, epi, grid, block, st);
-      else e = one ? dispatch_bl<uint16_t, 1, 4>(a, epi, grid, block, st)
-                   : dispatch_bl<uint16_t, 2, 4>(a, epi, grid, block, st);
-    } else {
-      if (ns == 8) e = one ? dispatch_bl<float, 1, 8>(a, epi, grid, block, st)
-                           : dispatch_bl<float, 2, 8>(a, epi, grid, block, st);
-      else e = one ? dispatch_bl<float, 1, 4>(a, epi, grid, block, st)
-                   : dispatch_bl<float, 2, 4>(a, epi, grid, block, st);
-    }
+    const hipError_t e = launch_stream(&a, 1, epi, bf16, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, int epi, bool bf16, float* part,
+                            hipStream_t st) {
+  if (a.K != b.K) return hipErrorInvalidValue;
+  if (gemm_tiled(a, bf16) && gemm_tiled(b, bf16)) {
+    const GemmArgs segs[2] = {a, b};
+    return launch_gemm_tiled(segs, 2, epi, part, st);
+  }
+  if (!gemm_tiled(a, bf16) && !gemm_tiled(b, bf16) && a.M <= 32 && b.M <= 32 && epi != EPI_ARGMAX) {
+    const GemmArgs segs[2] = {a, b};
+    return launch_stream(segs, 2, epi, bf16, st);
+  }
+  const hipError_t e = launch_gemm(a, epi, bf16, part, st);
+  if (e != hipSuccess) return e;
+  return launch_gemm(b, epi, bf16, part, st);
 }
 
 }  // namespace dlite

@@ -45,6 +45,7 @@ constexpr int kBM = 128;        // tokens per workgroup tile
 constexpr int kTileFloats = kBN * kBM;   // one fp32 partial tile
 constexpr int kSplitTarget = 256;        // work items wanted per launch
 constexpr int kMinSlice = 4;             // stages per k slice, at least
+constexpr int kDirectSum = 2;            // slices the epilogue pass adds itself
 
 enum Mode { MODE_FULL = 0, MODE_SLICE = 1, MODE_REDUCE = 2 };
 
@@ -190,8 +191,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
       return;
     }
   } else {
-    // ---- add the k slices of this tile in slice order
-    for (int sl = 0; sl < ta.ksplit; ++sl) {
+    // ---- add the k slices of this tile in slice order (or read slice 0
+    //      when a parallel pass has already added them there)
+    for (int sl = 0; sl < ta.nsum; ++sl) {
       const float4* pp = reinterpret_cast<const float4*>(part_at(sl));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -392,6 +394,22 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
   }
 }
 
+// Adds the k slices of every partial tile into slice 0, in slice order; one
+// thread per 4 floats, spread over the whole chip.
+__global__ __launch_bounds__(256) void slice_sum_kernel(float* part, int tiles, int ksplit) {
+  const long q = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;   // float4 index within all tiles
+  const long per = kTileFloats / 4;
+  if (q >= static_cast<long>(tiles) * per) return;
+  const long t = q / per, i = q % per;
+  float4* base = reinterpret_cast<float4*>(part) + t * ksplit * per + i;
+  float4 acc = base[0];
+  for (int sl = 1; sl < ksplit; ++sl) {
+    const float4 v = base[sl * per];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  base[0] = acc;
+}
+
 template <int EPI, int MODE>
 hipError_t launch_tile_t(const TileArgs& ta, int items, hipStream_t st) {
   const size_t sm = static_cast<size_t>(kBN + kBM) * kRowB + (256ull + 4ull * kBM) * 4;
@@ -410,7 +428,18 @@ hipError_t launch_tile_e(const TileArgs& ta, hipStream_t st) {
   if (ta.ksplit == 1) return launch_tile_t<EPI, MODE_FULL>(ta, ta.total, st);
   hipError_t e = launch_tile_t<EPI, MODE_SLICE>(ta, ta.total * ta.ksplit, st);
   if (e != hipSuccess) return e;
-  return launch_tile_t<EPI, MODE_REDUCE>(ta, ta.total, st);
+  TileArgs tr = ta;
+  tr.nsum = ta.ksplit;
+  if (ta.ksplit > kDirectSum) {
+    // many slices: add them with the whole chip first, the epilogue pass reads one
+    const long f4 = static_cast<long>(ta.total) * (kTileFloats / 4);
+    hipLaunchKernelGGL(slice_sum_kernel, dim3(static_cast<unsigned>((f4 + 255) / 256)), dim3(256), 0, st,
+                       ta.part, ta.total, ta.ksplit);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    tr.nsum = 1;
+  }
+  return launch_tile_t<EPI, MODE_REDUCE>(tr, ta.total, st);
 }
 
 // Output tiles of each problem and the k split of the launch.

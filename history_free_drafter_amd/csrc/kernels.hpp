@@ -68,6 +68,16 @@ struct GemmArgs {
 // Enqueues the GEMM; M > 32 is split into launches of 32 tokens on the
 // weight-streaming path, or handled in one launch by the tiled path.
 hipError_t launch_gemm(const GemmArgs& a, int epi, bool bf16, float* part, hipStream_t st);
+// Two problems with the same K and epilogue (e.g. query rows of the local
+// tokens and key/value rows of every slot), in one launch where the paths allow.
+hipError_t launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, int epi, bool bf16, float* part,
+                            hipStream_t st);
+// Weight-streaming kernel arguments: workgroups [0, g0) serve seg[0], the
+// rest seg[1].
+struct StreamArgs {
+  GemmArgs seg[2];
+  int g0;
+};
 // Number of partial sums of squares per row that an EPI_RESID launch writes.
 int gemm_resid_parts(const GemmArgs& a, bool bf16);
 
@@ -83,6 +93,7 @@ struct TileArgs {
   int tiles0, total;   // output tiles of problem 0, of the launch
   int per_xcd;         // work items handed to each of the 8 XCDs
   int ksplit;          // k slices per output tile
+  int nsum;            // slices the epilogue pass adds (ksplit, or 1 once pre-added)
   float* part;         // [total * ksplit][kTileFloats] partial tiles (ksplit > 1)
 };
 bool gemm_tiled(const GemmArgs& a, bool bf16);

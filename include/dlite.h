@@ -107,7 +107,9 @@ typedef struct dlite_weights {
 
 /*
  * Optional fp32 copies of intermediate tensors, for checking.  Any member may
- * be NULL; the same kernels run either way (the copy is a predicated store).
+ * be NULL.  z, x, state and logits are predicated stores of the kernels that
+ * run either way; hidden (which the fast path never forms in fp32: the final
+ * RMSNorm is folded into the GEMMs around it) adds one small kernel.
  *   z       [B, m, D]               normalised, depth-embedded feature slots
  *   x       [n_layers, B, 1 + K, D] anchor + placeholder residual stream after
  *                                   each layer (the anchor row of the last
