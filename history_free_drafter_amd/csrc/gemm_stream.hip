@@ -42,6 +42,7 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(StreamArgs sa) {
   // per tile: nwaves * NP * MT * 256 partials, nwaves <= 8
   __shared__ float red[2][8 * NP * MT * 256];
   __shared__ float inv_rms[32];
+  __shared__ uint4 wbuf[8 * 16 * NS * 4];   // per wave: 16 rows x NS * 4 chunks
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
@@ -99,19 +100,34 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(StreamArgs sa) {
   // chunk order rotated by workgroup so that workgroups read different
   // activation lines at any moment
   const int crot = static_cast<int>(g % nchunk);
+  // Weight loads are row-contiguous: raw load i of a unit covers rows
+  // i * RPI + lane / LPR of the 16-row tile, 16 bytes at chunk lane % LPR of
+  // the unit's k range (NS k-steps); compute() turns them into MFMA fragments
+  // through the wave's LDS buffer.
+  constexpr int LPR = NS * 4;           // 16-byte chunks of one row per unit
+  constexpr int RPI = 64 / LPR;         // rows per load instruction
+  const int rt = lane / LPR, cl = lane % LPR;
   auto issue = [&](int p, Stage<T, NP, MT, NS>& st) {
     const int t = p / nchunk, c = (p % nchunk + crot) % nchunk;
-    int row = r0 + t * 16 + c16;
-    row = row < r1 ? row : r1 - 1;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      int s = s0 + c * NS + i;
-      const int slast = s1 > 0 ? s1 - 1 : 0;
+    const int slast = s1 > 0 ? s1 - 1 : 0;
+    {
+      int s = s0 + c * NS + (cl >> 2);
       s = s < s1 ? s : slast;
-      const long k = static_cast<long>(s) * KS + grp * PER;
+      const long ka = static_cast<long>(s) * KS + (cl & 3) * PER;
 #pragma unroll
-      for (int q = 0; q < NP; ++q) st.a[q][i] = ld_stream(W + (row + q * a.pair_off) * a.ldw + k);
-      if (!BL) {
+      for (int i = 0; i < NS; ++i) {
+        int row = r0 + t * 16 + i * RPI + rt;
+        row = row < r1 ? row : r1 - 1;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) st.a[q][i] = ld_stream(W + (row + q * a.pair_off) * a.ldw + ka);
+      }
+    }
+    if (!BL) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        int s = s0 + c * NS + i;
+        s = s < s1 ? s : slast;
+        const long k = static_cast<long>(s) * KS + grp * PER;
 #pragma unroll
         for (int u = 0; u < MT; ++u)
           if (tok_ok[u]) st.b[u][i] = *reinterpret_cast<const uint4*>(X + srow[u] * a.ld_src + k);
@@ -128,25 +144,39 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(StreamArgs sa) {
   };
   zero_acc();
 
+  // the wave's 16 x LPR chunk buffer; chunk j of tile row r sits at
+  // position j ^ r, so both the row-wise writes and the column-wise fragment
+  // reads (16 rows, one chunk) hit distinct banks
+  uint4* wb = wbuf + wave * (16 * LPR);
   auto compute = [&](int p, const Stage<T, NP, MT, NS>& st) {
     const int c = (p % nchunk + crot) % nchunk;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const bool ok = s0 + c * NS + i < s1;
+    for (int q = 0; q < NP; ++q) {
 #pragma unroll
-      for (int u = 0; u < MT; ++u) {
-        uint4 bv;
-        if (BL) {
-          const int s = s0 + c * NS + i;
-          const int sc = s < s1 ? s : (s1 > 0 ? s1 - 1 : 0);
-          const int tok = tok_ok[u] ? u * 16 + c16 : 0;
-          bv = *reinterpret_cast<const uint4*>(Bs + tok * ldb + sc * KS + grp * PER);
-        } else {
-          bv = st.b[u][i];
+      for (int i = 0; i < NS; ++i) {
+        const int rr = i * RPI + rt;
+        wb[rr * LPR + (cl ^ rr)] = st.a[q][i];
+      }
+      uint4 fa[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) fa[i] = wb[c16 * LPR + ((i * 4 + grp) ^ c16)];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const bool ok = s0 + c * NS + i < s1;
+#pragma unroll
+        for (int u = 0; u < MT; ++u) {
+          uint4 bv;
+          if (BL) {
+            const int s = s0 + c * NS + i;
+            const int sc = s < s1 ? s : (s1 > 0 ? s1 - 1 : 0);
+            const int tok = tok_ok[u] ? u * 16 + c16 : 0;
+            bv = *reinterpret_cast<const uint4*>(Bs + tok * ldb + sc * KS + grp * PER);
+          } else {
+            bv = st.b[u][i];
+          }
+          bv = (ok && tok_ok[u]) ? bv : make_uint4(0, 0, 0, 0);
+          acc[q][u] = mma_step(fa[i], bv, acc[q][u], T());
         }
-        bv = (ok && tok_ok[u]) ? bv : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < NP; ++q) acc[q][u] = mma_step(st.a[q][i], bv, acc[q][u], T());
       }
     }
   };
@@ -248,10 +278,12 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(StreamArgs sa) {
   }
 }
 
-template <typename T, int MT, int NS, bool BL>
+template <typename T, int MT, int NS0, bool BL>
 hipError_t dispatch_epi(const StreamArgs& a, int epi, dim3 grid, dim3 block, size_t sm, hipStream_t st) {
-  // the gate/up pair at 32 tokens keeps a 4-step stage (register budget)
-  constexpr int NSG = (MT == 2 && NS == 8) ? 4 : NS;
+  // register budget: two token tiles without LDS staging keep 4-step stages,
+  // and so does the gate/up pair unless its token rows sit in LDS with one tile
+  constexpr int NS = (!BL && MT == 2) ? 4 : NS0;
+  constexpr int NSG = ((MT == 2 || !BL) && NS == 8) ? 4 : NS;
   const void* fn = nullptr;
   switch (epi) {
     case EPI_STORE_F32: fn = reinterpret_cast<const void*>(&gemm_stream_kernel<T, MT, NS, EPI_STORE_F32, BL>); break;
@@ -278,7 +310,8 @@ template <typename T, int MT, int NS>
 hipError_t dispatch_bl(const StreamArgs& a, int epi, dim3 grid, dim3 block, hipStream_t st) {
   // stage the token rows in LDS when they fit beside the reduction buffers
   const size_t es = sizeof(T);
-  const size_t red = 2ull * 8 * (epi == EPI_SWIGLU ? 2 : 1) * MT * 256 * 4;
+  const size_t red = 2ull * 8 * (epi == EPI_SWIGLU ? 2 : 1) * MT * 256 * 4 +
+                     8ull * 16 * NS * 4 * 16;   // + weight transposition buffers
   int mmax = a.seg[0].M;
   if (grid.x > static_cast<unsigned>(a.g0) && a.seg[1].M > mmax) mmax = a.seg[1].M;
   const size_t sm = static_cast<size_t>(mmax) * (a.seg[0].K + 8) * es;
