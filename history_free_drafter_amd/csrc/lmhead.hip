@@ -141,13 +141,16 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_kernel(LmArgs a) {
 // Pipelined variant for at most 16 tokens: each wave streams its tiles
 // (16 vocabulary rows, all r columns) through a two-stage register pipeline
 // so that the next tile's 16 KB is in flight while the current one is
-// multiplied and reduced.
+// multiplied and reduced.  Rows are read whole (one contiguous row per load
+// instruction) and transposed into MFMA fragments through LDS.
 template <typename T>
 __global__ __launch_bounds__(kWaves * 64) void lmhead_pipe_kernel(LmArgs a) {
   constexpr int PER = Elem<T>::kPerLane;
   constexpr int KS = PER * 4;
+  static_assert(kMaxSteps == 16, "one raw load per tile row");
   __shared__ float sv[kWaves][16];
   __shared__ int si[kWaves][16];
+  __shared__ uint4 wbuf[kWaves][16 * 64];   // per wave: 16 rows x 64 chunks
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, grp = lane >> 4;
@@ -169,24 +172,35 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_pipe_kernel(LmArgs a) {
     b[s] = *reinterpret_cast<const uint4*>(X + xrow + sc * KS + grp * PER);
   }
 
+  // Weight rows are loaded whole: raw load i of a tile is vocabulary row
+  // t * 16 + i, lane j holding its 16-byte chunk j (rows are at most 64
+  // chunks); consume() turns the chunks into MFMA fragments through the
+  // wave's LDS buffer, chunk j of tile row i at position j ^ i.
+  const int lpr = nsteps * 4;                       // chunks per row
+  const int jc = lane < lpr ? lane : lpr - 1;
   auto issue = [&](int t, uint4 (&st)[kMaxSteps]) {
-    int row = r0 + t * 16 + c16;
-    row = row < r1 ? row : r1 - 1;
-    const T* wr = W + static_cast<long>(row) * a.r + grp * PER;
 #pragma unroll
-    for (int s = 0; s < kMaxSteps; ++s) {
-      const int sc = s < nsteps ? s : nsteps - 1;
-      st[s] = ld_stream(wr + sc * KS);
+    for (int i = 0; i < 16; ++i) {
+      int row = r0 + t * 16 + i;
+      row = row < r1 ? row : r1 - 1;
+      st[i] = ld_stream(W + static_cast<long>(row) * a.r + jc * PER);
     }
   };
 
   float bv = -INFINITY;
   int bi = 0x7fffffff;
+  uint4* wb = wbuf[wave];
   auto consume = [&](int t, const uint4 (&st)[kMaxSteps]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (lane < lpr) wb[i * 64 + (lane ^ i)] = st[i];
     floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kMaxSteps; ++s)
-      if (s < nsteps) acc = mma_step(st[s], tok_ok ? b[s] : make_uint4(0, 0, 0, 0), acc, T());
+      if (s < nsteps) {
+        const uint4 fa = wb[c16 * 64 + ((s * 4 + grp) ^ c16)];
+        acc = mma_step(fa, tok_ok ? b[s] : make_uint4(0, 0, 0, 0), acc, T());
+      }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int vr = r0 + t * 16 + grp * 4 + i;
