@@ -315,7 +315,11 @@ hipError_t dispatch_bl(const StreamArgs& a, int epi, dim3 grid, dim3 block, hipS
   int mmax = a.seg[0].M;
   if (grid.x > static_cast<unsigned>(a.g0) && a.seg[1].M > mmax) mmax = a.seg[1].M;
   const size_t sm = static_cast<size_t>(mmax) * (a.seg[0].K + 8) * es;
-  if (sm + red + 1024 <= 160 * 1024) return dispatch_epi<T, MT, NS, true>(a, epi, grid, block, sm, st);
+  // staging pays off only when a workgroup owns at least one full tile of
+  // weight rows; with fewer, the token loads are better overlapped with them
+  const bool full_tiles = a.seg[0].N >= 16 * static_cast<int>(a.g0);
+  if (full_tiles && sm + red + 1024 <= 160 * 1024)
+    return dispatch_epi<T, MT, NS, true>(a, epi, grid, block, sm, st);
   return dispatch_epi<T, MT, NS, false>(a, epi, grid, block, 0, st);
 }
 
