@@ -44,10 +44,13 @@ constexpr int kRowB = kBK * 2;  // bytes of one LDS row
 constexpr int kBM = 128;        // tokens per workgroup tile
 constexpr int kTileFloats = kBN * kBM;   // one fp32 partial tile
 constexpr int kSplitTarget = 256;        // work items wanted per launch
+constexpr int kSplitBelow = 128;         // split K only for launches with fewer tiles
 constexpr int kMinSlice = 4;             // stages per k slice, at least
 constexpr int kDirectSum = 2;            // slices the epilogue pass adds itself
 
-enum Mode { MODE_FULL = 0, MODE_SLICE = 1, MODE_REDUCE = 2 };
+// MODE_REDUCE1: the reduce pass with one wave per workgroup (4 workgroups
+// per output tile) for epilogues that need no exchange between waves.
+enum Mode { MODE_FULL = 0, MODE_SLICE = 1, MODE_REDUCE = 2, MODE_REDUCE1 = 3 };
 
 __device__ __forceinline__ floatx16 mma32(uint4 a, uint4 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -92,9 +95,12 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
   //      fastest, then the k slice, then the weight tile, so the token tiles
   //      of one weight slice run side by side on one XCD
   const int S = MODE == MODE_SLICE ? ta.ksplit : 1;
+  constexpr int Q4 = MODE == MODE_REDUCE1 ? 4 : 1;   // workgroups per tile
   const int bid = blockIdx.x;
   int t = (bid & 7) * ta.per_xcd + (bid >> 3);
-  if (t >= ta.total * S) return;
+  if (t >= ta.total * S * Q4) return;
+  const int quarter = t % Q4;
+  t /= Q4;
   const int sg = t < ta.tiles0 * S ? 0 : 1;
   if (sg) t -= ta.tiles0 * S;
   const GemmArgs& a = ta.seg[sg];
@@ -104,7 +110,10 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
   const int m0 = mb * BM;
   const int tile = (sg ? ta.tiles0 : 0) + nb * nbm + mb;   // index of the output tile
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // tid: the thread's place in the 4-wave tile layout (one wave per
+  // workgroup in MODE_REDUCE1)
+  const int tid = MODE == MODE_REDUCE1 ? quarter * 64 + static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x);
+  const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   const int fr = lane & 31, fk = lane >> 5;
 
@@ -119,7 +128,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
   // partial tile layout: float4 j of thread tid at (j * 256 + tid) * 4
   auto part_at = [&](int sl) { return ta.part + (static_cast<long>(tile) * ta.ksplit + sl) * kTileFloats; };
 
-  if (MODE != MODE_REDUCE) {
+  if (MODE == MODE_FULL || MODE == MODE_SLICE) {
     const uint16_t* W = static_cast<const uint16_t*>(a.W);
     const uint16_t* X = static_cast<const uint16_t*>(a.src);
     // ---- stage loads: thread covers rows (tid / 8) + 32 i, 16-byte chunk tid % 8
@@ -210,8 +219,21 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
     }
   }
 
-  // ---- partial sums of squares of this tile's tokens (TPT threads per token)
-  if (a.ssq) {
+  // ---- partial sums of squares of this tile's tokens (TPT threads per token;
+  //      in MODE_REDUCE1 one thread per token of the wave's half)
+  if (a.ssq && MODE == MODE_REDUCE1) {
+    const int tl = wm * (BM / 2) + lane;
+    float v = 0.f;
+    const int tk = m0 + tl;
+    if (tk < a.M) {
+      const long prow = a.qmap.row(a.tok0 + tk);
+      const int np = (prow % a.ssq_group) < a.ssq_split ? a.np_lo : a.np_hi;
+      const float* sp = a.ssq + prow * kSsqParts;
+      for (int j = 0; j < np; ++j) v += sp[j];
+    }
+    red[tl] = v;
+    red[BM + tl] = 0.f;
+  } else if (a.ssq) {
     const int tl = tid % BM, part = tid / BM;
     float v = 0.f;
     const int tk = m0 + tl;
@@ -244,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
     }
   }
 
-  if (EPI == EPI_ARGMAX) {
+  if (EPI == EPI_ARGMAX && MODE != MODE_REDUCE1) {
     // a lane's values come in increasing row order, so "strictly greater"
     // keeps the lowest index among equal maxima; rows past N only exist in
     // the last weight tile
@@ -419,7 +441,7 @@ hipError_t launch_tile_t(const TileArgs& ta, int items, hipStream_t st) {
   const int per_xcd = (items + 7) / 8;
   TileArgs t = ta;
   t.per_xcd = per_xcd;
-  hipLaunchKernelGGL((gemm_tile_kernel<EPI, MODE>), dim3(8 * per_xcd), dim3(256), sm, st, t);
+  hipLaunchKernelGGL((gemm_tile_kernel<EPI, MODE>), dim3(8 * per_xcd), dim3(MODE == MODE_REDUCE1 ? 64 : 256), sm, st, t);
   return hipGetLastError();
 }
 
@@ -439,7 +461,8 @@ hipError_t launch_tile_e(const TileArgs& ta, hipStream_t st) {
     if (e != hipSuccess) return e;
     tr.nsum = 1;
   }
-  return launch_tile_t<EPI, MODE_REDUCE>(tr, ta.total, st);
+  if constexpr (EPI == EPI_ARGMAX) return launch_tile_t<EPI, MODE_REDUCE>(tr, ta.total, st);
+  else return launch_tile_t<EPI, MODE_REDUCE1>(tr, ta.total * 4, st);
 }
 
 // Output tiles of each problem and the k split of the launch.
@@ -458,7 +481,7 @@ TilePlan plan_tiles(const int* M, const int* N, int nseg, int K, int epi) {
   // split K when the tiles leave CUs idle, keeping at least kMinSlice stages a slice
   p.ksplit = 1;
   const int nk = K / kBK;
-  if (p.total > 0 && p.total < kSplitTarget) {
+  if (p.total > 0 && p.total < kSplitBelow) {
     int sp = (kSplitTarget + p.total - 1) / p.total;
     const int smax = nk / kMinSlice;
     sp = sp < smax ? sp : smax;

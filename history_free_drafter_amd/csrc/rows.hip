@@ -30,8 +30,10 @@ __device__ __forceinline__ float ld(const void* p, long i) {
   return Elem<T>::to_f32(static_cast<const T*>(p)[i]);
 }
 
-// One workgroup per slot (b, s).  Writes the fp32 slot row, its sum of
-// squares (slot 0 of the row's partials) and the pre-gained GEMM input rows:
+// One workgroup per slot (b, s).  Writes the row's sum of squares (slot 0 of
+// the row's partials), the fp32 residual row of anchor and placeholder slots
+// (context slots are key/value inputs only and never updated), and the
+// pre-gained GEMM input rows:
 // context slots for every layer (they do not change between layers), anchor
 // and placeholder rows for the first layer.  Each thread holds its share of
 // the row in registers (16-byte loads, all issued before the reduction).
@@ -107,10 +109,12 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
         v[t] = add ? gz[t] * ((h[t] + e[t]) * inv) : h[t];
         ss += v[t] * v[t];
       }
-      float* xo = x + idx * PER;
+      if (!add) {   // residual stream: anchor and placeholder rows only
+        float* xo = x + idx * PER;
 #pragma unroll
-      for (int t = 0; t < PER; t += 4)
-        *reinterpret_cast<float4*>(xo + t) = make_float4(v[t], v[t + 1], v[t + 2], v[t + 3]);
+        for (int t = 0; t < PER; t += 4)
+          *reinterpret_cast<float4*>(xo + t) = make_float4(v[t], v[t + 1], v[t + 2], v[t + 3]);
+      }
       if (add && a.tap_z) {
         float* tz = a.tap_z + (static_cast<long>(b) * a.m + s) * a.D + idx * PER;
 #pragma unroll
