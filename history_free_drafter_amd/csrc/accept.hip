@@ -14,14 +14,40 @@ __global__ __launch_bounds__(256) void accept_kernel(const int32_t* __restrict__
                                                      const int32_t* __restrict__ tgt,
                                                      int B, int K, int32_t* __restrict__ A,
                                                      int32_t* __restrict__ next) {
+  constexpr int kChunk = 16;
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
   const int32_t* c = cand + static_cast<long>(b) * K;
   const int32_t* t = tgt + static_cast<long>(b) * (K + 1);
-  int n = 0;
-  while (n < K && c[n] == t[n]) ++n;
+  // positions are compared kChunk at a time: all loads of a chunk are issued
+  // before any comparison, so a block costs one memory round trip, not K
+  const int bonus = t[K];
+  int n = 0, nv = bonus;
+  for (int k0 = 0; k0 < K; k0 += kChunk) {
+    int cv[kChunk], tv[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const int k = k0 + i < K ? k0 + i : K - 1;
+      cv[i] = c[k];
+      tv[i] = t[k];
+    }
+    int run = 0;
+    bool broken = false;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      broken = broken || k0 + i >= K || cv[i] != tv[i];
+      run += broken ? 0 : 1;
+    }
+    n += run;
+    if (run < kChunk) {
+      // the first failing position lies in this chunk (or is the bonus slot)
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) nv = (i == run && k0 + i < K) ? tv[i] : nv;
+      break;
+    }
+  }
   A[b] = n;
-  if (next) next[b] = t[n];
+  if (next) next[b] = nv;
 }
 
 }  // namespace

@@ -20,6 +20,9 @@ namespace dlite {
 
 namespace {
 
+// residual tiles whose elements are fetched at kernel start
+constexpr int kResTiles = 2;
+
 template <typename T, int NP, int MT, int NS>
 struct Stage {
   uint4 a[NP][NS];
@@ -181,23 +184,9 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(StreamArgs sa) {
     }
   };
 
-  // 1/rms of each token from the producer's partial sums of squares
-  if (a.ssq) {
-    for (int tl = wave; tl < MT * 16; tl += nwaves) {
-      float v = 0.f;
-      if (tl < a.M) {
-        const long prow = a.qmap.row(a.tok0 + tl);
-        const int np = (prow % a.ssq_group) < a.ssq_split ? a.np_lo : a.np_hi;
-        const float* sp = a.ssq + prow * kSsqParts;
-        for (int j = lane; j < np; j += 64) v += sp[j];
-      }
-      v = wave_sum(v);
-      if (lane == 0) inv_rms[tl] = 1.0f / sqrtf(v / static_cast<float>(a.norm_len) + a.eps);
-    }
-  }
-
   // per-thread running sum of squares of the updated residual rows
   float ssq_loc = 0.f;
+  float xres[kResTiles];
   const int per_wave = NP * MT * 256;
 
   auto finish_tile = [&](int t) {
@@ -234,7 +223,10 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(StreamArgs sa) {
           static_cast<T*>(a.out)[orow * a.ld_out + row] = Elem<T>::from_f32(v0);
         } else if (EPI == EPI_RESID) {
           float* x = static_cast<float*>(a.out) + orow * a.ld_out + row;
-          const float nv = *x + v0;
+          float xo = 0.f;
+#pragma unroll
+          for (int tt = 0; tt < kResTiles; ++tt) xo = tt == t ? xres[tt] : xo;
+          const float nv = (t < kResTiles ? xo : *x) + v0;
           *x = nv;
           ssq_loc += nv * nv;
           const T* ng = static_cast<const T*>(a.next_gain);
@@ -249,13 +241,41 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(StreamArgs sa) {
     }
   };
 
+  // 1/rms of each token from the producer's partial sums of squares
+  auto token_scales = [&]() {
+    if (!a.ssq) return;
+    for (int tl = wave; tl < MT * 16; tl += nwaves) {
+      float v = 0.f;
+      if (tl < a.M) {
+        const long prow = a.qmap.row(a.tok0 + tl);
+        const int np = (prow % a.ssq_group) < a.ssq_split ? a.np_lo : a.np_hi;
+        const float* sp = a.ssq + prow * kSsqParts;
+        for (int j = lane; j < np; j += 64) v += sp[j];
+      }
+      v = wave_sum(v);
+      if (lane == 0) inv_rms[tl] = 1.0f / sqrtf(v / static_cast<float>(a.norm_len) + a.eps);
+    }
+  };
+
   // two-stage pipeline over (tile, chunk) units
-  // the first two stages of weights are requested before the token rows are
-  // staged, so both round trips overlap
+  // the first two stages of weights are requested before anything else (token
+  // rows, residual elements, sums of squares), so all those round trips overlap
   Stage<T, NP, MT, NS> st0, st1;
   if (nunit > 0) issue(0, st0);
   if (nunit > 1) issue(1, st1);
+  // the residual elements this thread updates, requested behind the weights
+  if (EPI == EPI_RESID) {
+    const int e = threadIdx.x;
+#pragma unroll
+    for (int t = 0; t < kResTiles; ++t) {
+      xres[t] = 0.f;
+      const int row = r0 + t * 16 + (e & 15), tokl = e >> 4;
+      if (t < ntile && e < MT * 256 && row < r1 && tokl < a.M)
+        xres[t] = static_cast<const float*>(a.out)[a.omap.row(a.tok0 + tokl) * a.ld_out + row];
+    }
+  }
   if (BL) stage_tokens();
+  token_scales();
   for (int p = 0; p < nunit; p += 2) {
     if (p + 1 < nunit && p > 0) issue(p + 1, st1);
     compute(p, st0);
@@ -278,8 +298,34 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(StreamArgs sa) {
   }
 }
 
+// Workgroups of one launch are meant to be resident together: a second round
+// would repeat the whole load latency for a sliver of the rows.  When the
+// wanted grid exceeds what the device holds at once, the rows are spread over
+// fewer workgroups, shared between the two problems in proportion to their
+// rows.  Residual epilogues keep their grid: it fixes how many partial sums of
+// squares the next map reads (at most kSsqParts, one per workgroup, which fits
+// on the device in one round).
+void fit_resident(const void* fn, int threads, size_t sm, const StreamArgs& a, int& g0, int& g1) {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, threads, sm) != hipSuccess || per < 1)
+    return;
+  const long cap = static_cast<long>(cus) * per;
+  if (g0 + g1 <= cap) return;
+  if (g1 == 0) {
+    g0 = static_cast<int>(cap);
+    return;
+  }
+  const long n0 = a.seg[0].N, n1 = a.seg[1].N;
+  long c0 = cap * n0 / (n0 + n1);
+  c0 = c0 < 1 ? 1 : (c0 > cap - 1 ? cap - 1 : c0);
+  g0 = static_cast<int>(c0 < g0 ? c0 : g0);
+  g1 = static_cast<int>(cap - c0 < g1 ? cap - c0 : g1);
+}
+
 template <typename T, int MT, int NS0, bool BL>
-hipError_t dispatch_epi(const StreamArgs& a, int epi, dim3 grid, dim3 block, size_t sm, hipStream_t st) {
+hipError_t dispatch_epi(StreamArgs a, int epi, int g1, dim3 block, size_t sm, hipStream_t st) {
   // register budget: two token tiles without LDS staging keep 4-step stages,
   // and so does the gate/up pair unless its token rows sit in LDS with one tile
   constexpr int NS = (!BL && MT == 2) ? 4 : NS0;
@@ -296,6 +342,10 @@ hipError_t dispatch_epi(const StreamArgs& a, int epi, dim3 grid, dim3 block, siz
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
     if (e != hipSuccess) return e;
   }
+  int g0 = a.g0;
+  if (epi != EPI_RESID) fit_resident(fn, static_cast<int>(block.x), sm, a, g0, g1);
+  a.g0 = g0;
+  const dim3 grid(static_cast<unsigned>(g0 + g1));
   switch (epi) {
     case EPI_STORE_F32: hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NS, EPI_STORE_F32, BL>), grid, block, sm, st, a); break;
     case EPI_STORE_ACT: hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NS, EPI_STORE_ACT, BL>), grid, block, sm, st, a); break;
@@ -307,20 +357,20 @@ hipError_t dispatch_epi(const StreamArgs& a, int epi, dim3 grid, dim3 block, siz
 }
 
 template <typename T, int MT, int NS>
-hipError_t dispatch_bl(const StreamArgs& a, int epi, dim3 grid, dim3 block, hipStream_t st) {
+hipError_t dispatch_bl(const StreamArgs& a, int epi, int g1, dim3 block, hipStream_t st) {
   // stage the token rows in LDS when they fit beside the reduction buffers
   const size_t es = sizeof(T);
   const size_t red = 2ull * 8 * (epi == EPI_SWIGLU ? 2 : 1) * MT * 256 * 4 +
                      8ull * 16 * NS * 4 * 16;   // + weight transposition buffers
   int mmax = a.seg[0].M;
-  if (grid.x > static_cast<unsigned>(a.g0) && a.seg[1].M > mmax) mmax = a.seg[1].M;
+  if (g1 > 0 && a.seg[1].M > mmax) mmax = a.seg[1].M;
   const size_t sm = static_cast<size_t>(mmax) * (a.seg[0].K + 8) * es;
   // staging pays off only when a workgroup owns at least one full tile of
   // weight rows; with fewer, the token loads are better overlapped with them
   const bool full_tiles = a.seg[0].N >= 16 * static_cast<int>(a.g0);
   if (full_tiles && sm + red + 1024 <= 160 * 1024)
-    return dispatch_epi<T, MT, NS, true>(a, epi, grid, block, sm, st);
-  return dispatch_epi<T, MT, NS, false>(a, epi, grid, block, 0, st);
+    return dispatch_epi<T, MT, NS, true>(a, epi, g1, block, sm, st);
+  return dispatch_epi<T, MT, NS, false>(a, epi, g1, block, 0, st);
 }
 
 // Waves per workgroup: the first count in {8, 4, 2, 1} that splits the k-steps
@@ -356,7 +406,6 @@ hipError_t launch_stream(const GemmArgs* segs, int nseg, int epi, bool bf16, hip
   const int g0 = segs[0].N < kSsqParts ? segs[0].N : kSsqParts;
   const int g1 = nseg > 1 ? (segs[1].N < kSsqParts ? segs[1].N : kSsqParts) : 0;
   sa.g0 = g0;
-  const dim3 grid(static_cast<unsigned>(g0 + g1));
   int mmax = segs[0].M;
   if (nseg > 1 && segs[1].M > mmax) mmax = segs[1].M;
   // one epilogue element per thread: at least 4 waves per 16-token tile
@@ -366,15 +415,15 @@ hipError_t launch_stream(const GemmArgs* segs, int nseg, int epi, bool bf16, hip
   const dim3 block(nwaves * 64);
   const bool one = mmax <= 16;
   if (bf16) {
-    if (ns == 8) return one ? dispatch_bl<uint16_t, 1, 8>(sa, epi, grid, block, st)
-                            : dispatch_bl<uint16_t, 2, 8>(sa, epi, grid, block, st);
-    return one ? dispatch_bl<uint16_t, 1, 4>(sa, epi, grid, block, st)
-               : dispatch_bl<uint16_t, 2, 4>(sa, epi, grid, block, st);
+    if (ns == 8) return one ? dispatch_bl<uint16_t, 1, 8>(sa, epi, g1, block, st)
+                            : dispatch_bl<uint16_t, 2, 8>(sa, epi, g1, block, st);
+    return one ? dispatch_bl<uint16_t, 1, 4>(sa, epi, g1, block, st)
+               : dispatch_bl<uint16_t, 2, 4>(sa, epi, g1, block, st);
   }
-  if (ns == 8) return one ? dispatch_bl<float, 1, 8>(sa, epi, grid, block, st)
-                          : dispatch_bl<float, 2, 8>(sa, epi, grid, block, st);
-  return one ? dispatch_bl<float, 1, 4>(sa, epi, grid, block, st)
-             : dispatch_bl<float, 2, 4>(sa, epi, grid, block, st);
+  if (ns == 8) return one ? dispatch_bl<float, 1, 8>(sa, epi, g1, block, st)
+                          : dispatch_bl<float, 2, 8>(sa, epi, g1, block, st);
+  return one ? dispatch_bl<float, 1, 4>(sa, epi, g1, block, st)
+             : dispatch_bl<float, 2, 4>(sa, epi, g1, block, st);
 }
 
 }  // namespace

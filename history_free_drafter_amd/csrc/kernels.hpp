@@ -11,6 +11,8 @@ namespace dlite {
 
 // Workspace counters, zeroed by the first kernel of every draft step.
 // Words 0..15 are fixed counters; the scan's team barriers follow.
+// CNT_LM_DONE + c: finished workgroups of the c-th 32-token launch of the
+// streaming vocabulary kernels (fewer than 64 tokens, so c is 0 or 1).
 enum Counter { CNT_LM_DONE = 0, CNT_STATUS = 2, CNT_TEAM0 = 16 };
 int scan_counters();                        // team-barrier words after CNT_TEAM0
 size_t scan_scratch_floats(int B, int r);   // size of ScanArgs::U

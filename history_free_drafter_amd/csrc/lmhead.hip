@@ -5,9 +5,10 @@
 // Pass 1: workgroup g streams vocabulary rows [g V / G, (g+1) V / G) through
 // 16x16 MFMA tiles against the token block held in registers and keeps a
 // running (max, index) per token; the full logits are never written (unless
-// the logits tap is requested).  Pass 2, a second small kernel, reduces the G
-// partials of every token in a fixed order, so the result does not depend on
-// scheduling.
+// the logits tap is requested).  Pass 2 reduces the G partials of every token
+// in a fixed order, so the result does not depend on scheduling: done by the
+// last workgroup to finish pass 1, or by a second small kernel after the
+// tiled path.
 #include "kernels.hpp"
 
 namespace dlite {
@@ -17,21 +18,10 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kMaxSteps = 16;   // r <= 512 (bf16) / 256 (fp32)
 
-// Pass 2: one wave per token reduces the G partials in fixed order.  A
-// separate launch: the kernel boundary orders it after every partial.
-__global__ __launch_bounds__(256) void lmhead_reduce_kernel(LmArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tok >= a.M) return;
-  const long G = a.G;
-  const long base = static_cast<long>(a.tok0 + tok) * G;
-  float v = -INFINITY;
-  int i = 0x7fffffff;
-  for (long j = lane; j < G; j += 64) {
-    const float pv = a.part_max[base + j];
-    const int pi = a.part_idx[base + j];
-    if (better(pv, pi, v, i)) { v = pv; i = pi; }
-  }
+// Pass 2 for one token (one wave), after each lane has folded its strided
+// share of the G partials: a butterfly, then the candidate (ties resolve to
+// the lowest index throughout).
+__device__ __forceinline__ void finish_token(const LmArgs& a, int tok, int lane, float v, int i) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const float ov = __shfl_xor(v, o, kWave);
@@ -47,12 +37,68 @@ __global__ __launch_bounds__(256) void lmhead_reduce_kernel(LmArgs a) {
   }
 }
 
+// Pass 2 as its own launch (after the tiled path): the kernel boundary orders
+// it after every partial.
+__global__ __launch_bounds__(256) void lmhead_reduce_kernel(LmArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= a.M) return;
+  const long G = a.G;
+  const long base = static_cast<long>(a.tok0 + tok) * G;
+  float v = -INFINITY;
+  int i = 0x7fffffff;
+  for (long j = lane; j < G; j += 64) {
+    const float pv = a.part_max[base + j];
+    const int pi = a.part_idx[base + j];
+    if (better(pv, pi, v, i)) { v = pv; i = pi; }
+  }
+  finish_token(a, tok, lane, v, i);
+}
+
+// Pass 2 inside the streaming kernels: every workgroup stores its partials
+// with device-coherent (agent-scope atomic) stores, waits for them to
+// complete and counts itself in; the workgroup that arrives last reads all
+// partials back with device-coherent loads and reduces them, one wave per
+// token.  Only the partials and the counter cross workgroups, so no cache
+// write-back or invalidate is needed.  Nothing waits on another workgroup,
+// so nothing depends on which workgroups are resident; the counter is
+// cleared by the step's first kernel.
+__device__ __forceinline__ void publish_partial(const LmArgs& a, long o, float v, int i) {
+  __hip_atomic_store(a.part_max + o, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(a.part_idx + o, i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void reduce_if_last(const LmArgs& a, long G, int* last) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* cnt = a.counters + CNT_LM_DONE + a.tok0 / 32;
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last = prev + 1 == static_cast<unsigned>(G);
+  }
+  __syncthreads();
+  if (!*last) return;
+  const int lane = threadIdx.x & 63;
+  for (int tok = threadIdx.x >> 6; tok < a.M; tok += static_cast<int>(blockDim.x >> 6)) {
+    const long base = static_cast<long>(a.tok0 + tok) * G;
+    float v = -INFINITY;
+    int i = 0x7fffffff;
+    for (long j = lane; j < G; j += 64) {
+      const float pv = __hip_atomic_load(a.part_max + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int pi = __hip_atomic_load(a.part_idx + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (better(pv, pi, v, i)) { v = pv; i = pi; }
+    }
+    finish_token(a, tok, lane, v, i);
+  }
+}
+
 template <typename T, int MT>
 __global__ __launch_bounds__(kWaves * 64) void lmhead_kernel(LmArgs a) {
   constexpr int PER = Elem<T>::kPerLane;
   constexpr int KS = PER * 4;
   __shared__ float sv[kWaves][32];
   __shared__ int si[kWaves][32];
+  __shared__ int last;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, grp = lane >> 4;
@@ -131,11 +177,9 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_kernel(LmArgs a) {
     int i = si[0][threadIdx.x];
     for (int w = 1; w < kWaves; ++w)
       if (better(sv[w][threadIdx.x], si[w][threadIdx.x], v, i)) { v = sv[w][threadIdx.x]; i = si[w][threadIdx.x]; }
-    const long o = static_cast<long>(a.tok0 + threadIdx.x) * G + g;
-    a.part_max[o] = v;
-    a.part_idx[o] = i;
+    publish_partial(a, static_cast<long>(a.tok0 + threadIdx.x) * G + g, v, i);
   }
-
+  reduce_if_last(a, G, &last);
 }
 
 // Pipelined variant for at most 16 tokens: each wave streams its tiles
@@ -150,6 +194,7 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_pipe_kernel(LmArgs a) {
   static_assert(kMaxSteps == 16, "one raw load per tile row");
   __shared__ float sv[kWaves][16];
   __shared__ int si[kWaves][16];
+  __shared__ int last;
   __shared__ uint4 wbuf[kWaves][16 * 64];   // per wave: 16 rows x 64 chunks
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -238,10 +283,9 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_pipe_kernel(LmArgs a) {
     int i = si[0][threadIdx.x];
     for (int w = 1; w < kWaves; ++w)
       if (better(sv[w][threadIdx.x], si[w][threadIdx.x], v, i)) { v = sv[w][threadIdx.x]; i = si[w][threadIdx.x]; }
-    const long o = static_cast<long>(a.tok0 + threadIdx.x) * G + g;
-    a.part_max[o] = v;
-    a.part_idx[o] = i;
+    publish_partial(a, static_cast<long>(a.tok0 + threadIdx.x) * G + g, v, i);
   }
+  reduce_if_last(a, G, &last);
 }
 
 }  // namespace
@@ -278,10 +322,7 @@ hipError_t launch_lmhead(const LmArgs& a0, bool bf16, hipStream_t st) {
       if (a.M <= 16) hipLaunchKernelGGL((lmhead_pipe_kernel<float>), grid, block, 0, st, a);
       else hipLaunchKernelGGL((lmhead_kernel<float, 2>), grid, block, 0, st, a);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3((a.M + 3) / 4), dim3(256), 0, st, a);
-    e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
