@@ -47,7 +47,7 @@ size_t esize(const dlite_dims& d) { return d.dtype == DLITE_BF16 ? 2 : 4; }
 
 // Workspace regions, each 256-byte aligned.
 struct Plan {
-  size_t counters, X, XB, XF, SSQ, Q, KV, AO, ACT, P, U, Sf, Sb, pmax, pidx, TP, total;
+  size_t counters, X, XB, XF, SSQ, Q, KV, AO, ACT, P, U, Sf, Sb, pmax, pidx, TP, SP, total;
   int G;
 };
 
@@ -79,6 +79,33 @@ size_t tile_scratch_bytes(const dlite_dims& d) {
   return need;
 }
 
+// k-slice partials of the weight-streaming GEMMs: the largest need of any
+// launch of the step (launches of at most 32 tokens, the same decisions the
+// launchers take).
+size_t stream_scratch_bytes(const dlite_dims& d) {
+  const bool bf16 = d.dtype == DLITE_BF16;
+  const int B = d.B, S = d.m + 1 + d.K, L = 1 + d.K, K = d.K, D = d.D, F = d.ffn, r = d.rank;
+  const int Hq = d.n_q * d.d_h, Hkv2 = 2 * d.n_kv * d.d_h;
+  auto tiled = [&](int M, int Kd) { GemmArgs g{}; g.M = M; g.K = Kd; return gemm_tiled(g, bf16); };
+  auto c32 = [](int M) { return M < 32 ? M : 32; };
+  size_t need = 0;
+  auto keep = [&](size_t v) { need = v > need ? v : need; };
+  for (int Lr : {L, K}) {
+    const int Mq = B * Lr, Mkv = B * S;
+    if (!tiled(Mq, D) && !tiled(Mkv, D) && Mq <= 32 && Mkv <= 32) {
+      keep(gemm_stream_scratch(Mq, Mkv, Hq, Hkv2, D, EPI_STORE_F32, bf16));
+    } else {
+      if (!tiled(Mq, D)) keep(gemm_stream_scratch(c32(Mq), 0, Hq, 0, D, EPI_STORE_F32, bf16));
+      if (!tiled(Mkv, D)) keep(gemm_stream_scratch(c32(Mkv), 0, Hkv2, 0, D, EPI_STORE_F32, bf16));
+    }
+    if (!tiled(Mq, Hq)) keep(gemm_stream_scratch(c32(Mq), 0, D, 0, Hq, EPI_RESID, bf16));
+    if (!tiled(Mq, D)) keep(gemm_stream_scratch(c32(Mq), 0, F, 0, D, EPI_SWIGLU, bf16));
+    if (!tiled(Mq, F)) keep(gemm_stream_scratch(c32(Mq), 0, D, 0, F, EPI_RESID, bf16));
+  }
+  if (!tiled(B * K, D)) keep(gemm_stream_scratch(c32(B * K), 0, r, 0, D, EPI_STORE_F32, bf16));
+  return need;
+}
+
 Plan make_plan(const dlite_dims& d) {
   const size_t B = d.B, S = d.m + 1 + d.K, L = 1 + d.K, D = d.D;
   const size_t Hq = static_cast<size_t>(d.n_q) * d.d_h, Hkv = static_cast<size_t>(d.n_kv) * d.d_h;
@@ -105,6 +132,7 @@ Plan make_plan(const dlite_dims& d) {
   p.pmax = take(B * K * Gmax * 4);
   p.pidx = take(B * K * Gmax * 4);
   p.TP = take(tile_scratch_bytes(d));
+  p.SP = take(stream_scratch_bytes(d));
   p.total = off;
   return p;
 }
@@ -254,7 +282,9 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   void* Sb = ws + p.Sb;
   float* pmax = reinterpret_cast<float*>(ws + p.pmax);
   int* pidx = reinterpret_cast<int*>(ws + p.pidx);
-  float* TPs = p.TP != p.total ? reinterpret_cast<float*>(ws + p.TP) : nullptr;
+  float* TPs = p.TP != p.SP ? reinterpret_cast<float*>(ws + p.TP) : nullptr;
+  const StreamScratch gs{TPs, reinterpret_cast<float*>(ws + p.SP), (p.total - p.SP) / sizeof(float),
+                         counters + counter_gemm()};
   const dlite_taps no_taps{};
   const dlite_taps& tp = taps ? *taps : no_taps;
   const size_t xb_layer = static_cast<size_t>(B) * S * D * es;
@@ -296,7 +326,7 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
     kv.W = at(lw.wqkv, static_cast<size_t>(Hq) * D * es); kv.N = 2 * Hkv;
     kv.smap = all_slots; kv.qmap = all_slots; kv.M = B * S;
     kv.out = KVb; kv.ld_out = 2 * Hkv; kv.omap = all_slots;
-    DLITE_LAUNCH(launch_gemm_pair(q, kv, EPI_STORE_F32, bf16, TPs, st));
+    DLITE_LAUNCH(launch_gemm_pair(q, kv, EPI_STORE_F32, bf16, gs, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_QKV, false, st, l));
 
     AttnArgs aa{Qb, KVb, AO, B, m, K, d.n_q, d.n_kv, d.d_h, q0, d.rope_theta};
@@ -310,7 +340,7 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
     o.out = X; o.ld_out = D; o.omap = slot_rows;
     o.next_gain = lw.ffn_norm; o.xb_out = XF; o.ld_xb = D; o.xmap = local_rows; o.ssq_out = SSQ;
     DLITE_LAUNCH(mark(DLITE_STAGE_OPROJ, true, st, l));
-    DLITE_LAUNCH(launch_gemm(o, EPI_RESID, bf16, TPs, st));
+    DLITE_LAUNCH(launch_gemm(o, EPI_RESID, bf16, gs, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_OPROJ, false, st, l));
 
     GemmArgs gu{};
@@ -320,7 +350,7 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
     gu.np_hi = gu.np_lo; gu.norm_len = D; gu.eps = d.rms_eps;
     gu.out = ACT; gu.ld_out = F; gu.omap = local_rows;
     DLITE_LAUNCH(mark(DLITE_STAGE_GATE_UP, true, st, l));
-    DLITE_LAUNCH(launch_gemm(gu, EPI_SWIGLU, bf16, TPs, st));
+    DLITE_LAUNCH(launch_gemm(gu, EPI_SWIGLU, bf16, gs, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_GATE_UP, false, st, l));
 
     GemmArgs dn{};
@@ -334,7 +364,7 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
       dn.ld_tap = D; dn.tmap = local_rows;
     }
     DLITE_LAUNCH(mark(DLITE_STAGE_DOWN, true, st, l));
-    DLITE_LAUNCH(launch_gemm(dn, EPI_RESID, bf16, TPs, st));
+    DLITE_LAUNCH(launch_gemm(dn, EPI_RESID, bf16, gs, st));
     local_parts = gemm_resid_parts(dn, bf16);
     DLITE_LAUNCH(mark(DLITE_STAGE_DOWN, false, st, l));
   }
@@ -357,7 +387,7 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   ph.np_hi = local_parts; ph.norm_len = D; ph.eps = d.rms_eps;
   ph.out = P; ph.ld_out = r; ph.omap = RowMap{K, K, 0};
   DLITE_LAUNCH(mark(DLITE_STAGE_SEQ_PROJ, true, st));
-  DLITE_LAUNCH(launch_gemm(ph, EPI_STORE_F32, bf16, TPs, st));
+  DLITE_LAUNCH(launch_gemm(ph, EPI_STORE_F32, bf16, gs, st));
   DLITE_LAUNCH(mark(DLITE_STAGE_SEQ_PROJ, false, st));
 
   // 5. the K-step recurrence

@@ -10,13 +10,15 @@
 namespace dlite {
 
 // Workspace counters, zeroed by the first kernel of every draft step.
-// Words 0..15 are fixed counters; the scan's team barriers follow.
+// Words 0..15 are fixed counters; the scan's team barriers follow, then the
+// arrival counters of the weight-streaming GEMMs.
 // CNT_LM_DONE + c: finished workgroups of the c-th 32-token launch of the
 // streaming vocabulary kernels (fewer than 64 tokens, so c is 0 or 1).
 enum Counter { CNT_LM_DONE = 0, CNT_STATUS = 2, CNT_TEAM0 = 16 };
 int scan_counters();                        // team-barrier words after CNT_TEAM0
 size_t scan_scratch_floats(int B, int r);   // size of ScanArgs::U
-inline int counter_words() { return CNT_TEAM0 + scan_counters(); }
+inline int counter_gemm() { return CNT_TEAM0 + scan_counters(); }
+inline int counter_words() { return counter_gemm() + 2 * 128; }
 enum Status { STATUS_BARRIER_TIMEOUT = 1 };
 
 // Partial sums of squares per activation row: one slot per producing
@@ -67,19 +69,24 @@ struct GemmArgs {
   // partial at part_*[(tok0 + token) * G_part + tile]
   float* part_max; int* part_idx; int G_part;
 };
+// Scratch of the GEMM launches: partial tiles of the tiled path, k-slice
+// partials and arrival counters of the weight-streaming path.
+constexpr int kStreamRowBlocks = 128;   // arrival counters per problem
+struct StreamScratch {
+  float* tile_part;      // gemm_tile_scratch bytes (or null: no split K)
+  float* part;           // gemm_stream_scratch bytes
+  size_t part_floats;
+  unsigned* counters;    // 2 * kStreamRowBlocks words, zero between launches
+};
 // Enqueues the GEMM; M > 32 is split into launches of 32 tokens on the
 // weight-streaming path, or handled in one launch by the tiled path.
-hipError_t launch_gemm(const GemmArgs& a, int epi, bool bf16, float* part, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& a, int epi, bool bf16, const StreamScratch& ss, hipStream_t st);
 // Two problems with the same K and epilogue (e.g. query rows of the local
 // tokens and key/value rows of every slot), in one launch where the paths allow.
-hipError_t launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, int epi, bool bf16, float* part,
-                            hipStream_t st);
-// Weight-streaming kernel arguments: workgroups [0, g0) serve seg[0], the
-// rest seg[1].
-struct StreamArgs {
-  GemmArgs seg[2];
-  int g0;
-};
+hipError_t launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, int epi, bool bf16,
+                            const StreamScratch& ss, hipStream_t st);
+// Bytes of k-slice partials one weight-streaming launch needs (M0, M1 <= 32).
+size_t gemm_stream_scratch(int M0, int M1, int N0, int N1, int K, int epi, bool bf16);
 // Number of partial sums of squares per row that an EPI_RESID launch writes.
 int gemm_resid_parts(const GemmArgs& a, bool bf16);
 
