@@ -113,7 +113,8 @@ Plan make_plan(const dlite_dims& d) {
   Plan p{};
   p.G = lmhead_groups(d.vocab);
   const int Gt = gemm_tile_groups(d.vocab);
-  const size_t Gmax = p.G > Gt ? p.G : Gt;
+  size_t Gmax = p.G > Gt ? p.G : Gt;
+  if (seqhead_fused(d.B, d.K, d.rank, d.dtype == DLITE_BF16) && Gmax < kFuseMaxHelpers) Gmax = kFuseMaxHelpers;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
   p.counters = take(counter_words() * sizeof(unsigned));
@@ -390,21 +391,28 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   DLITE_LAUNCH(launch_gemm(ph, EPI_STORE_F32, bf16, gs, st));
   DLITE_LAUNCH(mark(DLITE_STAGE_SEQ_PROJ, false, st));
 
-  // 5. the K-step recurrence
+  // 5. the K-step recurrence, 6. vocabulary projection + argmax (one fused
+  //    launch for a few requests)
   ScanArgs sa{P, w->seq_w_down, w->seq_w_up, U, Sf, Sb, tp.state, counters, B, K, D, r, 0u, 0};
-  DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
-  DLITE_LAUNCH(launch_scan(sa, bf16, st));
-  DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st));
-
-  // 6. vocabulary projection + argmax
   LmArgs la{};
   la.W = w->lm_head; la.src = Sb; la.V = d.vocab; la.r = r; la.M = B * K; la.tok0 = 0;
   la.part_max = pmax; la.part_idx = pidx; la.G = p.G;
   la.cand = candidates; la.max_logit = max_logit; la.tap = tp.logits;
   la.anchors = anchor_ids; la.K = K; la.counters = counters; la.part = TPs;
-  DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, true, st));
-  DLITE_LAUNCH(launch_lmhead(la, bf16, st));
-  DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, false, st));
+  if (seqhead_fused(B, K, r, bf16)) {
+    DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
+    DLITE_LAUNCH(launch_seqhead(sa, la, st));
+    DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st));
+    DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, true, st));
+    DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, false, st));
+  } else {
+    DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
+    DLITE_LAUNCH(launch_scan(sa, bf16, st));
+    DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st));
+    DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, true, st));
+    DLITE_LAUNCH(launch_lmhead(la, bf16, st));
+    DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, false, st));
+  }
   return ok();
 }
 

@@ -14,10 +14,14 @@ namespace dlite {
 // arrival counters of the weight-streaming GEMMs.
 // CNT_LM_DONE + c: finished workgroups of the c-th 32-token launch of the
 // streaming vocabulary kernels (fewer than 64 tokens, so c is 0 or 1).
+// counter_seq_done(): scan team members that have published their states
+// (fused scan + vocabulary kernel); it sits on a 256-byte line of its own so
+// that the helpers polling it do not slow the team's own barrier words.
 enum Counter { CNT_LM_DONE = 0, CNT_STATUS = 2, CNT_TEAM0 = 16 };
 int scan_counters();                        // team-barrier words after CNT_TEAM0
 size_t scan_scratch_floats(int B, int r);   // size of ScanArgs::U
-inline int counter_gemm() { return CNT_TEAM0 + scan_counters(); }
+inline int counter_seq_done() { return ((CNT_TEAM0 + scan_counters() + 63) / 64) * 64; }
+inline int counter_gemm() { return counter_seq_done() + 64; }
 inline int counter_words() { return counter_gemm() + 2 * 128; }
 enum Status { STATUS_BARRIER_TIMEOUT = 1 };
 
@@ -168,6 +172,12 @@ struct LmArgs {
 };
 hipError_t launch_lmhead(const LmArgs& a, bool bf16, hipStream_t st);
 int lmhead_groups(int V);
+// Fused scan + vocabulary pass for a few requests (B * K <= 16, bf16,
+// r in {320, 512}): one launch replaces launch_scan + launch_lmhead.  Needs
+// kFuseMaxHelpers partials per token in LmArgs::part_max / part_idx.
+constexpr int kFuseMaxHelpers = 1024;
+bool seqhead_fused(int B, int K, int r, bool bf16);
+hipError_t launch_seqhead(const ScanArgs& s, const LmArgs& l, hipStream_t st);
 
 // --------------------------------------------------------------- accept ----
 hipError_t launch_accept(const int32_t* cand, const int32_t* tgt, int B, int K,

@@ -9,7 +9,7 @@
 // in a fixed order, so the result does not depend on scheduling: done by the
 // last workgroup to finish pass 1, or by a second small kernel after the
 // tiled path.
-#include "kernels.hpp"
+#include "scan_team.hpp"
 
 namespace dlite {
 
@@ -83,10 +83,20 @@ __device__ __forceinline__ void reduce_if_last(const LmArgs& a, long G, int* las
     const long base = static_cast<long>(a.tok0 + tok) * G;
     float v = -INFINITY;
     int i = 0x7fffffff;
-    for (long j = lane; j < G; j += 64) {
-      const float pv = __hip_atomic_load(a.part_max + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int pi = __hip_atomic_load(a.part_idx + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (better(pv, pi, v, i)) { v = pv; i = pi; }
+    // kBatch partials per lane requested at once, then folded in index order
+    constexpr int kBatch = 8;
+    for (long j0 = lane; j0 < G; j0 += 64 * kBatch) {
+      float pv[kBatch];
+      int pi[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const long j = j0 + 64 * q < G ? j0 + 64 * q : j0;
+        pv[q] = __hip_atomic_load(a.part_max + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pi[q] = __hip_atomic_load(a.part_idx + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        if (better(pv[q], pi[q], v, i)) { v = pv[q]; i = pi[q]; }
     }
     finish_token(a, tok, lane, v, i);
   }
@@ -288,11 +298,250 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_pipe_kernel(LmArgs a) {
   reduce_if_last(a, G, &last);
 }
 
+
+// ------------------------------------------ fused scan + vocabulary pass --
+//
+// For a few requests the sequential scan keeps one team of 8 workgroups busy
+// for K dependent steps while the rest of the chip idles, and the vocabulary
+// projection after it is a pure stream of V x r weights.  The fused kernel
+// overlaps the two: team workgroups run the scan (scan_team), every other
+// workgroup ("helper") owns a contiguous range of 16-row vocabulary tiles and,
+// while the scan runs, pulls its tiles on chip: TR tiles per wave into
+// registers as ready MFMA fragments, TL tiles per workgroup into LDS
+// (global_load_lds, fragment order).  When the team has published the states
+// (release on a device-scope counter), helpers acquire, stage the states in
+// LDS, multiply the resident tiles, stream the few tiles that did not fit,
+// and reduce (max, index) exactly as the streaming pass does.  Helpers wait
+// on the team but the team never waits on helpers, and the team's workgroups
+// come first in dispatch order, so the wait always ends; it is also bounded.
+constexpr int kFuseRegs = 192;            // VGPRs per lane for resident fragments
+constexpr int kFuseLdsTiles = 144 * 1024; // LDS bytes for resident tiles
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at l + 16 i (l is the same for the whole wave).
+__device__ __forceinline__ void load_lds16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
+}
+
+struct FuseArgs {
+  ScanArgs sa;
+  LmArgs la;
+  int nteam;        // scan teams (one request each): blocks xq * 8 + t, t < nteam, xq < 8
+  unsigned* done;   // published-state counter of the team members
+};
+
+template <int RK>   // k-steps of 32 (r / 32)
+__global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
+  using namespace scan_detail;
+  constexpr int TR = kFuseRegs / (4 * RK);         // register tiles per wave
+  constexpr int TL = kFuseLdsTiles / (RK * 1024);  // LDS tiles per workgroup
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float sv[kWaves][16];
+  __shared__ int si[kWaves][16];
+  __shared__ int last;
+
+  const int bx = blockIdx.x, xq = bx >> 3, x = bx & 7;
+  const int nteam = f.nteam;
+  unsigned* done = f.done;
+  if (xq < kTeam && x < nteam) {
+    scan_team<uint16_t>(f.sa, reinterpret_cast<float*>(smem), x, xq, done);
+    return;
+  }
+
+  const LmArgs& a = f.la;
+  const int h = bx < 8 * kTeam ? xq * (8 - nteam) + (x - nteam) : bx - kTeam * nteam;
+  const int G = static_cast<int>(gridDim.x) - kTeam * nteam;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, grp = lane >> 4;
+  const int r = a.r, V = a.V, M = a.M;
+  const int NT = (V + 15) / 16;
+  const int t0 = static_cast<int>(static_cast<long>(h) * NT / G);
+  const int t1 = static_cast<int>(static_cast<long>(h + 1) * NT / G);
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  // fragment (tile t, k-step s) of this lane: row t*16 + c16, 16 bytes at s*32 + grp*8
+  auto frag_ptr = [&](int t, int s) {
+    int row = t * 16 + c16;
+    row = row < V ? row : V - 1;
+    return W + static_cast<long>(row) * r + s * 32 + grp * 8;
+  };
+
+  uint4* lds_w = reinterpret_cast<uint4*>(smem);                                   // [TL][RK][64]
+  uint16_t* lds_s = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(TL) * RK * 1024);  // [M][r]
+
+  // ---- while the scan runs: resident tiles
+  const int treg = t0 + wave * TR;             // this wave's register tiles
+  uint4 wr[TR][RK];
+#pragma unroll
+  for (int i = 0; i < TR; ++i)
+#pragma unroll
+    for (int s = 0; s < RK; ++s) wr[i][s] = ld_stream(frag_ptr(treg + i, s));
+  const int tlds = t0 + kWaves * TR;           // first LDS tile
+  for (int j = wave; j < TL; j += kWaves)
+#pragma unroll
+    for (int s = 0; s < RK; ++s)
+      load_lds16(frag_ptr(tlds + j, s), lds_w + (j * RK + s) * 64);
+
+  // ---- the tiles that do not fit: touched once now (one dword per 128-byte
+  //      line, temporal loads) so that they sit in L2 when they are streamed
+  //      after the scan
+  const int tstream = tlds + TL;
+  unsigned touch = 0;
+  for (int t = tstream + wave; t < t1; t += kWaves) {
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(W + static_cast<long>(t) * 16 * r);
+    const int lines = (t * 16 + 16 <= V ? 16 : V - t * 16) * r / 64;   // 128-byte lines of the tile
+    for (int l = lane; l < lines; l += 64) touch ^= base[l * 32];
+  }
+
+  // ---- wait for the team's states (relaxed: the states themselves are
+  //      stored and loaded with device scope)
+  if (threadIdx.x == 0) {
+    const unsigned target = static_cast<unsigned>(kTeam * nteam);
+    unsigned spins = 0;
+    while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(8);
+      if (++spins > kSpinLimit) {
+        atomicOr(a.counters + CNT_STATUS, static_cast<unsigned>(STATUS_BARRIER_TIMEOUT));
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int n16 = M * r / 8;                 // [M][r] bf16 states, 16 bytes at a time
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(a.src), 0, n16 * 16, kRsrcWord3);
+    for (int e = threadIdx.x; e < n16; e += blockDim.x)
+      reinterpret_cast<u32x4*>(lds_s)[e] = __builtin_amdgcn_raw_buffer_load_b128(rs, e * 16, 0, kPolicySc1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): register and LDS tiles have landed too
+  __syncthreads();
+
+  const bool tok_ok = c16 < M;
+  auto bfrag = [&](int s) {
+    const uint4 v = *reinterpret_cast<const uint4*>(lds_s + (tok_ok ? c16 : 0) * r + s * 32 + grp * 8);
+    return tok_ok ? v : make_uint4(0, 0, 0, 0);
+  };
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  auto take = [&](int t, const floatx4& acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int vr = t * 16 + grp * 4 + i;
+      if (t < t1 && vr < V && tok_ok) {
+        const float v = acc[i];
+        if (better(v, vr, bv, bi)) { bv = v; bi = vr; }
+        if (a.tap) a.tap[static_cast<long>(c16) * V + vr] = v;
+      }
+    }
+  };
+
+  // register tiles
+  {
+    floatx4 acc[TR];
+#pragma unroll
+    for (int i = 0; i < TR; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < RK; ++s) {
+      const uint4 b = bfrag(s);
+#pragma unroll
+      for (int i = 0; i < TR; ++i) acc[i] = mma_step(wr[i][s], b, acc[i], uint16_t());
+    }
+#pragma unroll
+    for (int i = 0; i < TR; ++i) take(treg + i, acc[i]);
+  }
+  // tiles that did not fit: streamed now (from L2), one wave per tile, loads
+  // issued before the LDS tiles are multiplied
+  int t = tstream + wave;
+  uint4 nx[RK];
+  if (t < t1) {
+#pragma unroll
+    for (int s = 0; s < RK; ++s) nx[s] = ld_stream(frag_ptr(t, s));
+  }
+  for (int j = wave; j < TL; j += kWaves) {
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < RK; ++s) acc = mma_step(lds_w[(j * RK + s) * 64 + lane], bfrag(s), acc, uint16_t());
+    take(tlds + j, acc);
+  }
+  for (; t < t1; t += kWaves) {
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < RK; ++s) acc = mma_step(nx[s], bfrag(s), acc, uint16_t());
+    take(t, acc);
+    if (t + kWaves < t1) {
+#pragma unroll
+      for (int s = 0; s < RK; ++s) nx[s] = ld_stream(frag_ptr(t + kWaves, s));
+    }
+  }
+
+  // combine the four row groups of each token column, then the waves
+#pragma unroll
+  for (int o = 16; o < 64; o <<= 1) {
+    const float ov = __shfl_xor(bv, o, kWave);
+    const int oi = __shfl_xor(bi, o, kWave);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if (grp == 0) { sv[wave][c16] = bv; si[wave][c16] = bi; }
+  __syncthreads();
+  if (static_cast<int>(threadIdx.x) < M) {
+    float v = sv[0][threadIdx.x];
+    int i = si[0][threadIdx.x];
+    for (int w = 1; w < kWaves; ++w)
+      if (better(sv[w][threadIdx.x], si[w][threadIdx.x], v, i)) { v = sv[w][threadIdx.x]; i = si[w][threadIdx.x]; }
+    publish_partial(a, static_cast<long>(threadIdx.x) * G + h, v, i);
+  }
+  reduce_if_last(a, G, &last);
+  if (touch == 0x9e3779b9u && M < 0) a.cand[0] = 0;   // keeps the touch loads
+}
+
+template <int RK>
+size_t seqhead_lds(int M, int r) {
+  constexpr int TL = kFuseLdsTiles / (RK * 1024);
+  return static_cast<size_t>(TL) * RK * 1024 + static_cast<size_t>(M) * r * 2;
+}
+
 }  // namespace
 
 int lmhead_groups(int V) {
   const int tiles = (V + 15) / 16;
   return tiles < 256 ? tiles : 256;
+}
+
+bool seqhead_fused(int B, int K, int r, bool bf16) {
+  if (!bf16 || B * K > 16 || B > 8 || (r != 320 && r != 512)) return false;
+  const size_t lds = r == 512 ? seqhead_lds<16>(B * K, r) : seqhead_lds<10>(B * K, r);
+  return lds + 2048 <= 160 * 1024;   // + static LDS of the kernel
+}
+
+hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, hipStream_t st) {
+  using namespace scan_detail;
+  if (!seqhead_fused(s0.B, s0.K, s0.r, true) || l0.M != s0.B * s0.K || l0.tok0 != 0) return hipErrorInvalidValue;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  FuseArgs f{};
+  f.sa = s0;
+  f.sa.rpt = 1;
+  f.sa.cnt_base = 0;
+  f.nteam = s0.B;
+  f.done = s0.counters + counter_seq_done();
+  const int grid = cus > kTeam * 8 ? cus : kTeam * 8;
+  f.la = l0;
+  f.la.G = grid - kTeam * f.nteam;
+  if (f.la.G > kFuseMaxHelpers) return hipErrorInvalidValue;
+  const int RK = s0.r / 32;
+  const size_t sm_scan = scan_smem(s0.r, 1, s0.K);
+  const void* fn = RK == 16 ? reinterpret_cast<const void*>(&seqhead_kernel<16>)
+                            : reinterpret_cast<const void*>(&seqhead_kernel<10>);
+  size_t sm = RK == 16 ? seqhead_lds<16>(l0.M, s0.r) : seqhead_lds<10>(l0.M, s0.r);
+  sm = sm > sm_scan ? sm : sm_scan;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
+  if (e != hipSuccess) return e;
+  if (RK == 16) hipLaunchKernelGGL(seqhead_kernel<16>, dim3(grid), dim3(kWaves * 64), sm, st, f);
+  else hipLaunchKernelGGL(seqhead_kernel<10>, dim3(grid), dim3(kWaves * 64), sm, st, f);
+  return hipGetLastError();
 }
 
 hipError_t launch_lmhead(const LmArgs& a0, bool bf16, hipStream_t st) {
