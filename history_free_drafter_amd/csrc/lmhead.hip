@@ -316,6 +316,7 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_pipe_kernel(LmArgs a) {
 // come first in dispatch order, so the wait always ends; it is also bounded.
 constexpr int kFuseRegs = 192;            // VGPRs per lane for resident fragments
 constexpr int kFuseLdsTiles = 144 * 1024; // LDS bytes for resident tiles
+constexpr int kStatePad = 32;             // bf16 elements after each staged state row (spreads banks)
 
 // 16 bytes per lane from global memory straight into LDS: lane i's bytes land
 // at l + 16 i (l is the same for the whole wave).
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
   };
 
   uint4* lds_w = reinterpret_cast<uint4*>(smem);                                   // [TL][RK][64]
-  uint16_t* lds_s = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(TL) * RK * 1024);  // [M][r]
+  uint16_t* lds_s = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(TL) * RK * 1024);  // [M][r + pad]
 
   // ---- while the scan runs: resident tiles
   const int treg = t0 + wave * TR;             // this wave's register tiles
@@ -410,15 +411,17 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
     const int n16 = M * r / 8;                 // [M][r] bf16 states, 16 bytes at a time
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(a.src), 0, n16 * 16, kRsrcWord3);
+    const int per_row = r / 8;
     for (int e = threadIdx.x; e < n16; e += blockDim.x)
-      reinterpret_cast<u32x4*>(lds_s)[e] = __builtin_amdgcn_raw_buffer_load_b128(rs, e * 16, 0, kPolicySc1);
+      *reinterpret_cast<u32x4*>(lds_s + (e / per_row) * (r + kStatePad) + (e % per_row) * 8) =
+          __builtin_amdgcn_raw_buffer_load_b128(rs, e * 16, 0, kPolicySc1);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): register and LDS tiles have landed too
   __syncthreads();
 
   const bool tok_ok = c16 < M;
   auto bfrag = [&](int s) {
-    const uint4 v = *reinterpret_cast<const uint4*>(lds_s + (tok_ok ? c16 : 0) * r + s * 32 + grp * 8);
+    const uint4 v = *reinterpret_cast<const uint4*>(lds_s + (tok_ok ? c16 : 0) * (r + kStatePad) + s * 32 + grp * 8);
     return tok_ok ? v : make_uint4(0, 0, 0, 0);
   };
   float bv = -INFINITY;
@@ -435,38 +438,48 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
     }
   };
 
-  // register tiles
+  // register tiles (state fragments requested two steps ahead)
   {
     floatx4 acc[TR];
 #pragma unroll
     for (int i = 0; i < TR; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    uint4 bb[3];
+    bb[0] = bfrag(0);
+    if (RK > 1) bb[1] = bfrag(1);
 #pragma unroll
     for (int s = 0; s < RK; ++s) {
-      const uint4 b = bfrag(s);
+      if (s + 2 < RK) bb[(s + 2) % 3] = bfrag(s + 2);
 #pragma unroll
-      for (int i = 0; i < TR; ++i) acc[i] = mma_step(wr[i][s], b, acc[i], uint16_t());
+      for (int i = 0; i < TR; ++i) acc[i] = mma_step(wr[i][s], bb[s % 3], acc[i], uint16_t());
     }
 #pragma unroll
     for (int i = 0; i < TR; ++i) take(treg + i, acc[i]);
   }
-  // tiles that did not fit: streamed now (from L2), one wave per tile, loads
-  // issued before the LDS tiles are multiplied
+  // the register file is free again: the first tile that did not fit
+  // (touched into L2 above) is requested, then the LDS tiles are multiplied
+  // while it arrives; one wave per streamed tile
   int t = tstream + wave;
   uint4 nx[RK];
   if (t < t1) {
 #pragma unroll
     for (int s = 0; s < RK; ++s) nx[s] = ld_stream(frag_ptr(t, s));
   }
+  uint4 bq[RK];
+#pragma unroll
+  for (int s = 0; s < RK; ++s) bq[s] = bfrag(s);
   for (int j = wave; j < TL; j += kWaves) {
+    uint4 af[RK];
+#pragma unroll
+    for (int s = 0; s < RK; ++s) af[s] = lds_w[(j * RK + s) * 64 + lane];
     floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < RK; ++s) acc = mma_step(lds_w[(j * RK + s) * 64 + lane], bfrag(s), acc, uint16_t());
+    for (int s = 0; s < RK; ++s) acc = mma_step(af[s], bq[s], acc, uint16_t());
     take(tlds + j, acc);
   }
   for (; t < t1; t += kWaves) {
     floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < RK; ++s) acc = mma_step(nx[s], bfrag(s), acc, uint16_t());
+    for (int s = 0; s < RK; ++s) acc = mma_step(nx[s], bq[s], acc, uint16_t());
     take(t, acc);
     if (t + kWaves < t1) {
 #pragma unroll
@@ -497,7 +510,7 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
 template <int RK>
 size_t seqhead_lds(int M, int r) {
   constexpr int TL = kFuseLdsTiles / (RK * 1024);
-  return static_cast<size_t>(TL) * RK * 1024 + static_cast<size_t>(M) * r * 2;
+  return static_cast<size_t>(TL) * RK * 1024 + static_cast<size_t>(M) * (r + kStatePad) * 2;
 }
 
 }  // namespace
