@@ -18,21 +18,21 @@ namespace dlite {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kMaxD = 128;
 constexpr int kLd = kMaxD + 4;   // padded LDS row: 16-byte aligned, banks spread
 constexpr int kMaxS = 81;        // m <= 64, K <= 16
-constexpr int kLoads = 12;       // 16-byte global loads per thread and pass
+constexpr int kLoads = 4;        // 16-byte global loads per thread and pass
 
 __device__ __forceinline__ float rope_pos(int slot, int m) { return slot <= m ? 0.f : static_cast<float>(slot - m); }
 
-template <typename T>
+template <typename T, int DH>   // DH: head width (64 or 128), fixed so the dot products unroll
 __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   extern __shared__ __align__(16) float sm[];
   const int hpw = a.n_q / gridDim.x;          // query heads of this workgroup
   const int h0 = blockIdx.x * hpw, b = blockIdx.y;
   const int G = a.n_q / a.n_kv, kvh = h0 / G;
-  const int d = a.d_h, half = d / 2, hq = half / 4;   // float4 groups per half row
+  constexpr int d = DH, half = d / 2, hq = half / 4;   // float4 groups per half row
   const int S = a.m + 1 + a.K, L = 1 + a.K;
   const int Hq = a.n_q * d, Hkv = a.n_kv * d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -133,6 +133,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
       const bool ok = s < S;
       const float* kr = Ks + (ok ? s : 0) * kLd;
       float a0 = 0.f, a1 = 0.f;
+#pragma unroll
       for (int e = 0; e < d; e += 8) {
         const float4 k0 = *reinterpret_cast<const float4*>(kr + e);
         const float4 k1 = *reinterpret_cast<const float4*>(kr + e + 4);
@@ -160,16 +161,34 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     const int hh = t / lr, j = a.q0 + t % lr;
     const float* pr = Ps + (hh * L + j) * (S + 1);
     T* out = static_cast<T*>(a.out) + (static_cast<long>(b) * L + j) * Hq + (h0 + hh) * d;
-    for (int e = lane; e < d; e += 64) {
-      float acc0 = 0.f, acc1 = 0.f;
-      int s = 0;
-      for (; s + 1 < S; s += 2) {
-        acc0 += pr[s] * Vs[s * kLd + e];
-        acc1 += pr[s + 1] * Vs[(s + 1) * kLd + e];
+    // lane owns elements lane + 64 c; keys in groups of four, all reads of a
+    // group issued together
+    constexpr int NE = d / 64;
+    float acc[NE][2];
+#pragma unroll
+    for (int c = 0; c < NE; ++c) acc[c][0] = acc[c][1] = 0.f;
+    int s = 0;
+    for (; s + 3 < S; s += 4) {
+      float pv[4], vv[4][NE];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        pv[u] = pr[s + u];
+#pragma unroll
+        for (int c = 0; c < NE; ++c) vv[u][c] = Vs[(s + u) * kLd + lane + 64 * c];
       }
-      if (s < S) acc0 += pr[s] * Vs[s * kLd + e];
-      out[e] = Elem<T>::from_f32(acc0 + acc1);
+#pragma unroll
+      for (int c = 0; c < NE; ++c) {
+        acc[c][0] += pv[0] * vv[0][c] + pv[1] * vv[1][c];
+        acc[c][1] += pv[2] * vv[2][c] + pv[3] * vv[3][c];
+      }
     }
+    for (; s < S; ++s) {
+      const float p = pr[s];
+#pragma unroll
+      for (int c = 0; c < NE; ++c) acc[c][0] += p * Vs[s * kLd + lane + 64 * c];
+    }
+#pragma unroll
+    for (int c = 0; c < NE; ++c) out[lane + 64 * c] = Elem<T>::from_f32(acc[c][0] + acc[c][1]);
   }
 }
 
@@ -196,15 +215,22 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t st) {
   if (a.m + 1 + a.K > kMaxS || a.d_h > kMaxD) return hipErrorInvalidValue;
   const dim3 grid(a.n_q / pick_hpw(a), a.B), block(kThreads);
   const size_t sm = attention_smem(a);
-  const void* fn = bf16 ? reinterpret_cast<const void*>(&attention_kernel<uint16_t>)
-                        : reinterpret_cast<const void*>(&attention_kernel<float>);
+  if (a.d_h != 64 && a.d_h != 128) return hipErrorInvalidValue;
+  const void* fn;
+  if (bf16) fn = a.d_h == 128 ? reinterpret_cast<const void*>(&attention_kernel<uint16_t, 128>)
+                              : reinterpret_cast<const void*>(&attention_kernel<uint16_t, 64>);
+  else fn = a.d_h == 128 ? reinterpret_cast<const void*>(&attention_kernel<float, 128>)
+                         : reinterpret_cast<const void*>(&attention_kernel<float, 64>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(sm));
   if (e != hipSuccess) return e;
-  if (bf16)
-    hipLaunchKernelGGL(attention_kernel<uint16_t>, grid, block, sm, st, a);
-  else
-    hipLaunchKernelGGL(attention_kernel<float>, grid, block, sm, st, a);
+  if (bf16) {
+    if (a.d_h == 128) hipLaunchKernelGGL((attention_kernel<uint16_t, 128>), grid, block, sm, st, a);
+    else hipLaunchKernelGGL((attention_kernel<uint16_t, 64>), grid, block, sm, st, a);
+  } else {
+    if (a.d_h == 128) hipLaunchKernelGGL((attention_kernel<float, 128>), grid, block, sm, st, a);
+    else hipLaunchKernelGGL((attention_kernel<float, 64>), grid, block, sm, st, a);
+  }
   return hipGetLastError();
 }
 
