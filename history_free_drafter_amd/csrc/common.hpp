@@ -19,6 +19,12 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at l + 16 i (l is the same for the whole wave; inactive lanes write nothing).
+__device__ __forceinline__ void load_lds16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
+}
+
 // ------------------------------------------------------------ bf16 <-> f32 --
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

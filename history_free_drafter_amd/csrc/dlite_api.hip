@@ -301,6 +301,8 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   for (int l = 0; l < d.n_layers; ++l) fa.attn_norm[l] = w->layers[l].attn_norm;
   fa.anchors = anchor_ids; fa.X = X; fa.XB = XB; fa.ssq = SSQ; fa.tap_z = tp.z;
   fa.counters = counters; fa.n_counters = counter_words();
+  fa.clear = reinterpret_cast<uint4*>(U);
+  fa.n_clear = static_cast<long>(scan_scratch_floats(B, r) * sizeof(float) / 16);
   fa.B = B; fa.m = m; fa.K = K; fa.D = D; fa.V = d.vocab; fa.n_layers = d.n_layers;
   fa.eps = d.rms_eps;
   DLITE_LAUNCH(mark(DLITE_STAGE_FEATURES, true, st));

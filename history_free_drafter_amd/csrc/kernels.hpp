@@ -15,12 +15,10 @@ namespace dlite {
 // CNT_LM_DONE + c: finished workgroups of the c-th 32-token launch of the
 // streaming vocabulary kernels (fewer than 64 tokens, so c is 0 or 1).
 // counter_seq_done(): scan team members that have published their states
-// (fused scan + vocabulary kernel); it sits on a 256-byte line of its own so
-// that the helpers polling it do not slow the team's own barrier words.
-enum Counter { CNT_LM_DONE = 0, CNT_STATUS = 2, CNT_TEAM0 = 16 };
-int scan_counters();                        // team-barrier words after CNT_TEAM0
+// (fused scan + vocabulary kernel), on a 256-byte line of its own.
+enum Counter { CNT_LM_DONE = 0, CNT_STATUS = 2 };
 size_t scan_scratch_floats(int B, int r);   // size of ScanArgs::U
-inline int counter_seq_done() { return ((CNT_TEAM0 + scan_counters() + 63) / 64) * 64; }
+inline int counter_seq_done() { return 64; }
 inline int counter_gemm() { return counter_seq_done() + 64; }
 inline int counter_words() { return counter_gemm() + 2 * 128; }
 enum Status { STATUS_BARRIER_TIMEOUT = 1 };
@@ -45,6 +43,8 @@ struct FeatureArgs {
   float* tap_z;           // [B, m, D] or null
   unsigned* counters;     // counter_words() words, zeroed here
   int n_counters;
+  uint4* clear;           // scan exchange slots, zeroed here (n_clear 16-byte words)
+  long n_clear;
   int B, m, K, D, V, n_layers;
   float eps;
 };
@@ -94,6 +94,7 @@ size_t gemm_stream_scratch(int M0, int M1, int N0, int N1, int K, int epi, bool 
 // Number of partial sums of squares per row that an EPI_RESID launch writes.
 int gemm_resid_parts(const GemmArgs& a, bool bf16);
 
+
 // Tiled MFMA path for many token rows: up to two independent problems with
 // the same epilogue in one launch.
 // Launches with few output tiles split K over several workgroups: each writes
@@ -142,16 +143,16 @@ struct ScanArgs {
   const float* P;        // [B, K, r]  seq_w_down[:, :D] h_k
   const void* w_down;    // [r, D + r] (state columns used)
   const void* w_up;      // [r, r]
-  float* U;              // scan_scratch_floats(B, r) floats of scratch
+  float* U;              // scan_scratch_floats(B, r) floats of scratch, zeroed before the launch
   float* Sf;             // [B, K, r] states (fp32)
   void* Sb;              // [B, K, r] states (storage type) for the vocabulary GEMM
   float* tap;            // [B, K, r] or null
   unsigned* counters;
   int B, K, D, r;
-  unsigned cnt_base;     // barrier counts already accumulated by earlier launches
-  int rpt;               // requests per team (set by launch_scan)
+  unsigned tag0;         // steps run by earlier launches of this call (offsets the exchange tags)
+  int rpt;               // requests per team (set by the launcher)
+  int stage;             // byte offset of the weight staging area in dynamic LDS (0: none)
 };
-size_t scan_lds_bytes(int r, bool bf16, int K);
 hipError_t launch_scan(const ScanArgs& a, bool bf16, hipStream_t st);
 
 // ------------------------------------------- vocabulary GEMM + argmax ----

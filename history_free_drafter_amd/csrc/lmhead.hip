@@ -318,12 +318,6 @@ constexpr int kFuseRegs = 192;            // VGPRs per lane for resident fragmen
 constexpr int kFuseLdsTiles = 144 * 1024; // LDS bytes for resident tiles
 constexpr int kStatePad = 32;             // bf16 elements after each staged state row (spreads banks)
 
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
-// at l + 16 i (l is the same for the whole wave).
-__device__ __forceinline__ void load_lds16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
-}
-
 struct FuseArgs {
   ScanArgs sa;
   LmArgs la;
@@ -537,7 +531,7 @@ hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, hipStream_t st) 
   FuseArgs f{};
   f.sa = s0;
   f.sa.rpt = 1;
-  f.sa.cnt_base = 0;
+  f.sa.tag0 = 0;
   f.nteam = s0.B;
   f.done = s0.counters + counter_seq_done();
   const int grid = cus > kTeam * 8 ? cus : kTeam * 8;
@@ -545,7 +539,7 @@ hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, hipStream_t st) 
   f.la.G = grid - kTeam * f.nteam;
   if (f.la.G > kFuseMaxHelpers) return hipErrorInvalidValue;
   const int RK = s0.r / 32;
-  const size_t sm_scan = scan_smem(s0.r, 1, s0.K);
+  const size_t sm_scan = team_lds(s0.r, 1, s0.K, true, &f.sa.stage);
   const void* fn = RK == 16 ? reinterpret_cast<const void*>(&seqhead_kernel<16>)
                             : reinterpret_cast<const void*>(&seqhead_kernel<10>);
   size_t sm = RK == 16 ? seqhead_lds<16>(l0.M, s0.r) : seqhead_lds<10>(l0.M, s0.r);

@@ -54,6 +54,9 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
   float* x = a.X + row * a.D;
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < a.n_counters; i += blockDim.x) a.counters[i] = 0u;
+  for (long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; i < a.n_clear;
+       i += static_cast<long>(gridDim.x) * blockDim.x)
+    a.clear[i] = make_uint4(0u, 0u, 0u, 0u);
   const int nvec = a.D / PER;
 
   const T* src;

@@ -11,23 +11,20 @@ namespace {
 template <typename T>
 __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
   extern __shared__ __align__(16) float sm[];
-  const int xq = blockIdx.x >> 3;
-  const int j = xq % kTeam, team = (xq / kTeam) * 8 + (blockIdx.x & 7);
-  scan_team<T>(a, sm, team, j, nullptr);
+  scan_team<T>(a, sm, blockIdx.x / kTeam, blockIdx.x % kTeam, nullptr);
 }
 
 }  // namespace
 
 size_t scan_scratch_floats(int B, int r) {
   const int b = B < kTeamsPerLaunch * kReq ? B : kTeamsPerLaunch * kReq;
-  return 2 * static_cast<size_t>(b) * kTeam * r;
+  return 4 * static_cast<size_t>(b) * kTeam * r;   // [2][b][kTeam][r] tagged 64-bit words
 }
-int scan_counters() { return 2 * kTeamsPerLaunch; }   // arrival counters, placement words
-size_t scan_lds_bytes(int r, bool bf16, int K) { (void)bf16; return scan_smem(r, kReq, K); }
 
 hipError_t launch_scan(const ScanArgs& a0, bool bf16, hipStream_t st) {
   const int rpt = pick_rpt(a0.B);
-  const size_t sm = scan_smem(a0.r, rpt, a0.K);
+  int stage = 0;
+  const size_t sm = team_lds(a0.r, rpt, a0.K, bf16, &stage);
   const int per_launch = kTeamsPerLaunch * rpt;
   const void* fn = bf16 ? reinterpret_cast<const void*>(&scan_kernel<uint16_t>)
                         : reinterpret_cast<const void*>(&scan_kernel<float>);
@@ -38,16 +35,16 @@ hipError_t launch_scan(const ScanArgs& a0, bool bf16, hipStream_t st) {
   for (int b = 0; b < a0.B; b += per_launch, ++chunk) {
     ScanArgs a = a0;
     a.rpt = rpt;
+    a.stage = stage;
     a.B = (a0.B - b) < per_launch ? (a0.B - b) : per_launch;
     const long off = static_cast<long>(b) * a0.K * a0.r;
     a.P = a0.P + off;
     a.Sf = a0.Sf + off;
     a.Sb = static_cast<char*>(a0.Sb) + off * (bf16 ? 2 : 4);
     a.tap = a0.tap ? a0.tap + off : nullptr;
-    a.cnt_base = static_cast<unsigned>(chunk * a0.K * kTeam);
-    // team t on XCD t % 8: 8 kTeam workgroups per group of 8 teams
+    a.tag0 = static_cast<unsigned>(chunk * a0.K);
     const int nteam = (a.B + rpt - 1) / rpt;
-    const dim3 grid(((nteam + 7) / 8) * 8 * kTeam), block(kThreads);
+    const dim3 grid(nteam * kTeam), block(kThreads);
     if (bf16)
       hipLaunchKernelGGL(scan_kernel<uint16_t>, grid, block, sm, st, a);
     else

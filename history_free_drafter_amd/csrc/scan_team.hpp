@@ -13,28 +13,28 @@
 // of the gate input t = P_k + W_s s (wave w multiplies its 1/8 of the columns,
 // lane = row; the eight partial sums are added through LDS in wave order),
 // then its full-length contribution W_up[:, r0:r1] silu(t[r0:r1]) (thread =
-// output row); after one team barrier every workgroup adds all kTeam
-// contributions in the same fixed order, so each holds the identical new state
-// without a second exchange.  Requests are split into teams of up to kReq
-// requests; teams run independently.
+// output row).  Each contribution is stored as one 64-bit word, the value
+// beside a tag naming the step; every workgroup reads all kTeam contributions
+// back, re-reading until every tag is the current step's, and adds them in
+// the same fixed order, so each holds the identical new state without a
+// second exchange and without an arrival counter.  Contributions are
+// double-buffered by step parity: a slot is rewritten two steps later, after
+// its readers have contributed to the step in between.  Tags are unique
+// within a call (launch chunks offset them) and the slots are zeroed by the
+// first kernel of every call, so no value left by an earlier call matches.
+// Requests are split into teams of up to kReq requests; teams run
+// independently.
 //
 // Latency matters more than bandwidth here: the weight slices and every
-// step's P values are requested at once at the start (W_s last: the first
-// step multiplies a zero state and does not need it), the state is read from
-// LDS as broadcasts, and the partial contributions are read back with one
-// 16-byte load per team member.
-//
-// The members of a team run on one XCD (workgroup i runs on XCD i % 8, so
-// member j of team t gets workgroup ((t / 8) kTeam + j) 8 + t % 8) and
-// exchange their contributions through that XCD's L2: device-coherent
-// stores and loads that skip the per-CU L1, a wait for the stores, and a
-// relaxed arrival counter, with no L2 write-back or invalidate per step.
-// Every member checks its XCD id once; unless all members confirm the
-// placement, the team uses release/acquire barriers instead (L2 write-back
-// and invalidate around every exchange).
+// step's P values are requested at once at the start and settled before the
+// first step, the state is read from LDS as broadcasts (all 16 reads of a
+// 64-wide slice issued before the first multiply), and the exchange needs no
+// barrier: each 64-bit word is one device-scope atomic store and is read
+// with device-scope atomic loads, so value and tag arrive together wherever
+// the team members run, and no ordering between different words is needed.
 //
 // All workgroups of a launch are resident at once (at most 256 workgroups,
-// one per CU), and every wait is bounded: a barrier that does not complete
+// one per CU), and every wait is bounded: a wait that does not complete
 // within its spin budget is flagged in the status word and released, so the
 // kernel always drains.
 #pragma once
@@ -55,38 +55,11 @@ constexpr int kRsrcWord3 = 0x00020000;    // raw 32-bit buffer resource
 // is resident at once).
 constexpr int kTeamsPerLaunch = 256 / kTeam;
 
-// Team barrier.  safe: release arrival and acquire after the wait (formal
-// device-scope ordering).  Otherwise (all members on one XCD): every thread
-// waits for its own device-coherent stores, and the arrival and the polling
-// are relaxed atomics.
-__device__ __forceinline__ void team_sync(unsigned* cnt, unsigned target, unsigned* status, bool safe) {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores are done
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if (safe) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    else __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned spins = 0;
-    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        atomicOr(status, static_cast<unsigned>(STATUS_BARRIER_TIMEOUT));
-        break;
-      }
-    }
-    if (safe) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-}
-
-// Device-coherent 32-bit accesses (served by L2, never by a stale L1 line).
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// 16 bytes at float index i of a buffer, device-coherent (policy bit sc1);
-// indices past the buffer read zeros.
-__device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t rs, int i) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 4, 0, kPolicySc1);
-  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+// One tagged contribution (value in the low word, step tag in the high word),
+// a device-scope atomic load: never served by a stale cache line, and value
+// and tag always come from the same store.
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Up to 64 consecutive elements (count of them, a multiple of 4) into fp32
@@ -113,11 +86,75 @@ __device__ __forceinline__ void load_row64(const T* p, int count, bool vec, floa
   }
 }
 
+// Up to 64 consecutive bf16 elements (count of them, a multiple of 4) as
+// packed pairs; the rest are zero.  vec: 16-byte aligned rows.
+__device__ __forceinline__ void load_row64_bf16(const uint16_t* p, int count, bool vec, uint32_t (&out)[32]) {
+  if (vec) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const bool ok = 8 * c < count;
+      const uint4 v = *reinterpret_cast<const uint4*>(p + (ok ? 8 * c : 0));
+      out[4 * c] = ok ? v.x : 0u;
+      out[4 * c + 1] = ok ? v.y : 0u;
+      out[4 * c + 2] = ok ? v.z : 0u;
+      out[4 * c + 3] = ok ? v.w : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const bool ok = 2 * i < count;
+      const uint32_t lo = p[ok ? 2 * i : 0], hi = p[ok ? 2 * i + 1 : 0];
+      out[i] = ok ? (lo | (hi << 16)) : 0u;
+    }
+  }
+}
+
+// The first n (a multiple of 4, at most 64) bf16 values at p (8-byte
+// aligned) as packed pairs, all requested before any is used; the rest zero.
+__device__ __forceinline__ void read_slice_bf16(const uint16_t* p, int n, uint2 (&x)[16]) {
+#pragma unroll
+  for (int c = 0; c < 16; ++c) x[c] = 4 * c < n ? *reinterpret_cast<const uint2*>(p + 4 * c) : make_uint2(0u, 0u);
+}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// sum_e w[e] x[e] over 64 bf16 pairs-of-products (fp32 accumulation, two
+// products per instruction), four independent partial sums
+__device__ __forceinline__ float dot64_bf16(const uint32_t (&w)[32], const uint2 (&x)[16]) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    acc[c & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[2 * c]),
+                                                  __builtin_bit_cast(bf16x2, x[c].x), acc[c & 3], false);
+    acc[c & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[2 * c + 1]),
+                                                  __builtin_bit_cast(bf16x2, x[c].y), acc[c & 3], false);
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// The first n (a multiple of 4, at most 64) floats at p, 16 bytes at a time,
+// all requested before any is used (LDS latency is paid once); the rest zero.
+__device__ __forceinline__ void read_slice(const float* p, int n, float4 (&x)[16]) {
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    x[c] = 4 * c < n ? *reinterpret_cast<const float4*>(p + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+// sum_e w[e] x[e] over 64 elements, four independent partial sums
+__device__ __forceinline__ float dot64(const float (&w)[64], const float4 (&x)[16]) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    acc[c & 3] += (w[4 * c] * x[c].x + w[4 * c + 1] * x[c].y) + (w[4 * c + 2] * x[c].z + w[4 * c + 3] * x[c].w);
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 // LDS layout (fp32):
 //   s   [rpt][r]        state (identical in every team member)
 //   u   [rpt][64]       silu(t) of this workgroup's rows
 //   pk  [rpt][K][64]    P values of this workgroup's rows
 //   red [8][rpt][64]    per-wave partial sums of t
+// and, for bf16 weights, bf16 copies of s [rpt][r] and u [rpt][64] (the
+// matrix-vector inputs: bf16 products, fp32 sums); then, at byte offset stage (256-aligned) when given, the staged bf16 weight
+// slices as 16-byte chunks: W_up[:, r0:r1] as [r][8] (row slices padded to 8
+// chunks) and W_s[r0:r1, :] as [nr][r / 8].
 // One team member: workgroup j of team `team` (requests team * rpt ...).
 // done: when given (bf16 states), the bf16 states are stored with
 // device-scope stores and the member counts itself in there once they are
@@ -127,7 +164,6 @@ __device__ __forceinline__ void scan_team(const ScanArgs& a, float* sm, int team
   const int r = a.r;
   const int rpt = a.rpt;                      // requests per team
   const int b0 = team * rpt;
-  if (b0 >= a.B) return;   // placeholder workgroup of a partly used XCD slot
   const int nb = (a.B - b0) < rpt ? (a.B - b0) : rpt;
   const int nr = r / kTeam, r0 = j * nr;     // this workgroup's rows; also columns per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -136,98 +172,132 @@ __device__ __forceinline__ void scan_team(const ScanArgs& a, float* sm, int team
   float* u = s + rpt * r;
   float* pk = u + rpt * 64;
   float* red = pk + rpt * a.K * 64;
+  uint16_t* s16 = reinterpret_cast<uint16_t*>(red + 8 * rpt * 64);
+  uint16_t* u16 = s16 + rpt * r;
+  constexpr bool kBf16 = sizeof(T) == 2;
 
   const T* Wd = static_cast<const T*>(a.w_down);
   const T* Wu = static_cast<const T*>(a.w_up);
   const long ldd = static_cast<long>(a.D) + r;
   const bool vec = Elem<T>::kPerLane == 4 || (nr % 8) == 0;   // 16-byte aligned slices
 
-  // ---- one-shot preload: W_up columns (phase 2, thread = output row n),
-  //      the P values, then W_s rows (phase 1 from the second step on)
-  float wu_reg[64], ws_reg[64];
-  {
-    const int n = threadIdx.x < r ? threadIdx.x : 0;
-    load_row64(Wu + static_cast<long>(n) * r + r0, nr, vec, wu_reg);
+  // ---- one-shot preload: the P values, W_up columns (phase 2, thread =
+  //      output row n) and W_s rows (phase 1, lane = row, wave = column slice)
+  float wu_reg[64], ws_reg[64];              // fp32 weights
+  uint32_t wu_p[32], ws_p[32];                // bf16 weights, packed pairs
+  constexpr int kPMax = 8;                    // P values per thread and pass
+  const int np = nb * a.K * nr;
+  auto p_index = [&](int idx) {
+    const int bb = idx / (a.K * nr), k = (idx / nr) % a.K, i = idx % nr;
+    return (static_cast<long>(b0 + bb) * a.K + k) * r + r0 + i;
+  };
+  auto p_slot = [&](int idx) {
+    const int bb = idx / (a.K * nr), k = (idx / nr) % a.K, i = idx % nr;
+    return (bb * a.K + k) * 64 + i;
+  };
+  bool staged = false;
+  if constexpr (sizeof(T) == 2) {
+    if (a.stage > 0 && np <= kPMax * kThreads) {
+      // Both slices pass through LDS: direct-to-LDS loads in which consecutive
+      // lanes take consecutive 16-byte chunks of a row, so one wave
+      // instruction covers whole cache lines (thread-per-row loads would touch
+      // 64 lines per instruction); then each thread reads its row back.  The
+      // chunk index inside a row is XOR-ed with the row's low three bits, so
+      // that the read-back of one chunk by 8 consecutive rows hits 8 different
+      // bank groups.
+      staged = true;
+      float pv[kPMax];
+#pragma unroll
+      for (int q = 0; q < kPMax; ++q) {
+        const int idx = static_cast<int>(threadIdx.x) + q * kThreads;
+        pv[q] = a.P[p_index(idx < np ? idx : np - 1)];
+      }
+      const int cpr = nr / 8, cps = r / 8;    // 16-byte chunks of a W_up row slice / of a W_s row
+      uint4* su = reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(sm) + a.stage);   // [r][8]
+      uint4* sw = su + r * 8;                                                                   // [nr][cps]
+      for (int i = wave * 64; i < r * 8; i += kThreads) {
+        const int p = i + lane, n = p >> 3, k = (p & 7) ^ (n & 7);
+        if (k < cpr) load_lds16(Wu + static_cast<long>(n) * r + r0 + k * 8, su + i);
+      }
+      for (int i = wave * 64; i < nr * cps; i += kThreads) {
+        const int p = i + lane, row = p / cps, c = (p % cps) ^ (row & 7);
+        if (row < nr) load_lds16(Wd + static_cast<long>(r0 + row) * ldd + a.D + c * 8, sw + i);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+      __syncthreads();
+      const int n = static_cast<int>(threadIdx.x) < r ? static_cast<int>(threadIdx.x) : 0;
+      const int row = lane < nr ? lane : 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+        const uint4 vu = k < cpr ? su[n * 8 + (k ^ (n & 7))] : zero;
+        const uint4 vs = k < cpr ? sw[row * cps + ((wave * cpr + k) ^ (row & 7))] : zero;
+        wu_p[4 * k] = vu.x; wu_p[4 * k + 1] = vu.y; wu_p[4 * k + 2] = vu.z; wu_p[4 * k + 3] = vu.w;
+        ws_p[4 * k] = vs.x; ws_p[4 * k + 1] = vs.y; ws_p[4 * k + 2] = vs.z; ws_p[4 * k + 3] = vs.w;
+      }
+#pragma unroll
+      for (int q = 0; q < kPMax; ++q) {
+        const int idx = static_cast<int>(threadIdx.x) + q * kThreads;
+        if (idx < np) pk[p_slot(idx)] = pv[q];
+      }
+    }
   }
-  {
-    constexpr int kPMax = 8;                  // values per thread and pass
-    const int np = nb * a.K * nr;
+  if (!staged) {
+    {
+      const int n = threadIdx.x < r ? threadIdx.x : 0;
+      if constexpr (kBf16) load_row64_bf16(Wu + static_cast<long>(n) * r + r0, nr, vec, wu_p);
+      else load_row64(Wu + static_cast<long>(n) * r + r0, nr, vec, wu_reg);
+    }
     for (int base = threadIdx.x; base < np; base += kPMax * kThreads) {
       float pv[kPMax];
 #pragma unroll
       for (int q = 0; q < kPMax; ++q) {
-        int idx = base + q * kThreads;
-        idx = idx < np ? idx : np - 1;   // clamped: unconditional loads
-        const int bb = idx / (a.K * nr), k = (idx / nr) % a.K, i = idx % nr;
-        pv[q] = a.P[(static_cast<long>(b0 + bb) * a.K + k) * r + r0 + i];
+        const int idx = base + q * kThreads;
+        pv[q] = a.P[p_index(idx < np ? idx : np - 1)];   // clamped: unconditional loads
       }
 #pragma unroll
       for (int q = 0; q < kPMax; ++q) {
         const int idx = base + q * kThreads;
-        if (idx < np) {
-          const int bb = idx / (a.K * nr), k = (idx / nr) % a.K, i = idx % nr;
-          pk[(bb * a.K + k) * 64 + i] = pv[q];
-        }
+        if (idx < np) pk[p_slot(idx)] = pv[q];
       }
     }
-  }
-  {
-    const int row = lane < nr ? lane : 0;
-    load_row64(Wd + (r0 + row) * ldd + a.D + wave * nr, nr, vec, ws_reg);
+    {
+      const int row = lane < nr ? lane : 0;
+      if constexpr (kBf16) load_row64_bf16(Wd + (r0 + row) * ldd + a.D + wave * nr, nr, vec, ws_p);
+      else load_row64(Wd + (r0 + row) * ldd + a.D + wave * nr, nr, vec, ws_reg);
+    }
   }
 
-  unsigned* cnt = a.counters + CNT_TEAM0 + team;
-  unsigned* place = a.counters + CNT_TEAM0 + kTeamsPerLaunch + team;
   unsigned* status = a.counters + CNT_STATUS;
-  __shared__ int safe_sh;
-  // placement check, settled before the first step while the W_s loads are in
-  // flight: every member adds 1 to the team's placement word if XCC_ID
-  // (hardware register 20, 4 bits) matches the assumed workgroup -> XCD
-  // assignment, 1 << 16 if not; once all members have counted in, any high
-  // bit selects the release/acquire barriers.  One device-scope atomic word
-  // carries both, so no other ordering is needed.
-  if (threadIdx.x == 0) {
-    const int xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15;
-    const unsigned mine = xcc == static_cast<int>(blockIdx.x & 7) ? 1u : (1u << 16);
-    unsigned v = __hip_atomic_fetch_add(place, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + mine;
-    const unsigned target = (a.cnt_base / static_cast<unsigned>(a.K * kTeam) + 1) * kTeam;
-    unsigned spins = 0;
-    while ((v & 0xffffu) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      v = __hip_atomic_load(place, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (++spins > kSpinLimit) {
-        atomicOr(status, static_cast<unsigned>(STATUS_BARRIER_TIMEOUT));
-        v |= 1u << 16;
-        break;
-      }
-    }
-    safe_sh = (v >> 16) != 0;
-  }
   for (int idx = threadIdx.x; idx < rpt * r; idx += kThreads) s[idx] = 0.f;
   // u past the workgroup's rows stays zero (read by the 8-wide chunks)
   for (int idx = threadIdx.x; idx < rpt * 64; idx += kThreads) u[idx] = 0.f;
+  if constexpr (kBf16) {
+    for (int idx = threadIdx.x; idx < rpt * r; idx += kThreads) s16[idx] = 0;
+    for (int idx = threadIdx.x; idx < rpt * 64; idx += kThreads) u16[idx] = 0;
+  }
+  // the weight slices are used at every step: settle their loads once here,
+  // so that no wait inside the loop is tied to them
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
-  const bool safe = safe_sh != 0;
-  const __amdgpu_buffer_rsrc_t urs = __builtin_amdgcn_make_buffer_rsrc(
-      a.U, 0, 2 * a.B * kTeam * r * static_cast<int>(sizeof(float)), kRsrcWord3);
+  uint64_t* U64 = reinterpret_cast<uint64_t*>(a.U);
 
   for (int k = 0; k < a.K; ++k) {
     // (1) t = P_k + W_s s: wave w multiplies columns [w nr, (w+1) nr) for
     //     row r0 + lane; the state is zero at the first step
     if (k > 0) {
       for (int bb = 0; bb < nb; ++bb) {
-        const float* sv = s + bb * r + wave * nr;
-        float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 64; e += 8) {
-          if (e < nr) {   // uniform
-            const float4 x0 = *reinterpret_cast<const float4*>(sv + e);
-            const float4 x1 = *reinterpret_cast<const float4*>(sv + e + 4);
-            acc0 += (ws_reg[e] * x0.x + ws_reg[e + 1] * x0.y) + (ws_reg[e + 2] * x0.z + ws_reg[e + 3] * x0.w);
-            acc1 += (ws_reg[e + 4] * x1.x + ws_reg[e + 5] * x1.y) + (ws_reg[e + 6] * x1.z + ws_reg[e + 7] * x1.w);
-          }
+        float d;
+        if constexpr (kBf16) {
+          uint2 x[16];
+          read_slice_bf16(s16 + bb * r + wave * nr, nr, x);
+          d = dot64_bf16(ws_p, x);
+        } else {
+          float4 x[16];
+          read_slice(s + bb * r + wave * nr, nr, x);
+          d = dot64(ws_reg, x);
         }
-        red[(wave * rpt + bb) * 64 + lane] = acc0 + acc1;
+        red[(wave * rpt + bb) * 64 + lane] = d;
       }
     }
     __syncthreads();
@@ -241,59 +311,86 @@ __device__ __forceinline__ void scan_team(const ScanArgs& a, float* sm, int team
           for (int w = 0; w < 8; ++w) acc += red[(w * rpt + bb) * 64 + lane];
           t += acc;
         }
-        u[bb * 64 + lane] = t / (1.0f + expf(-t));
+        const float sl = t / (1.0f + expf(-t));
+        if constexpr (kBf16) u16[bb * 64 + lane] = f32_to_bf16(sl);
+        else u[bb * 64 + lane] = sl;
       }
     }
     __syncthreads();
     // (2) this workgroup's contribution c_n = sum_i W_up[n, r0 + i] u_i,
-    //     thread = output row n
-    float* part_out = a.U + ((static_cast<long>(k & 1) * a.B + b0) * kTeam + j) * r;
+    //     thread = output row n, stored with the step's tag beside it
+    const unsigned tag = a.tag0 + static_cast<unsigned>(k) + 1u;
+    uint64_t* part_out = U64 + ((static_cast<long>(k & 1) * a.B + b0) * kTeam + j) * r;
     if (static_cast<int>(threadIdx.x) < r) {
       for (int bb = 0; bb < nb; ++bb) {
-        const float* uv = u + bb * 64;
-        float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 64; e += 8) {
-          if (e < nr) {   // uniform
-            const float4 x0 = *reinterpret_cast<const float4*>(uv + e);
-            const float4 x1 = *reinterpret_cast<const float4*>(uv + e + 4);
-            acc0 += (wu_reg[e] * x0.x + wu_reg[e + 1] * x0.y) + (wu_reg[e + 2] * x0.z + wu_reg[e + 3] * x0.w);
-            acc1 += (wu_reg[e + 4] * x1.x + wu_reg[e + 5] * x1.y) + (wu_reg[e + 6] * x1.z + wu_reg[e + 7] * x1.w);
-          }
+        float d;
+        if constexpr (kBf16) {
+          uint2 x[16];
+          read_slice_bf16(u16 + bb * 64, nr, x);
+          d = dot64_bf16(wu_p, x);
+        } else {
+          float4 x[16];
+          read_slice(u + bb * 64, nr, x);
+          d = dot64(wu_reg, x);
         }
-        st_dev(part_out + static_cast<long>(bb) * kTeam * r + threadIdx.x, acc0 + acc1);
+        const uint64_t tv = (static_cast<uint64_t>(tag) << 32) | __float_as_uint(d);
+        __hip_atomic_store(part_out + static_cast<long>(bb) * kTeam * r + threadIdx.x, tv, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    team_sync(cnt, a.cnt_base + static_cast<unsigned>((k + 1) * kTeam), status, safe);
-    // (3) s += sum over the team's contributions, in workgroup order
-    const float* pkk = a.U + (static_cast<long>(k & 1) * a.B + b0) * kTeam * r;
-    for (int q = threadIdx.x; q < nb * (r / 4); q += kThreads) {
-      const int bb = q / (r / 4), n = (q % (r / 4)) * 4;
-      float4 v[kTeam];
-#pragma unroll
-      for (int w = 0; w < kTeam; ++w)
-        v[w] = ld_dev4(urs, static_cast<int>((pkk - a.U) + (static_cast<long>(bb) * kTeam + w) * r + n));
-      float4 acc = *reinterpret_cast<const float4*>(s + bb * r + n);
+    // (3) s += sum over the team's contributions, in workgroup order; each
+    //     thread re-reads its entries until all carry this step's tag
+    const long ubase = (static_cast<long>(k & 1) * a.B + b0) * kTeam * r;
+    for (int q = threadIdx.x; q < nb * (r / 2); q += kThreads) {
+      const int bb = q / (r / 2), n = (q % (r / 2)) * 2;
+      const uint64_t* src = U64 + ubase + static_cast<long>(bb) * kTeam * r + n;
+      uint64_t v[kTeam][2];
 #pragma unroll
       for (int w = 0; w < kTeam; ++w) {
-        acc.x += v[w].x; acc.y += v[w].y; acc.z += v[w].z; acc.w += v[w].w;
+        v[w][0] = ld_tagged(src + w * r);
+        v[w][1] = ld_tagged(src + w * r + 1);
       }
-      *reinterpret_cast<float4*>(s + bb * r + n) = acc;
-      if (n >= r0 && n < r0 + nr) {   // this workgroup's rows (n, r0, nr are multiples of 4)
+      unsigned spins = 0;
+      for (;;) {
+        unsigned bad = 0;
+#pragma unroll
+        for (int w = 0; w < kTeam; ++w)
+          bad |= static_cast<unsigned>(v[w][0] >> 32) ^ tag | static_cast<unsigned>(v[w][1] >> 32) ^ tag;
+        if (bad == 0) break;
+        if (++spins > kSpinLimit) {
+          atomicOr(status, static_cast<unsigned>(STATUS_BARRIER_TIMEOUT));
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int w = 0; w < kTeam; ++w) {
+          v[w][0] = ld_tagged(src + w * r);
+          v[w][1] = ld_tagged(src + w * r + 1);
+        }
+      }
+      float2 acc = *reinterpret_cast<const float2*>(s + bb * r + n);
+#pragma unroll
+      for (int w = 0; w < kTeam; ++w) {
+        acc.x += __uint_as_float(static_cast<unsigned>(v[w][0]));
+        acc.y += __uint_as_float(static_cast<unsigned>(v[w][1]));
+      }
+      *reinterpret_cast<float2*>(s + bb * r + n) = acc;
+      if constexpr (kBf16)
+        *reinterpret_cast<uint32_t*>(s16 + bb * r + n) =
+            static_cast<uint32_t>(f32_to_bf16(acc.x)) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
+      if (n >= r0 && n < r0 + nr) {   // this workgroup's rows (n, r0, nr are even)
         const long o = (static_cast<long>(b0 + bb) * a.K + k) * r + n;
-        *reinterpret_cast<float4*>(a.Sf + o) = acc;
-        if (a.tap) *reinterpret_cast<float4*>(a.tap + o) = acc;
-        const float av[4] = {acc.x, acc.y, acc.z, acc.w};
+        *reinterpret_cast<float2*>(a.Sf + o) = acc;
+        if (a.tap) *reinterpret_cast<float2*>(a.tap + o) = acc;
         if (sizeof(T) == 2 && done) {
           // read by other workgroups in this launch: one device-scope store
-          uint64_t pk4 = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pk4 |= static_cast<uint64_t>(Elem<T>::from_f32(av[e])) << (16 * e);
-          __hip_atomic_store(reinterpret_cast<uint64_t*>(static_cast<T*>(a.Sb) + o), pk4, __ATOMIC_RELAXED,
+          const uint32_t pk2 = static_cast<uint32_t>(Elem<T>::from_f32(acc.x)) |
+                               (static_cast<uint32_t>(Elem<T>::from_f32(acc.y)) << 16);
+          __hip_atomic_store(reinterpret_cast<uint32_t*>(static_cast<T*>(a.Sb) + o), pk2, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
         } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) static_cast<T*>(a.Sb)[o + e] = Elem<T>::from_f32(av[e]);
+          static_cast<T*>(a.Sb)[o] = Elem<T>::from_f32(acc.x);
+          static_cast<T*>(a.Sb)[o + 1] = Elem<T>::from_f32(acc.y);
         }
       }
     }
@@ -307,7 +404,21 @@ __device__ __forceinline__ void scan_team(const ScanArgs& a, float* sm, int team
 }
 
 inline size_t scan_smem(int r, int rpt, int K) {
-  return (static_cast<size_t>(rpt) * r + rpt * 64 + static_cast<size_t>(rpt) * K * 64 + 8 * rpt * 64) * 4;
+  return (static_cast<size_t>(rpt) * r + rpt * 64 + static_cast<size_t>(rpt) * K * 64 + 8 * rpt * 64) * 4 +
+         (static_cast<size_t>(rpt) * r + rpt * 64) * 2;
+}
+
+// Team LDS with the weight staging area behind the scan's own regions when
+// it fits (bf16 weights, 16-byte row slices, one pass of P values).
+constexpr size_t kTeamLdsMax = 152 * 1024;
+inline size_t team_lds(int r, int rpt, int K, bool bf16, int* stage) {
+  const size_t base = (scan_smem(r, rpt, K) + 255) / 256 * 256;
+  const int nr = r / kTeam;
+  const size_t st = (static_cast<size_t>(r) * 8 + static_cast<size_t>(nr) * (r / 8)) * 16;   // [r][8] + [nr][r/8] chunks
+  const bool ok = bf16 && nr % 8 == 0 && static_cast<long>(rpt) * K * nr <= 8 * kThreads &&
+                  base + st <= kTeamLdsMax;
+  *stage = ok ? static_cast<int>(base) : 0;
+  return ok ? base + st : scan_smem(r, rpt, K);
 }
 
 // Requests per team: enough to cover B with one launch of kTeamsPerLaunch
