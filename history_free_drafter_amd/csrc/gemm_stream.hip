@@ -183,8 +183,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_stream_kernel(SArgs sa) {
   }
 
   // behind the first weight loads: each token's 1/rms, and the residual
-  // elements the epilogue updates (kRes per thread), so that their round
-  // trips overlap the stream
+  // elements the epilogue updates with their next-norm gains (kRes per
+  // thread), so that their round trips overlap the stream
   if (a.ssq) {
     for (int tl = wave; tl < M; tl += nwaves) {
       const long prow = a.qmap.row(a.tok0 + tl);
@@ -196,14 +196,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_stream_kernel(SArgs sa) {
       if (lane == 0) inv_rms[tl] = 1.0f / sqrtf(v / static_cast<float>(a.norm_len) + a.eps);
     }
   }
-  float xres[kRes];
+  float xres[kRes], gres[kRes];
 #pragma unroll
   for (int j = 0; j < kRes; ++j) {
     xres[j] = 0.f;
+    gres[j] = 0.f;
     const int e = threadIdx.x + j * blockDim.x;
     if (EPI == EPI_RESID && e < M * nrow) {
       const int tok = e / nrow, row = e % nrow;
       xres[j] = static_cast<const float*>(a.out)[a.omap.row(a.tok0 + tok) * a.ld_out + row0 + row];
+      gres[j] = Elem<T>::to_f32(static_cast<const T*>(a.next_gain)[row0 + row]);
     }
   }
   for (int ti = 0; ti < ntw; ++ti) {
@@ -289,14 +291,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_stream_kernel(SArgs sa) {
       static_cast<T*>(a.out)[orow * a.ld_out + grow] = Elem<T>::from_f32(v0);
     } else if (EPI == EPI_RESID) {
       float* x = static_cast<float*>(a.out) + orow * a.ld_out + grow;
-      float xo = 0.f;
+      float xo = 0.f, go = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < kRes; ++jj) xo = jj == j ? xres[jj] : xo;
+      for (int jj = 0; jj < kRes; ++jj) {
+        xo = jj == j ? xres[jj] : xo;
+        go = jj == j ? gres[jj] : go;
+      }
       const float nv = (j < kRes ? xo : *x) + v0;
       *x = nv;
-      const T* ng = static_cast<const T*>(a.next_gain);
-      static_cast<T*>(a.xb_out)[a.xmap.row(a.tok0 + tok) * a.ld_xb + grow] =
-          Elem<T>::from_f32(Elem<T>::to_f32(ng[grow]) * nv);
+      const float gain = j < kRes ? go : Elem<T>::to_f32(static_cast<const T*>(a.next_gain)[grow]);
+      static_cast<T*>(a.xb_out)[a.xmap.row(a.tok0 + tok) * a.ld_xb + grow] = Elem<T>::from_f32(gain * nv);
       if (a.tap) a.tap[a.tmap.row(a.tok0 + tok) * a.ld_tap + grow] = nv;
       Y[tok * R + row] = nv * nv;
     } else {  // SwiGLU: silu(gate) * up
