@@ -137,6 +137,10 @@ SMALL = [
     # one 64-wide k stage everywhere, token counts just above the tile threshold
     _small("tiled_k64_bf16", B=70, m=1, D=64, n_q=1, n_kv=1, ffn=64, K=1, rank=64,
            vocab=300, n_layers=1),
+    # more requests than one scan launch takes (256): a second launch reuses
+    # the exchange slots with step tags offset past the first launch's
+    _small("scan_chunks_bf16", B=300, m=1, D=64, n_q=1, n_kv=1, ffn=32, K=2, rank=32,
+           vocab=200, n_layers=1),
 ]
 
 
