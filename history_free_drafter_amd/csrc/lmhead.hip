@@ -321,7 +321,7 @@ constexpr int kStatePad = 32;             // bf16 elements after each staged sta
 struct FuseArgs {
   ScanArgs sa;
   LmArgs la;
-  int nteam;        // scan teams (one request each): blocks xq * 8 + t, t < nteam, xq < 8
+  int nteam;        // scan teams (one request each): blocks xq * 8 + t, t < nteam, xq < team size
   unsigned* done;   // published-state counter of the team members
 };
 
@@ -338,8 +338,9 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
   const int bx = blockIdx.x, xq = bx >> 3, x = bx & 7;
   const int nteam = f.nteam;
   unsigned* done = f.done;
+  constexpr int kTeam = (RK * 32) % 256 == 0 ? 16 : 8;   // members per scan team (team_size(r, B), B <= 8)
   if (xq < kTeam && x < nteam) {
-    scan_team<uint16_t>(f.sa, reinterpret_cast<float*>(smem), x, xq, done);
+    scan_team<uint16_t, kTeam>(f.sa, reinterpret_cast<float*>(smem), x, xq, done);
     return;
   }
 
@@ -534,12 +535,13 @@ hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, hipStream_t st) 
   f.sa.tag0 = 0;
   f.nteam = s0.B;
   f.done = s0.counters + counter_seq_done();
-  const int grid = cus > kTeam * 8 ? cus : kTeam * 8;
+  const int team = team_size(s0.r, s0.B);
+  const int grid = cus > team * 8 ? cus : team * 8;
   f.la = l0;
-  f.la.G = grid - kTeam * f.nteam;
+  f.la.G = grid - team * f.nteam;
   if (f.la.G > kFuseMaxHelpers) return hipErrorInvalidValue;
   const int RK = s0.r / 32;
-  const size_t sm_scan = team_lds(s0.r, 1, s0.K, true, &f.sa.stage);
+  const size_t sm_scan = team_lds(s0.r, team, 1, s0.K, true, &f.sa.stage);
   const void* fn = RK == 16 ? reinterpret_cast<const void*>(&seqhead_kernel<16>)
                             : reinterpret_cast<const void*>(&seqhead_kernel<10>);
   size_t sm = RK == 16 ? seqhead_lds<16>(l0.M, s0.r) : seqhead_lds<10>(l0.M, s0.r);

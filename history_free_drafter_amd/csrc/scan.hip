@@ -8,28 +8,38 @@ using namespace scan_detail;
 
 namespace {
 
-template <typename T>
+template <typename T, int TEAM>
 __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
   extern __shared__ __align__(16) float sm[];
-  scan_team<T>(a, sm, blockIdx.x / kTeam, blockIdx.x % kTeam, nullptr);
+  scan_team<T, TEAM>(a, sm, blockIdx.x / TEAM, blockIdx.x % TEAM, nullptr);
+}
+
+template <typename T, int TEAM>
+hipError_t launch_team(const ScanArgs& a, size_t sm, hipStream_t st) {
+  const int nteam = (a.B + a.rpt - 1) / a.rpt;
+  hipLaunchKernelGGL((scan_kernel<T, TEAM>), dim3(nteam * TEAM), dim3(kThreads), sm, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 size_t scan_scratch_floats(int B, int r) {
-  const int b = B < kTeamsPerLaunch * kReq ? B : kTeamsPerLaunch * kReq;
-  return 4 * static_cast<size_t>(b) * kTeam * r;   // [2][b][kTeam][r] tagged 64-bit words
+  const int per = teams_per_launch(r, B) * kReq;
+  const int b = B < per ? B : per;
+  return 4 * static_cast<size_t>(b) * team_size(r, B) * r;   // [2][b][team][r] tagged 64-bit words
 }
 
 hipError_t launch_scan(const ScanArgs& a0, bool bf16, hipStream_t st) {
-  const int rpt = pick_rpt(a0.B);
+  const int team = team_size(a0.r, a0.B);
+  const int rpt = pick_rpt(a0.B, a0.r);
   int stage = 0;
-  const size_t sm = team_lds(a0.r, rpt, a0.K, bf16, &stage);
-  const int per_launch = kTeamsPerLaunch * rpt;
-  const void* fn = bf16 ? reinterpret_cast<const void*>(&scan_kernel<uint16_t>)
-                        : reinterpret_cast<const void*>(&scan_kernel<float>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(sm));
+  const size_t sm = team_lds(a0.r, team, rpt, a0.K, bf16, &stage);
+  const int per_launch = teams_per_launch(a0.r, a0.B) * rpt;
+  const void* fn = bf16 ? (team == 16 ? reinterpret_cast<const void*>(&scan_kernel<uint16_t, 16>)
+                                      : reinterpret_cast<const void*>(&scan_kernel<uint16_t, 8>))
+                        : (team == 16 ? reinterpret_cast<const void*>(&scan_kernel<float, 16>)
+                                      : reinterpret_cast<const void*>(&scan_kernel<float, 8>));
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
   if (e != hipSuccess) return e;
   int chunk = 0;
   for (int b = 0; b < a0.B; b += per_launch, ++chunk) {
@@ -43,13 +53,8 @@ hipError_t launch_scan(const ScanArgs& a0, bool bf16, hipStream_t st) {
     a.Sb = static_cast<char*>(a0.Sb) + off * (bf16 ? 2 : 4);
     a.tap = a0.tap ? a0.tap + off : nullptr;
     a.tag0 = static_cast<unsigned>(chunk * a0.K);
-    const int nteam = (a.B + rpt - 1) / rpt;
-    const dim3 grid(nteam * kTeam), block(kThreads);
-    if (bf16)
-      hipLaunchKernelGGL(scan_kernel<uint16_t>, grid, block, sm, st, a);
-    else
-      hipLaunchKernelGGL(scan_kernel<float>, grid, block, sm, st, a);
-    e = hipGetLastError();
+    if (bf16) e = team == 16 ? launch_team<uint16_t, 16>(a, sm, st) : launch_team<uint16_t, 8>(a, sm, st);
+    else e = team == 16 ? launch_team<float, 16>(a, sm, st) : launch_team<float, 8>(a, sm, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
