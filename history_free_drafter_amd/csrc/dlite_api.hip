@@ -401,6 +401,7 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   la.part_max = pmax; la.part_idx = pidx; la.G = p.G;
   la.cand = candidates; la.max_logit = max_logit; la.tap = tp.logits;
   la.anchors = anchor_ids; la.K = K; la.counters = counters; la.part = TPs;
+  la.xcd_counters = counters + counter_lm_xcd();
   if (seqhead_fused(B, K, r, bf16)) {
     DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
     DLITE_LAUNCH(launch_seqhead(sa, la, st));

@@ -10,17 +10,18 @@
 namespace dlite {
 
 // Workspace counters, zeroed by the first kernel of every draft step.
-// Words 0..15 are fixed counters; the scan's team barriers follow, then the
-// arrival counters of the weight-streaming GEMMs.
-// CNT_LM_DONE + c: finished workgroups of the c-th 32-token launch of the
-// streaming vocabulary kernels (fewer than 64 tokens, so c is 0 or 1).
+// CNT_LM_DONE: XCD groups of a streaming vocabulary launch whose workgroups
+// have all published (counter_lm_xcd(): the per-group arrivals); both levels
+// reset themselves, so consecutive 32-token launches reuse them.
 // counter_seq_done(): scan team members that have published their states
 // (fused scan + vocabulary kernel), on a 256-byte line of its own.
+// counter_gemm(): arrival counters of the weight-streaming GEMMs' k slices.
 enum Counter { CNT_LM_DONE = 0, CNT_STATUS = 2 };
 size_t scan_scratch_floats(int B, int r);   // size of ScanArgs::U
 inline int counter_seq_done() { return 64; }
 inline int counter_gemm() { return counter_seq_done() + 64; }
-inline int counter_words() { return counter_gemm() + 2 * 128; }
+inline int counter_lm_xcd() { return counter_gemm() + 2 * 128; }   // [8 XCDs] x 16 words
+inline int counter_words() { return counter_lm_xcd() + 8 * 16; }
 enum Status { STATUS_BARRIER_TIMEOUT = 1 };
 
 // Partial sums of squares per activation row: one slot per producing
@@ -169,6 +170,7 @@ struct LmArgs {
   const int32_t* anchors; // [B]: requests with an out-of-range anchor get -1
   int K;                 // tokens per request (token t belongs to request t / K)
   unsigned* counters;
+  unsigned* xcd_counters; // counter_lm_xcd() words: arrivals per XCD (64-byte apart)
   float* part;           // partial-tile scratch of the tiled path (gemm_tile_scratch)
 };
 hipError_t launch_lmhead(const LmArgs& a, bool bf16, hipStream_t st);

@@ -68,13 +68,27 @@ __device__ __forceinline__ void publish_partial(const LmArgs& a, long o, float v
   __hip_atomic_store(a.part_idx + o, i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void reduce_if_last(const LmArgs& a, long G, int* last) {
+// Arrival is counted in two levels so that no counter takes more than about
+// 32 atomics: per XCD of the workgroup (blockIdx % 8; n_xcd = workgroups of
+// this launch that publish on that XCD), then the last one of each XCD counts
+// in globally (n_busy = XCDs with at least one such workgroup).
+__device__ __forceinline__ void reduce_if_last(const LmArgs& a, long G, int* last, int n_xcd, int n_busy) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned* cnt = a.counters + CNT_LM_DONE + a.tok0 / 32;
-    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *last = prev + 1 == static_cast<unsigned>(G);
+    // the last arrival at each level puts its counter back to zero for the
+    // next launch on the stream (a step may run several 32-token launches)
+    unsigned* cx = a.xcd_counters + static_cast<int>(blockIdx.x & 7) * 16;
+    const unsigned px = __hip_atomic_fetch_add(cx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool lg = false;
+    if (px + 1 == static_cast<unsigned>(n_xcd)) {
+      __hip_atomic_store(cx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned* cnt = a.counters + CNT_LM_DONE;
+      const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lg = prev + 1 == static_cast<unsigned>(n_busy);
+      if (lg) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *last = lg;
   }
   __syncthreads();
   if (!*last) return;
@@ -189,7 +203,10 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_kernel(LmArgs a) {
       if (better(sv[w][threadIdx.x], si[w][threadIdx.x], v, i)) { v = sv[w][threadIdx.x]; i = si[w][threadIdx.x]; }
     publish_partial(a, static_cast<long>(a.tok0 + threadIdx.x) * G + g, v, i);
   }
-  reduce_if_last(a, G, &last);
+  {
+    const int gw = static_cast<int>(G), x = static_cast<int>(blockIdx.x & 7);
+    reduce_if_last(a, G, &last, (gw - x + 7) / 8, gw < 8 ? gw : 8);
+  }
 }
 
 // Pipelined variant for at most 16 tokens: each wave streams its tiles
@@ -295,7 +312,10 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_pipe_kernel(LmArgs a) {
       if (better(sv[w][threadIdx.x], si[w][threadIdx.x], v, i)) { v = sv[w][threadIdx.x]; i = si[w][threadIdx.x]; }
     publish_partial(a, static_cast<long>(a.tok0 + threadIdx.x) * G + g, v, i);
   }
-  reduce_if_last(a, G, &last);
+  {
+    const int gw = static_cast<int>(G), x = static_cast<int>(blockIdx.x & 7);
+    reduce_if_last(a, G, &last, (gw - x + 7) / 8, gw < 8 ? gw : 8);
+  }
 }
 
 
@@ -498,7 +518,16 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
       if (better(sv[w][threadIdx.x], si[w][threadIdx.x], v, i)) { v = sv[w][threadIdx.x]; i = si[w][threadIdx.x]; }
     publish_partial(a, static_cast<long>(threadIdx.x) * G + h, v, i);
   }
-  reduce_if_last(a, G, &last);
+  {
+    // helpers only: the team members of XCD x do not publish
+    int nx = 0, busy = 0;
+    for (int q = 0; q < 8; ++q) {
+      const int n = (static_cast<int>(gridDim.x) - q + 7) / 8 - (q < nteam ? kTeam : 0);
+      busy += n > 0;
+      if (q == static_cast<int>(blockIdx.x & 7)) nx = n;
+    }
+    reduce_if_last(a, G, &last, nx, busy);
+  }
   if (touch == 0x9e3779b9u && M < 0) a.cand[0] = 0;   // keeps the touch loads
 }
 
