@@ -367,10 +367,27 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
         }
     } else {
       float ssq = 0.f;
+      // residual epilogue of the reduce pass: the residual and gain loads of
+      // a 32-row block go out together before any of its stores (a load
+      // issued after a store the compiler cannot tell apart waits a round
+      // trip; the full-K kernel keeps its registers for the main loop)
+      constexpr bool kBatch = EPI == EPI_RESID && MODE == MODE_REDUCE1;
+      float4 xr[4];
+      uint2 gr[4];
+      auto fetch = [&](int i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          int n = nb * kBN + wn * 128 + i * 32 + 8 * q + 4 * fk;
+          n = (CHK && n >= a.N) ? nb * kBN : n;   // in range; unused
+          xr[q] = *reinterpret_cast<const float4*>(static_cast<const float*>(a.out) + orow * a.ld_out + n);
+          gr[q] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.next_gain) + n);
+        }
+      };
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          if (kBatch && q == 0) fetch(i);
           const int n = nb * kBN + wn * 128 + i * 32 + 8 * q + 4 * fk;
           if (CHK && n >= a.N) continue;
           const float4 y = make_float4(acc[i][u][4 * q] * inv[u], acc[i][u][4 * q + 1] * inv[u],
@@ -383,11 +400,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow * a.ld_out + n) = make_uint2(h0, h1);
           } else {  // residual
             float4* xp = reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * a.ld_out + n);
-            float4 x = *xp;
+            float4 x = kBatch ? xr[q] : *xp;
             x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
             *xp = x;
             ssq += (x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w);
-            const uint2 gw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.next_gain) + n);
+            const uint2 gw = kBatch ? gr[q] : *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.next_gain) + n);
             const float g0 = __uint_as_float(gw.x << 16), g1 = __uint_as_float(gw.x & 0xffff0000u);
             const float g2 = __uint_as_float(gw.y << 16), g3 = __uint_as_float(gw.y & 0xffff0000u);
             const uint32_t h0 = static_cast<uint32_t>(f32_to_bf16(g0 * x.x)) | (static_cast<uint32_t>(f32_to_bf16(g1 * x.y)) << 16);
