@@ -246,6 +246,28 @@ def accept_prefix(cand: np.ndarray, target: np.ndarray):
     return A.astype(np.int64), nxt.astype(np.int64)
 
 
+def boundary_features(verify_hidden: np.ndarray, A: np.ndarray) -> np.ndarray:
+    """The next round's boundary features, taken from the verify pass at index A.
+
+    [W] "一轮执行后，缓存、锚点与隐藏状态怎样对齐", step 5 and the state-relation
+    pseudo-code after it: the m selected target layers' hidden states are read
+    at verify index A_b of the input [a, d_1..d_K], the last input that stays
+    (index 0 is the anchor a when nothing passed, index 2 is d_2 when two
+    passed); positions of rejected candidates are never used.
+    verify_hidden: [m, B, T, D], one [B, T, D] block per selected layer (T
+    verify inputs per request); A: [B] with 0 <= A_b < T.  Returns [B, m, D].
+    """
+    verify_hidden = np.asarray(verify_hidden)
+    A = np.asarray(A)
+    m, B, T, D = verify_hidden.shape
+    if A.shape != (B,) or (A < 0).any() or (A >= T).any():
+        raise ValueError("accept lengths must lie in [0, T)")
+    H = np.empty((B, m, D), dtype=verify_hidden.dtype)
+    for b in range(B):
+        H[b] = verify_hidden[:, b, int(A[b]), :]
+    return H
+
+
 def prefix_survival(c: np.ndarray) -> np.ndarray:
     """P(A >= k) = prod_{i<=k} c_i for k = 1..K ([F] "为什么验证仍然只接受最长前缀")."""
     return np.cumprod(np.asarray(c, dtype=np.float64), axis=-1)

@@ -52,6 +52,52 @@ def test_verify_index_semantics():
         assert int(nxt[0]) == int(tgt[0, A_want])
 
 
+def _coded_verify_hidden(m, B, T, D):
+    """[m, B, T, D] whose every element names its (layer, request, position)."""
+    l, b, i = np.meshgrid(np.arange(m), np.arange(B), np.arange(T), indexing="ij")
+    code = (1_000_000 * l + 100 * b + i).astype(np.float64)
+    return np.repeat(code[..., None], D, axis=3)
+
+
+def test_boundary_features_take_verify_index_a():
+    """Next-round features come from verify index A (A = 0: a, A = 2: d_2)."""
+    rows = dict(r.split(":", 1) for r in golden("verify_index.txt"))
+    K, m, D = 4, 3, 5
+    names = ["a"] + [f"d_{i}" for i in range(1, K + 1)]
+    for a_str, name in rows.items():
+        pattern = [1] * int(a_str) + [0] * (K - int(a_str))
+        cand, tgt = _pattern_to_tokens(pattern)
+        A, _ = oracle.accept_prefix(cand, tgt)
+        vh = _coded_verify_hidden(m, 1, K + 1, D)
+        H = oracle.boundary_features(vh, A)
+        assert H.shape == (1, m, D)
+        pos = H[0, :, 0] % 100
+        assert (pos == names.index(name.strip())).all()
+        assert (H[0, :, 0] // 1_000_000 == np.arange(m)).all()     # layer order kept
+
+
+def test_boundary_features_never_use_rejected_positions():
+    rng = np.random.default_rng(5)
+    B, K, m, D = 64, 7, 2, 3
+    cand = rng.integers(0, 3, size=(B, K))
+    tgt = rng.integers(0, 3, size=(B, K + 1))
+    A, _ = oracle.accept_prefix(cand, tgt)
+    H = oracle.boundary_features(_coded_verify_hidden(m, B, K + 1, D), A)
+    for b in range(B):
+        p = int(H[b, 0, 0] % 100)
+        assert int(H[b, 0, 0] // 100) % 10_000 == b
+        assert (cand[b, :p] == tgt[b, :p]).all()            # every earlier draft passed
+        assert p == K or cand[b, p] != tgt[b, p]            # d_{p+1} (if any) was rejected
+
+
+def test_boundary_features_reject_out_of_range():
+    vh = np.zeros((1, 2, 3, 4))
+    with pytest.raises(ValueError):
+        oracle.boundary_features(vh, np.array([0, 3]))
+    with pytest.raises(ValueError):
+        oracle.boundary_features(vh, np.array([-1, 0]))
+
+
 def test_round_accounting():
     for row in golden("round_accounting.txt"):
         lhs, rhs = row.split(":")
@@ -152,6 +198,10 @@ class _FakeTarget:
             h = ((h ^ int(t)) * 1099511628211) % (1 << 61)
         return int((h + 7 * len(seq)) % self.V)
 
+    def hidden(self, layer, seq):
+        """A stand-in hidden state of `layer` after processing `seq` (exact in fp64)."""
+        return float(sum((j + 1) * int(t) for j, t in enumerate(seq)) % 65521 + 100000 * layer)
+
 
 @pytest.mark.parametrize("p_right", [0.0, 0.6, 0.95, 1.0])
 def test_loop_reproduces_target_greedy_path(p_right):
@@ -182,10 +232,18 @@ def test_loop_reproduces_target_greedy_path(p_right):
         verify_in = [anchor] + cands
         t = [tgt_model.next(seq + verify_in[: i + 1]) for i in range(K + 1)]
         A, nxt = oracle.accept_prefix(np.array([cands]), np.array([t]))
+        # hidden states of two layers at every verify input (causal: input i
+        # sees the processed prefix and verify inputs 0..i)
+        vh = np.array([[[[tgt_model.hidden(l, seq + verify_in[: i + 1])]
+                         for i in range(K + 1)]] for l in range(2)], dtype=np.float64)
+        H = oracle.boundary_features(vh, A)
         A = int(A[0])
         before = len(seq)
         seq = seq + [anchor] + cands[:A]
         assert len(seq) - before == A + 1
+        # the next round is conditioned on the state after exactly the
+        # committed tokens (the cache cropped to n + A + 1)
+        assert [H[0, l, 0] for l in range(2)] == [tgt_model.hidden(l, seq) for l in range(2)]
         anchor = int(nxt[0])
         rounds += 1
     assert seq == ref[: len(seq)]
