@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(PKG, "libdlite.so")
 DLITE_F32, DLITE_BF16 = 0, 1
 ERRORS = {-1: "DLITE_ERR_NULL", -2: "DLITE_ERR_SHAPE", -3: "DLITE_ERR_DTYPE",
           -4: "DLITE_ERR_WORKSPACE", -5: "DLITE_ERR_UNSUPPORTED", -6: "DLITE_ERR_HIP"}
-EXPORTS = ["dlite_workspace_bytes", "dlite_draft_block", "dlite_accept_prefix",
-           "dlite_set_stage_events", "dlite_last_error", "dlite_version"]
+EXPORTS = ["dlite_workspace_bytes", "dlite_draft_block", "dlite_draft_block_at",
+           "dlite_accept_prefix", "dlite_set_stage_events", "dlite_last_error", "dlite_version"]
 STAGES = ["features", "qkv", "attention", "oproj", "gate_up", "down", "final_norm",
           "seq_proj", "scan", "lm_head"]
 
@@ -68,6 +68,10 @@ def load_library(path: str = LIB_PATH):
                                       c_void_p, c_void_p, c_void_p, POINTER(DliteTaps),
                                       c_void_p, c_size_t, c_void_p]
     lib.dlite_draft_block.restype = c_int
+    lib.dlite_draft_block_at.argtypes = [POINTER(DliteDims), POINTER(DliteWeights), c_void_p,
+                                         c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         POINTER(DliteTaps), c_void_p, c_size_t, c_void_p]
+    lib.dlite_draft_block_at.restype = c_int
     lib.dlite_accept_prefix.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                         c_void_p, c_void_p]
     lib.dlite_accept_prefix.restype = c_int
@@ -148,6 +152,21 @@ def dlite_draft_block(dims, weights, features, anchor_ids, candidates, max_logit
         ctypes.byref(dims), ctypes.byref(weights), _ptr(features), _ptr(anchor_ids),
         _ptr(candidates), _ptr(max_logit), ctypes.byref(taps) if taps is not None else None,
         _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc)
+
+
+def dlite_draft_block_at(dims, weights, verify_hidden, T, accept_len, anchor_ids, candidates,
+                         max_logit=None, taps=None, workspace=None, workspace_bytes=None,
+                         stream=None):
+    """Enqueue a draft step fed from the verify pass at index A; see include/dlite.h."""
+    ws_bytes = workspace_bytes
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load_library().dlite_draft_block_at(
+        ctypes.byref(dims), ctypes.byref(weights), _ptr(verify_hidden), T, _ptr(accept_len),
+        _ptr(anchor_ids), _ptr(candidates), _ptr(max_logit),
+        ctypes.byref(taps) if taps is not None else None, _ptr(workspace), ws_bytes,
+        _stream(stream))
     _check(rc)
 
 

@@ -201,38 +201,18 @@ int check_ptr(const void* p, const char* name) {
 
 const char* at(const void* base, size_t bytes) { return static_cast<const char*>(base) + bytes; }
 
-}  // namespace
+struct FeatureSource {
+  const void* H;
+  long sb, sl, st;          // element strides: request, layer slot, position
+  const int32_t* pos;       // [B] positions or null
+  int T;                    // positions per request
+};
 
-extern "C" {
-
-const char* dlite_last_error(void) { return g_err.c_str(); }
-
-int dlite_set_stage_events(int stage, hipEvent_t before, hipEvent_t after) {
-  if (!before && !after) {
-    g_ev = StageEvents{};
-    return ok();
-  }
-  if (!before || !after) return fail(DLITE_ERR_NULL, "both events are needed");
-  if (stage < 0 || stage >= DLITE_NUM_STAGES) return fail(DLITE_ERR_SHAPE, "unknown stage %d", stage);
-  g_ev.stage = stage;
-  g_ev.before = before;
-  g_ev.after = after;
-  return ok();
-}
-
-const char* dlite_version(void) { return "dlite-mi355x 0.1 (gfx950)"; }
-
-size_t dlite_workspace_bytes(const dlite_dims* dims) {
-  if (check_dims(dims) != DLITE_OK) return 0;
-  ok();
-  return make_plan(*dims).total;
-}
-
-int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void* features,
-                      const int32_t* anchor_ids, int32_t* candidates, float* max_logit,
-                      const dlite_taps* taps, void* workspace, size_t workspace_bytes,
-                      hipStream_t st) {
-  DLITE_TRY(check_dims(dims));
+// The draft step with the boundary features read through `fs` (both entry
+// points; dims and the feature pointer are checked by the caller).
+int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSource& fs,
+               const int32_t* anchor_ids, int32_t* candidates, float* max_logit,
+               const dlite_taps* taps, void* workspace, size_t workspace_bytes, hipStream_t st) {
   const dlite_dims& d = *dims;
   if (!w) return fail(DLITE_ERR_NULL, "weights is NULL");
   DLITE_TRY(check_ptr(w->depth_emb, "weights.depth_emb"));
@@ -253,7 +233,6 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
     DLITE_TRY(check_ptr(lw.w_gate_up, "layer.w_gate_up"));
     DLITE_TRY(check_ptr(lw.w_down, "layer.w_down"));
   }
-  DLITE_TRY(check_ptr(features, "features"));
   if (!anchor_ids) return fail(DLITE_ERR_NULL, "anchor_ids is NULL");
   if (!candidates) return fail(DLITE_ERR_NULL, "candidates is NULL");
   if (!workspace) return fail(DLITE_ERR_NULL, "workspace is NULL");
@@ -296,7 +275,8 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   // 1. feature slots, anchor and placeholder rows, first GEMM inputs
   //    (also clears the counters)
   FeatureArgs fa{};
-  fa.H = features; fa.depth_emb = w->depth_emb; fa.feat_norm = w->feat_norm;
+  fa.H = fs.H; fa.h_sb = fs.sb; fa.h_sl = fs.sl; fa.h_st = fs.st; fa.h_pos = fs.pos; fa.h_T = fs.T;
+  fa.depth_emb = w->depth_emb; fa.feat_norm = w->feat_norm;
   fa.tok_emb = w->tok_emb; fa.ph_emb = w->ph_emb;
   for (int l = 0; l < d.n_layers; ++l) fa.attn_norm[l] = w->layers[l].attn_norm;
   fa.anchors = anchor_ids; fa.X = X; fa.XB = XB; fa.ssq = SSQ; fa.tap_z = tp.z;
@@ -400,7 +380,7 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   la.W = w->lm_head; la.src = Sb; la.V = d.vocab; la.r = r; la.M = B * K; la.tok0 = 0;
   la.part_max = pmax; la.part_idx = pidx; la.G = p.G;
   la.cand = candidates; la.max_logit = max_logit; la.tap = tp.logits;
-  la.anchors = anchor_ids; la.K = K; la.counters = counters; la.part = TPs;
+  la.anchors = anchor_ids; la.pos = fs.pos; la.pos_n = fs.T; la.K = K; la.counters = counters; la.part = TPs;
   la.xcd_counters = counters + counter_lm_xcd();
   if (seqhead_fused(B, K, r, bf16)) {
     DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
@@ -417,6 +397,59 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
     DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, false, st));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dlite_last_error(void) { return g_err.c_str(); }
+
+int dlite_set_stage_events(int stage, hipEvent_t before, hipEvent_t after) {
+  if (!before && !after) {
+    g_ev = StageEvents{};
+    return ok();
+  }
+  if (!before || !after) return fail(DLITE_ERR_NULL, "both events are needed");
+  if (stage < 0 || stage >= DLITE_NUM_STAGES) return fail(DLITE_ERR_SHAPE, "unknown stage %d", stage);
+  g_ev.stage = stage;
+  g_ev.before = before;
+  g_ev.after = after;
+  return ok();
+}
+
+const char* dlite_version(void) { return "dlite-mi355x 0.1 (gfx950)"; }
+
+size_t dlite_workspace_bytes(const dlite_dims* dims) {
+  if (check_dims(dims) != DLITE_OK) return 0;
+  ok();
+  return make_plan(*dims).total;
+}
+
+int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void* features,
+                      const int32_t* anchor_ids, int32_t* candidates, float* max_logit,
+                      const dlite_taps* taps, void* workspace, size_t workspace_bytes,
+                      hipStream_t st) {
+  DLITE_TRY(check_dims(dims));
+  DLITE_TRY(check_ptr(features, "features"));
+  const long D = dims->D;
+  const FeatureSource fs{features, static_cast<long>(dims->m) * D, D, 0, nullptr, 1};
+  return draft_impl(dims, w, fs, anchor_ids, candidates, max_logit, taps, workspace, workspace_bytes, st);
+}
+
+int dlite_draft_block_at(const dlite_dims* dims, const dlite_weights* w, const void* verify_hidden,
+                         int32_t T, const int32_t* accept_len, const int32_t* anchor_ids,
+                         int32_t* candidates, float* max_logit, const dlite_taps* taps,
+                         void* workspace, size_t workspace_bytes, hipStream_t st) {
+  DLITE_TRY(check_dims(dims));
+  DLITE_TRY(check_ptr(verify_hidden, "verify_hidden"));
+  if (!accept_len) return fail(DLITE_ERR_NULL, "accept_len is NULL");
+  if (T < 1 || T > 65) return fail(DLITE_ERR_SHAPE, "T=%d not in [1, 65]", T);
+  const long D = dims->D;
+  // [m, B, T, D]: layer l of request b at verify index A_b
+  const FeatureSource fs{verify_hidden, static_cast<long>(T) * D, static_cast<long>(dims->B) * T * D, D,
+                         accept_len, T};
+  return draft_impl(dims, w, fs, anchor_ids, candidates, max_logit, taps, workspace, workspace_bytes, st);
 }
 
 int dlite_accept_prefix(const int32_t* candidates, const int32_t* target_tokens, int32_t B,

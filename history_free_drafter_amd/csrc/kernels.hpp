@@ -31,7 +31,13 @@ constexpr int kMaxLayers = 16;
 
 // ------------------------------------------------------------ feature build --
 struct FeatureArgs {
-  const void* H;          // [B, m, D] storage type
+  // context row (b, l) = H + b h_sb + l h_sl + pos_b h_st elements, with
+  // pos_b = h_pos[b] when h_pos is given (rows outside [0, h_T) read position
+  // 0; their requests are reported as invalid by the argmax), else 0
+  const void* H;
+  long h_sb, h_sl, h_st;
+  const int32_t* h_pos;
+  int h_T;
   const void* depth_emb;  // [m, D]
   const void* feat_norm;  // [D]
   const void* tok_emb;    // [V, D]
@@ -168,6 +174,8 @@ struct LmArgs {
   float* max_logit;      // [T] or null
   float* tap;            // [T, V] or null
   const int32_t* anchors; // [B]: requests with an out-of-range anchor get -1
+  const int32_t* pos;    // [B] or null: feature positions; outside [0, pos_n) also gives -1
+  int pos_n;
   int K;                 // tokens per request (token t belongs to request t / K)
   unsigned* counters;
   unsigned* xcd_counters; // counter_lm_xcd() words: arrivals per XCD (64-byte apart)

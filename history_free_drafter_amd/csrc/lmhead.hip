@@ -31,7 +31,11 @@ __device__ __forceinline__ void finish_token(const LmArgs& a, int tok, int lane,
   if (lane == 0) {
     const int gt = a.tok0 + tok;
     const int anchor = a.anchors[gt / a.K];
-    const bool ok = anchor >= 0 && anchor < a.V;
+    bool ok = anchor >= 0 && anchor < a.V;
+    if (a.pos) {
+      const int pb = a.pos[gt / a.K];
+      ok = ok && pb >= 0 && pb < a.pos_n;
+    }
     a.cand[gt] = ok ? i : -1;
     if (a.max_logit) a.max_logit[gt] = ok ? v : 0.f;
   }

@@ -62,7 +62,13 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
   const T* src;
   const T* add = nullptr;
   if (s < a.m) {
-    src = static_cast<const T*>(a.H) + (static_cast<long>(b) * a.m + s) * a.D;
+    int pos = 0;
+    if (a.h_pos) {
+      const int pb = a.h_pos[b];
+      pos = (pb >= 0 && pb < a.h_T) ? pb : 0;
+    }
+    src = static_cast<const T*>(a.H) + static_cast<long>(b) * a.h_sb + static_cast<long>(s) * a.h_sl +
+          static_cast<long>(pos) * a.h_st;
     add = static_cast<const T*>(a.depth_emb) + static_cast<long>(s) * a.D;
   } else if (s == a.m) {
     const int tok = a.anchors[b];

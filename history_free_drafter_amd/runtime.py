@@ -50,6 +50,14 @@ class DraftModel:
                              self.workspace, self.ws_bytes, stream)
         return self.candidates
 
+    def draft_at(self, verify_hidden: torch.Tensor, accept_len: torch.Tensor,
+                 anchors: torch.Tensor, taps=None, stream=None):
+        """Draft from the previous verify pass: verify_hidden [m, B, T, D] at index accept_len."""
+        _b.dlite_draft_block_at(self.dims, self.wstruct, verify_hidden, int(verify_hidden.shape[2]),
+                                accept_len, anchors, self.candidates, self.max_logit, taps,
+                                self.workspace, self.ws_bytes, stream)
+        return self.candidates
+
     def accept(self, target_tokens: torch.Tensor, stream=None):
         B, K = self.shape["B"], self.shape["K"]
         _b.dlite_accept_prefix(self.candidates, target_tokens, B, K, self.accept_len,

@@ -1,12 +1,14 @@
 /*
  * dlite.h — C ABI of the DLite draft step on AMD Instinct MI355X (gfx950).
  *
- * Two operations, following the statement of the problem on the DLite pages:
+ * The operations, following the statement of the problem on the DLite pages:
  *
  *   dlite_draft_block   boundary features [B, m, D] + anchor ids [B] + drafter
  *                       weights  ->  K greedy candidates per request [B, K].
  *   dlite_accept_prefix candidates [B, K] + target greedy tokens [B, K + 1]
  *                       ->  accepted prefix length A [B] and next anchor [B].
+ *   dlite_draft_block_at the next round's draft step with its features read
+ *                       from the verify pass's hidden states at index A.
  *
  * Sources (page title and section; no code is printed on them):
  *   [W] "DLite 完全拆解" walkthrough (pinghaoyang.com.cn);
@@ -160,6 +162,35 @@ int dlite_draft_block(const dlite_dims *dims, const dlite_weights *weights,
                       int32_t *candidates, float *max_logit,
                       const dlite_taps *taps, void *workspace,
                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dlite_draft_block_at — the draft step of the next round, fed straight from
+ * the previous round's verify pass (no host round trip between rounds).
+ *
+ * [W] "一轮执行后，缓存、锚点与隐藏状态怎样对齐", step 5 and the state-relation
+ * pseudo-code: the next round's boundary features are the m selected target
+ * layers' hidden states at verify index A_b of the input [a, d_1..d_K] (the
+ * last input that stays: index 0 is the anchor when nothing passed), and the
+ * next anchor is the target token there.  Identical to dlite_draft_block with
+ *   features[b, l, :] = verify_hidden[l, b, accept_len[b], :]
+ * (the same kernels; the feature build reads the rows in place).
+ *
+ * verify_hidden [m, B, T, D] (dtype)  per selected layer, that layer's hidden
+ *                                    states at the T verify inputs of every
+ *                                    request (one [B, T, D] block per layer)
+ * T             verify inputs per request (the previous round's K + 1), 1..65
+ * accept_len    [B] int32, device: A of the previous round (dlite_accept_prefix
+ *               output).  A value outside [0, T) cannot be checked before the
+ *               launch; the kernels then read position 0 (in bounds) and the
+ *               request's candidates are -1 and max_logit 0.
+ * anchor_ids    [B] int32: the next anchors (dlite_accept_prefix's next_anchor)
+ * All other arguments, the workspace and the errors are as dlite_draft_block.
+ */
+int dlite_draft_block_at(const dlite_dims *dims, const dlite_weights *weights,
+                         const void *verify_hidden, int32_t T, const int32_t *accept_len,
+                         const int32_t *anchor_ids, int32_t *candidates, float *max_logit,
+                         const dlite_taps *taps, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /*
  * dlite_accept_prefix — greedy verification of one round.

@@ -133,7 +133,7 @@ def _store(a32: np.ndarray, dtype: str) -> np.ndarray:
 # ------------------------------------------------------------------ draws ---
 
 def _streams(w: Workload) -> Dict[str, np.random.SeedSequence]:
-    names = ["weights", "features", "anchors", "match", "tokens", "tok_emb"]
+    names = ["weights", "features", "anchors", "match", "tokens", "tok_emb", "verify"]
     kids = np.random.SeedSequence(w.seed).spawn(len(names))
     return dict(zip(names, kids))
 
@@ -226,6 +226,25 @@ def make_features(w: Workload) -> np.ndarray:
     if w.feat_scale_step:
         h *= (1.0 + w.feat_scale_step * np.arange(w.m, dtype=np.float32))[None, :, None]
     return _store(h, w.dtype)
+
+
+def make_verify_hidden(w: Workload, T: int):
+    """Hidden states of the m selected target layers at T verify inputs.
+
+    Returns (verify_hidden [m, B, T, D] stored like the features, A [B]):
+    N(0,1) rows with the features' per-slot scaling, and accept lengths that
+    take 0 and T - 1 at the first two requests and are uniform on [0, T)
+    elsewhere.
+    """
+    rng = np.random.Generator(np.random.PCG64(_streams(w)["verify"]))
+    h = rng.standard_normal((w.m, w.B, T, w.D), dtype=np.float32)
+    if w.feat_scale_step:
+        h *= (1.0 + w.feat_scale_step * np.arange(w.m, dtype=np.float32))[:, None, None, None]
+    A = rng.integers(0, T, size=w.B).astype(np.int32)
+    A[0] = 0
+    if w.B > 1:
+        A[1] = T - 1
+    return _store(h, w.dtype), A
 
 
 def make_anchors(w: Workload) -> np.ndarray:

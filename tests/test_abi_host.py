@@ -101,6 +101,27 @@ def test_draft_block_validation_codes():
     assert call(ctypes.byref(bad), ctypes.byref(w), fake, fake, fake, fake, need) == -2
 
 
+def test_draft_block_at_validation_codes():
+    lib = B.load_library()
+    wl = WORKLOADS["tiny_f32"]
+    d = _dims(wl)
+    need = B.dlite_workspace_bytes(d)
+    w, keep = _fake_weights(wl.n_layers)
+    fake = 0x200000
+    call = lambda dims, vh, T, A, ws, nbytes: lib.dlite_draft_block_at(
+        dims, ctypes.byref(w), vh, T, A, fake, fake, None, None, ws, nbytes, None)
+    assert call(None, fake, 8, fake, fake, need) == -1
+    assert call(ctypes.byref(d), None, 8, fake, fake, need) == -1
+    assert call(ctypes.byref(d), fake, 8, None, fake, need) == -1
+    assert call(ctypes.byref(d), fake, 0, fake, fake, need) == -2
+    assert call(ctypes.byref(d), fake, 66, fake, fake, need) == -2
+    assert call(ctypes.byref(d), fake + 8, 8, fake, fake, need) == -5
+    assert call(ctypes.byref(d), fake, 8, fake, fake, need - 1) == -4
+    assert call(ctypes.byref(_dims(wl, K=0)), fake, 8, fake, fake, need) == -2
+    assert lib.dlite_draft_block_at(ctypes.byref(d), ctypes.byref(w), fake, 8, fake, None, fake,
+                                    None, None, fake, need, None) == -1
+
+
 def test_accept_validation_codes():
     lib = B.load_library()
     f = 0x300000

@@ -17,7 +17,7 @@ import oracle
 from history_free_drafter_amd import binding as B
 from history_free_drafter_amd.runtime import DraftModel, to_device
 from synth import (WORKLOADS, as_f64, custom, make_anchors, make_features,
-                   make_target_tokens, make_weights)
+                   make_target_tokens, make_verify_hidden, make_weights)
 from tests._util import f64_weights
 
 pytestmark = pytest.mark.gpu
@@ -213,6 +213,103 @@ def test_out_of_range_anchor_gives_minus_one():
     assert (gpu["cand"][1] == -1).all()
     good = ref["margin"][0] >= MARGIN[w.dtype]
     np.testing.assert_array_equal(gpu["cand"][0][good], ref["cand"][0][good])
+
+
+# ------------------------------------------ draft from the verify pass ---
+# dlite_draft_block_at reads the next round's features in place from the
+# verify pass's hidden states [m, B, T, D] at index A_b.
+
+
+def _run_gpu_at(w, weights, vh, A, anchors, taps=True, model=None):
+    dev = "cuda"
+    model = model or DraftModel(_dims_dict(w), weights, dev)
+    vd, Ad = to_device(vh, dev), torch.from_numpy(np.ascontiguousarray(A, dtype=np.int32)).to(dev)
+    ad = torch.from_numpy(anchors).to(dev)
+    tb = {}
+    if taps:
+        f = lambda *s: torch.full(s, float("nan"), dtype=torch.float32, device=dev)
+        tb = dict(z=f(w.B, w.m, w.D), x=f(w.n_layers, w.B, 1 + w.K, w.D),
+                  hidden=f(w.B, w.K, w.D), state=f(w.B, w.K, w.rank),
+                  logits=f(w.B, w.K, w.vocab))
+    model.draft_at(vd, Ad, ad, taps=B.make_taps(**tb) if taps else None)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in tb.items()}
+    out["cand"] = model.candidates.cpu().numpy()
+    out["max_logit"] = model.max_logit.cpu().numpy()
+    return out, model
+
+
+@pytest.mark.parametrize("key,T_extra", [("small_bf16", 0), ("small_f32", 0),
+                                         ("batch40_bf16", 0), ("k16_m64_bf16", 3)])
+def test_draft_from_verify_matches_oracle(key, T_extra):
+    _announce(f"draft_at {key}")
+    w, weights, _, a, _ = _prepared(key)
+    T = w.K + 1 + T_extra
+    vh, A = make_verify_hidden(w, T)
+    ref = _run_oracle(w, weights, oracle.boundary_features(vh, A), a)
+    gpu, _ = _run_gpu_at(w, weights, vh, A, a)
+    report, exempt = _compare(w, gpu, ref)
+    print(key, "A", A[:8].tolist(), report, f"exempt={exempt:.3f}", flush=True)
+    assert exempt < 0.5
+
+
+@pytest.mark.parametrize("key", ["batch40_bf16", "qwen3_8b_b1"])
+def test_draft_from_verify_is_the_draft_of_the_gathered_features(key):
+    """Bitwise: reading in place equals drafting from the gathered [B, m, D] copy."""
+    _announce(f"draft_at bitwise {key}")
+    w, weights, _, a, _ = _prepared(key)
+    T = w.K + 1
+    vh, A = make_verify_hidden(w, T)
+    model = DraftModel(_dims_dict(w), weights, "cuda")
+    at, _ = _run_gpu_at(w, weights, vh, A, a, taps=False, model=model)
+    # the gathered copy, made on the device (plain indexing, no library call)
+    vd = to_device(vh)
+    Hd = vd[:, torch.arange(w.B, device="cuda"), torch.from_numpy(A).long().cuda()]
+    Hd = Hd.permute(1, 0, 2).contiguous()
+    model.draft(Hd, torch.from_numpy(a).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(at["cand"], model.candidates.cpu().numpy())
+    np.testing.assert_array_equal(at["max_logit"], model.max_logit.cpu().numpy())
+
+
+def test_draft_from_verify_out_of_range_position_gives_minus_one():
+    _announce("draft_at bad positions batch40_bf16")
+    w, weights, _, a, _ = _prepared("batch40_bf16")
+    T = w.K + 1
+    vh, A = make_verify_hidden(w, T)
+    good, model = _run_gpu_at(w, weights, vh, A, a, taps=False)
+    bad = A.copy()
+    bad[3], bad[7] = T, -1
+    out, _ = _run_gpu_at(w, weights, vh, bad, a, taps=False, model=model)
+    assert (out["cand"][[3, 7]] == -1).all() and (out["max_logit"][[3, 7]] == 0).all()
+    keep = np.setdiff1d(np.arange(w.B), [3, 7])
+    np.testing.assert_array_equal(out["cand"][keep], good["cand"][keep])
+
+
+def test_accept_then_draft_from_verify_without_host_sync():
+    """One round trip on the device: accept gives A and the next anchor, the
+    next draft reads them in place; the result is the oracle's next round."""
+    _announce("accept -> draft_at small_bf16")
+    w, weights, H, a, ref = _prepared("small_bf16")
+    model = DraftModel(_dims_dict(w), weights, "cuda")
+    model.draft(to_device(H), torch.from_numpy(a).cuda())
+    t = make_target_tokens(w, ref["cand"])
+    T = w.K + 1
+    vh, _ = make_verify_hidden(w, T)
+    vd = to_device(vh)
+    A_d, next_d = model.accept(torch.from_numpy(t.astype(np.int32)).cuda())
+    model.draft_at(vd, A_d, next_d)            # no synchronisation in between
+    torch.cuda.synchronize()
+    gpu_c = model.candidates.cpu().numpy()
+    A_ref, next_ref = oracle.accept_prefix(ref["cand"], t)
+    ref2 = _run_oracle(w, weights, oracle.boundary_features(vh, A_ref), next_ref.astype(np.int32))
+    # requests whose first-round candidates were decided at clear margins
+    # (near-tie tokens may differ and then legitimately change A)
+    same = (ref["margin"] >= MARGIN[w.dtype]).all(axis=1)
+    assert same.any()
+    np.testing.assert_array_equal(A_d.cpu().numpy()[same], A_ref[same])
+    clear = (ref2["margin"] >= MARGIN[w.dtype]) & same[:, None]
+    np.testing.assert_array_equal(gpu_c[clear], ref2["cand"][clear])
 
 
 # ---------------------------------------------------------------- accept ---
