@@ -186,6 +186,59 @@ def lm_head_argmax(s: np.ndarray, lm_head: np.ndarray):
     return logits, tok.astype(np.int64), margin
 
 
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def gated_head(h: np.ndarray, anchor: int, head: dict, forced=None) -> dict:
+    """The walkthrough's own sequential head for one request, greedy.
+
+    [W] "官方顺序头具体算了什么": the previous token enters through an R-wide
+    embedding, d_0 = a, v_i = E_R(d_{i-1}); then
+        [g_i ; c_i] = W_s [s_{i-1} ; v_i] + b_s,   f_i = sigmoid(g_i),
+        s_i = f_i * s_{i-1} + (1 - f_i) * tanh(c_i),
+        r_i = W_h [s_i ; u_i] + b_h,               logits_i = W_o r_i,
+    and d_i is chosen from logits_i before position i + 1 ([W] "贪心模式与随机
+    模式要分别说明": the largest logit at temperature 0; ties to the lowest
+    index, as everywhere here).
+    READING: s_0 = 0 (the state starts at the block start, no warm-up token);
+    u_i = h_i, the final-normed backbone row of placeholder i; an anchor id
+    outside [0, V) reads a zero embedding row (its candidates are reported
+    as -1 by the caller).
+    h: [K, D]; head: emb [V, R], w_s [2R, 2R], b_s [2R], w_h [R, R + D],
+    b_h [R], w_o [V, R].  forced: optional [K] tokens fed back in place of
+    the chosen ones (to follow a run that chose differently at a near tie).
+    Returns s [K, R], r [K, R], logits [K, V], cand [K], margin [K].
+    """
+    K = h.shape[0]
+    emb, w_s, b_s = head["emb"], head["w_s"], head["b_s"]
+    w_h, b_h, w_o = head["w_h"], head["b_h"], head["w_o"]
+    R = emb.shape[1]
+    V = w_o.shape[0]
+    s = np.zeros(R)
+    out = dict(s=np.empty((K, R)), r=np.empty((K, R)), logits=np.empty((K, V)),
+               cand=np.empty(K, dtype=np.int64), margin=np.empty(K))
+    d_prev = int(anchor)
+    for i in range(K):
+        v = emb[d_prev] if 0 <= d_prev < emb.shape[0] else np.zeros(R)
+        gc = w_s @ np.concatenate([s, v]) + b_s
+        f = sigmoid(gc[:R])
+        s = f * s + (1.0 - f) * np.tanh(gc[R:])
+        r = w_h @ np.concatenate([s, h[i]]) + b_h
+        logits, tok, margin = lm_head_argmax(r, w_o)
+        out["s"][i], out["r"][i], out["logits"][i] = s, r, logits
+        out["cand"][i], out["margin"][i] = tok, margin
+        d_prev = int(tok) if forced is None else int(forced[i])
+    return out
+
+
+def gated_heads(h: np.ndarray, anchors: np.ndarray, head: dict, forced=None) -> dict:
+    """gated_head for every request: h [B, K, D], anchors [B] ids, forced [B, K] or None."""
+    runs = [gated_head(h[b], int(anchors[b]), head, None if forced is None else forced[b])
+            for b in range(h.shape[0])]
+    return {k: np.stack([o[k] for o in runs]) for k in runs[0]}
+
+
 # ------------------------------------------------------------------- step ---
 
 
