@@ -45,6 +45,9 @@ def parse():
                    help="time budget of the CPU oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stages", action="store_true", help="also time every stage separately")
+    p.add_argument("--head", choices=["fixed", "gated"], default="fixed",
+                   help="sequential head: the fixed token-free recurrence (one vocabulary "
+                        "pass) or the walkthrough's gated head (one vocabulary pass per position)")
     p.add_argument("--kernel", default=None,
                    help="stage whose roofline is reported (default: the one with the "
                         "largest algorithmic time at peak)")
@@ -56,9 +59,12 @@ def parse():
 
 # ------------------------------------------------------- algorithmic costs ---
 
-def stage_costs(w):
-    """Algorithmic HBM bytes and flops per stage (each weight read once; token
-    table: B rows; activations counted once in and once out)."""
+def stage_costs(w, head="fixed"):
+    """Algorithmic HBM bytes and flops per stage launch group (each weight read
+    once; token table: B rows; activations counted once in and once out).
+    With the gated head, "scan" and "lm_head" are one position's state update
+    and vocabulary pass (the stage events time the first position); the step
+    runs them K times (stage_reps)."""
     e = 2 if w.dtype == "bf16" else 4
     B, m, K, D, F, r, V = w.B, w.m, w.K, w.D, w.ffn, w.rank, w.vocab
     S, L = m + 1 + K, 1 + K
@@ -82,13 +88,25 @@ def stage_costs(w):
     c["seq_proj"] = [r * D * e + B * K * D * e + B * K * r * 4, 2.0 * B * K * D * r]
     c["scan"] = [2 * r * r * e + B * K * r * (4 + 4 + e), 4.0 * B * K * r * r]
     c["lm_head"] = [V * r * e + B * K * r * e + B * K * 8, 2.0 * B * K * r * V]
+    if head == "gated":
+        # W_h's backbone columns over all B K rows; per position: W_s and W_h's
+        # state columns, B rows of E_R, states in/out, r_i out; then W_o
+        c["seq_proj"] = [r * D * e + B * K * D * e + B * K * r * 4, 2.0 * B * K * D * r]
+        c["scan"] = [(4 * r * r + r * r + 3 * r) * e + B * r * (e + 4 + 4 + 4 + e),
+                     2.0 * B * (4 * r * r + r * r)]
+        c["lm_head"] = [V * r * e + B * r * e + B * 12, 2.0 * B * r * V]
     return c
 
 
-def step_costs(w):
-    c = stage_costs(w)
-    by = sum(v[0] for v in c.values()) + w.B * (w.K + (w.K + 1) + 2) * 4  # + accept
-    fl = sum(v[1] for v in c.values())
+def stage_reps(w, head="fixed"):
+    return {"scan": w.K, "lm_head": w.K} if head == "gated" else {}
+
+
+def step_costs(w, head="fixed"):
+    c = stage_costs(w, head)
+    reps = stage_reps(w, head)
+    by = sum(v[0] * reps.get(k, 1) for k, v in c.items()) + w.B * (w.K + (w.K + 1) + 2) * 4  # + accept
+    fl = sum(v[1] * reps.get(k, 1) for k, v in c.items())
     return by, fl
 
 
@@ -161,8 +179,9 @@ class HipEvents:
 
 # ------------------------------------------------------------- CPU baseline ---
 
-def cpu_baseline(w, weights, H, anchors, budget_s):
-    """The fp64 oracle timed on the host cores on a bounded sample."""
+def cpu_baseline(w, weights, H, anchors, budget_s, head=None):
+    """The fp64 oracle timed on the host cores on a bounded sample (with the
+    gated head's weights: the backbone, then the gated head)."""
     import oracle
     from synth import as_f64, make_target_tokens
     try:
@@ -173,10 +192,15 @@ def cpu_baseline(w, weights, H, anchors, budget_s):
     Wf = {k: as_f64(v) for k, v in weights.items() if k not in ("layers", "tok_emb")}
     Wf["layers"] = [{k: as_f64(v) for k, v in lw.items()} for lw in weights["layers"]]
     Hf, rows = as_f64(H), as_f64(weights["tok_emb"][anchors])
+    hf = None if head is None else {k: as_f64(v) for k, v in head.items()}
     ref, tgt = None, None
     n, t0 = 0, time.perf_counter()
     while True:
-        ref = oracle.draft_block(w, Wf, Hf, rows)
+        if hf is None:
+            ref = oracle.draft_block(w, Wf, Hf, rows)
+        else:
+            ref = oracle.draft_block(w, Wf, Hf, rows, with_head=False)
+            ref.update(oracle.gated_heads(ref["h"], anchors, hf))
         if tgt is None:
             tgt = make_target_tokens(w, ref["cand"])
         oracle.accept_prefix(ref["cand"], tgt)
@@ -186,8 +210,8 @@ def cpu_baseline(w, weights, H, anchors, budget_s):
             break
     value = n * w.B * w.K / el
     res = {"value": value, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-           "sample": f"{n} full draft+accept step(s) of {w.name} (B={w.B}), fp64 numpy, "
-                     f"{el:.1f} s"}
+           "sample": f"{n} full draft+accept step(s) of {w.name} (B={w.B}"
+                     f"{', gated head' if hf is not None else ''}), fp64 numpy, {el:.1f} s"}
     return res, ref, tgt
 
 
@@ -213,18 +237,20 @@ def main():
         return
     from history_free_drafter_amd import binding as B
     from history_free_drafter_amd.runtime import DraftModel, to_device
-    from synth import (WORKLOADS, make_anchors, make_features, make_target_tokens,
-                       make_weights)
+    from synth import (WORKLOADS, make_anchors, make_features, make_gated_head,
+                       make_target_tokens, make_weights)
 
     w = WORKLOADS[args.workload]
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     weights = make_weights(w)
     H, anchors = make_features(w), make_anchors(w)
+    gated = args.head == "gated"
+    head = make_gated_head(w) if gated else None
 
     cpu, ref, tgt = None, None, None
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
-        cpu, ref, tgt = cpu_baseline(w, weights, H, anchors, args.cpu_seconds)
+        cpu, ref, tgt = cpu_baseline(w, weights, H, anchors, args.cpu_seconds, head)
     else:
         rng = np.random.default_rng(0)
         tgt = make_target_tokens(w, rng.integers(0, w.vocab, size=(w.B, w.K)))
@@ -245,12 +271,21 @@ def main():
         s, k = B.make_weights(wc)
         copies.append(s)
         keep.append((wc, k))
+    heads = []
+    if gated:
+        model.set_gated_head(head)
+        del head
+        heads = [model.ghstruct]
+        for _ in range(max(0, args.copies - 1)):
+            hc = {k: v.clone() for k, v in model.gh.items()}
+            heads.append(B.make_gated_head(hc))
+            keep.append(hc)
     Hd = to_device(H, "cuda")
     ad = torch.from_numpy(anchors).cuda()
     td = torch.from_numpy(tgt).cuda()
     torch.cuda.synchronize()
 
-    costs = stage_costs(w)
+    costs = stage_costs(w, args.head)
     # dominant kernel: the stage with the largest algorithmic time at peak
     def t_roof(s):
         return max(costs[s][0] / HBM_PEAK, costs[s][1] / MFMA_BF16_PEAK)
@@ -260,7 +295,10 @@ def main():
     ev = HipEvents()
 
     def step(i):
-        model.draft(Hd, ad, weights=copies[i % len(copies)])
+        if gated:
+            model.draft_gated(Hd, ad, weights=copies[i % len(copies)], head=heads[i % len(heads)])
+        else:
+            model.draft(Hd, ad, weights=copies[i % len(copies)])
         model.accept(td)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -296,9 +334,9 @@ def main():
         achieved, peak, unit = costs[dom][0] / k_avg / 1e9, HBM_PEAK / 1e9, "GB/s"
     else:
         achieved, peak, unit = costs[dom][1] / k_avg / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
-    sb, sf = step_costs(w)
+    sb, sf = step_costs(w, args.head)
     step_s = wall_s / args.steps
-    traffic = traffic_record(w.name, dom)
+    traffic = traffic_record(w.name + ("+gated" if gated else ""), dom)
 
     stages = None
     if args.stages:
@@ -333,7 +371,8 @@ def main():
         "data": "synthetic (seeded N(0,1) features, N(0,0.02) weights)",
         "config": {"workload": w.name, "B": w.B, "m": w.m, "D": w.D, "n_layers": w.n_layers,
                    "heads": f"{w.n_q}q/{w.n_kv}kv x{w.d_h}", "ffn": w.ffn, "K": w.K,
-                   "rank": w.rank, "vocab": w.vocab, "weight_copies": len(copies),
+                   "rank": w.rank, "vocab": w.vocab, "head": args.head,
+                   "weight_copies": len(copies),
                    "parallelism": "single GPU"},
         "roofline": {"bound": bound, "kernel": dom, "achieved": round(achieved, 1),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
@@ -351,6 +390,8 @@ def main():
     }
     if ref is not None:
         clear = ref["margin"] >= 1e-2
+        if gated:   # a token differing at a near tie changes every later position
+            clear = np.cumprod(clear, axis=1).astype(bool)
         out["parity_tokens_clear_margin"] = float((cand == ref["cand"])[clear].mean()) if clear.any() else None
     if stages is not None:
         out["stages_us"] = stages

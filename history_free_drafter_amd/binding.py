@@ -18,6 +18,7 @@ DLITE_F32, DLITE_BF16 = 0, 1
 ERRORS = {-1: "DLITE_ERR_NULL", -2: "DLITE_ERR_SHAPE", -3: "DLITE_ERR_DTYPE",
           -4: "DLITE_ERR_WORKSPACE", -5: "DLITE_ERR_UNSUPPORTED", -6: "DLITE_ERR_HIP"}
 EXPORTS = ["dlite_workspace_bytes", "dlite_draft_block", "dlite_draft_block_at",
+           "dlite_draft_block_gated",
            "dlite_accept_prefix", "dlite_set_stage_events", "dlite_last_error", "dlite_version"]
 STAGES = ["features", "qkv", "attention", "oproj", "gate_up", "down", "final_norm",
           "seq_proj", "scan", "lm_head"]
@@ -39,6 +40,10 @@ class DliteWeights(Structure):
                 ("ph_emb", c_void_p), ("layers", POINTER(DliteLayerWeights)),
                 ("final_norm", c_void_p), ("seq_w_down", c_void_p), ("seq_w_up", c_void_p),
                 ("lm_head", c_void_p)]
+
+
+class DliteGatedHead(Structure):
+    _fields_ = [(n, c_void_p) for n in ("emb", "w_s", "b_s", "w_h", "b_h", "w_o")]
 
 
 class DliteTaps(Structure):
@@ -68,6 +73,11 @@ def load_library(path: str = LIB_PATH):
                                       c_void_p, c_void_p, c_void_p, POINTER(DliteTaps),
                                       c_void_p, c_size_t, c_void_p]
     lib.dlite_draft_block.restype = c_int
+    lib.dlite_draft_block_gated.argtypes = [POINTER(DliteDims), POINTER(DliteWeights),
+                                            POINTER(DliteGatedHead), c_void_p, c_void_p,
+                                            c_void_p, c_void_p, POINTER(DliteTaps), c_void_p,
+                                            c_size_t, c_void_p]
+    lib.dlite_draft_block_gated.restype = c_int
     lib.dlite_draft_block_at.argtypes = [POINTER(DliteDims), POINTER(DliteWeights), c_void_p,
                                          c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                          POINTER(DliteTaps), c_void_p, c_size_t, c_void_p]
@@ -152,6 +162,26 @@ def dlite_draft_block(dims, weights, features, anchor_ids, candidates, max_logit
         ctypes.byref(dims), ctypes.byref(weights), _ptr(features), _ptr(anchor_ids),
         _ptr(candidates), _ptr(max_logit), ctypes.byref(taps) if taps is not None else None,
         _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc)
+
+
+def make_gated_head(h: dict):
+    """dlite_gated_head from a dict of device tensors (keys as in include/dlite.h)."""
+    return DliteGatedHead(*[_ptr(h[k]) for k in ("emb", "w_s", "b_s", "w_h", "b_h", "w_o")])
+
+
+def dlite_draft_block_gated(dims, weights, head, features, anchor_ids, candidates,
+                            max_logit=None, taps=None, workspace=None, workspace_bytes=None,
+                            stream=None):
+    """Enqueue a draft step with the gated sequential head; see include/dlite.h."""
+    ws_bytes = workspace_bytes
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load_library().dlite_draft_block_gated(
+        ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(head) if head is not None else None,
+        _ptr(features), _ptr(anchor_ids), _ptr(candidates), _ptr(max_logit),
+        ctypes.byref(taps) if taps is not None else None, _ptr(workspace), ws_bytes,
+        _stream(stream))
     _check(rc)
 
 

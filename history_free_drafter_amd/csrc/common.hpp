@@ -120,7 +120,7 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 // tokens come in groups of g consecutive rows starting at `off` inside blocks
 // of `stride` rows.
 struct RowMap {
-  int g, stride, off;
+  int g = 1, stride = 1, off = 0;   // default: the identity
   __device__ __forceinline__ long row(int r) const {
     return static_cast<long>(r / g) * stride + off + (r % g);
   }

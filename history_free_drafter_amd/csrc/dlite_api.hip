@@ -47,7 +47,7 @@ size_t esize(const dlite_dims& d) { return d.dtype == DLITE_BF16 ? 2 : 4; }
 
 // Workspace regions, each 256-byte aligned.
 struct Plan {
-  size_t counters, X, XB, XF, SSQ, Q, KV, AO, ACT, P, U, Sf, Sb, pmax, pidx, TP, SP, total;
+  size_t counters, X, XB, XF, SSQ, Q, KV, AO, ACT, P, U, Sf, Sb, GR, GT, pmax, pidx, TP, SP, total;
   int G;
 };
 
@@ -130,6 +130,8 @@ Plan make_plan(const dlite_dims& d) {
   p.U = take(scan_scratch_floats(d.B, d.rank) * 4);
   p.Sf = take(B * K * r * 4);
   p.Sb = take(B * K * r * es);
+  p.GR = take(B * r * es);        // gated head: r_i of the current step
+  p.GT = take(B * 4);             // gated head: d_i of the current step
   p.pmax = take(B * K * Gmax * 4);
   p.pidx = take(B * K * Gmax * 4);
   p.TP = take(tile_scratch_bytes(d));
@@ -211,8 +213,9 @@ struct FeatureSource {
 // The draft step with the boundary features read through `fs` (both entry
 // points; dims and the feature pointer are checked by the caller).
 int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSource& fs,
-               const int32_t* anchor_ids, int32_t* candidates, float* max_logit,
-               const dlite_taps* taps, void* workspace, size_t workspace_bytes, hipStream_t st) {
+               const dlite_gated_head* gh, const int32_t* anchor_ids, int32_t* candidates,
+               float* max_logit, const dlite_taps* taps, void* workspace, size_t workspace_bytes,
+               hipStream_t st) {
   const dlite_dims& d = *dims;
   if (!w) return fail(DLITE_ERR_NULL, "weights is NULL");
   DLITE_TRY(check_ptr(w->depth_emb, "weights.depth_emb"));
@@ -220,9 +223,21 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   DLITE_TRY(check_ptr(w->tok_emb, "weights.tok_emb"));
   DLITE_TRY(check_ptr(w->ph_emb, "weights.ph_emb"));
   DLITE_TRY(check_ptr(w->final_norm, "weights.final_norm"));
-  DLITE_TRY(check_ptr(w->seq_w_down, "weights.seq_w_down"));
-  DLITE_TRY(check_ptr(w->seq_w_up, "weights.seq_w_up"));
-  DLITE_TRY(check_ptr(w->lm_head, "weights.lm_head"));
+  if (gh) {
+    DLITE_TRY(check_ptr(gh->emb, "head.emb"));
+    DLITE_TRY(check_ptr(gh->w_s, "head.w_s"));
+    DLITE_TRY(check_ptr(gh->b_s, "head.b_s"));
+    DLITE_TRY(check_ptr(gh->w_h, "head.w_h"));
+    DLITE_TRY(check_ptr(gh->b_h, "head.b_h"));
+    DLITE_TRY(check_ptr(gh->w_o, "head.w_o"));
+    if (d.rank > kGatedMaxRank || d.rank % 8)
+      return fail(DLITE_ERR_UNSUPPORTED, "gated head: rank %d must be a multiple of 8 up to %d", d.rank,
+                  kGatedMaxRank);
+  } else {
+    DLITE_TRY(check_ptr(w->seq_w_down, "weights.seq_w_down"));
+    DLITE_TRY(check_ptr(w->seq_w_up, "weights.seq_w_up"));
+    DLITE_TRY(check_ptr(w->lm_head, "weights.lm_head"));
+  }
   if (!w->layers) return fail(DLITE_ERR_NULL, "weights.layers is NULL");
   for (int l = 0; l < d.n_layers; ++l) {
     const dlite_layer_weights& lw = w->layers[l];
@@ -364,7 +379,14 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   // 4. hidden part of the sequential head's input projection, all B*K rows at once
   const RowMap ph_rows{K, S, m + 1};
   GemmArgs ph{};
-  ph.W = w->seq_w_down; ph.ldw = static_cast<long>(D) + r; ph.N = r; ph.K = D;
+  // fixed head: W_down[:, :D] h (hidden columns first); gated head:
+  // W_h[:, R:] u (state columns first)
+  if (gh) {
+    ph.W = static_cast<const char*>(gh->w_h) + static_cast<size_t>(r) * es;
+  } else {
+    ph.W = w->seq_w_down;
+  }
+  ph.ldw = static_cast<long>(D) + r; ph.N = r; ph.K = D;
   ph.src = XB + d.n_layers * xb_layer; ph.ld_src = D; ph.smap = ph_rows; ph.M = B * K;
   ph.ssq = SSQ; ph.qmap = ph_rows; ph.ssq_group = S; ph.ssq_split = 0; ph.np_lo = local_parts;
   ph.np_hi = local_parts; ph.norm_len = D; ph.eps = d.rms_eps;
@@ -382,7 +404,35 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   la.cand = candidates; la.max_logit = max_logit; la.tap = tp.logits;
   la.anchors = anchor_ids; la.pos = fs.pos; la.pos_n = fs.T; la.K = K; la.counters = counters; la.part = TPs;
   la.xcd_counters = counters + counter_lm_xcd();
-  if (seqhead_fused(B, K, r, bf16)) {
+  if (gh) {
+    // the walkthrough's gated head: K dependent steps, each a state update,
+    // its output r_i and one vocabulary pass over the B requests whose greedy
+    // tokens feed the next step (stage events: the first step)
+    float* Sst = tp.state ? tp.state : Sf;
+    int32_t* GT = reinterpret_cast<int32_t*>(ws + p.GT);
+    for (int i = 0; i < K; ++i) {
+      GatedArgs ga{};
+      ga.emb = gh->emb; ga.w_s = gh->w_s; ga.b_s = gh->b_s; ga.w_h = gh->w_h; ga.b_h = gh->b_h;
+      ga.tok = i == 0 ? anchor_ids : GT;
+      ga.s_prev = i == 0 ? nullptr : Sst + static_cast<size_t>(i - 1) * r;
+      ga.s_out = Sst + static_cast<size_t>(i) * r;
+      ga.ld_s = static_cast<long>(K) * r;
+      ga.qh = P + static_cast<size_t>(i) * r;
+      ga.ld_q = static_cast<long>(K) * r;
+      ga.r_out = ws + p.GR;
+      ga.B = B; ga.R = r; ga.V = d.vocab; ga.D = D;
+      DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st, i));
+      DLITE_LAUNCH(launch_gated_step(ga, bf16, st));
+      DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st, i));
+      LmArgs lg = la;
+      lg.W = gh->w_o; lg.src = ws + p.GR; lg.M = B; lg.tok0 = 0;
+      lg.omap = RowMap{1, K, i};
+      lg.raw = GT;
+      DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, true, st, i));
+      DLITE_LAUNCH(launch_lmhead(lg, bf16, st));
+      DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, false, st, i));
+    }
+  } else if (seqhead_fused(B, K, r, bf16)) {
     DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
     DLITE_LAUNCH(launch_seqhead(sa, la, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st));
@@ -434,7 +484,21 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   DLITE_TRY(check_ptr(features, "features"));
   const long D = dims->D;
   const FeatureSource fs{features, static_cast<long>(dims->m) * D, D, 0, nullptr, 1};
-  return draft_impl(dims, w, fs, anchor_ids, candidates, max_logit, taps, workspace, workspace_bytes, st);
+  return draft_impl(dims, w, fs, nullptr, anchor_ids, candidates, max_logit, taps, workspace,
+                    workspace_bytes, st);
+}
+
+int dlite_draft_block_gated(const dlite_dims* dims, const dlite_weights* w, const dlite_gated_head* head,
+                            const void* features, const int32_t* anchor_ids, int32_t* candidates,
+                            float* max_logit, const dlite_taps* taps, void* workspace,
+                            size_t workspace_bytes, hipStream_t st) {
+  DLITE_TRY(check_dims(dims));
+  if (!head) return fail(DLITE_ERR_NULL, "head is NULL");
+  DLITE_TRY(check_ptr(features, "features"));
+  const long D = dims->D;
+  const FeatureSource fs{features, static_cast<long>(dims->m) * D, D, 0, nullptr, 1};
+  return draft_impl(dims, w, fs, head, anchor_ids, candidates, max_logit, taps, workspace,
+                    workspace_bytes, st);
 }
 
 int dlite_draft_block_at(const dlite_dims* dims, const dlite_weights* w, const void* verify_hidden,
@@ -449,7 +513,8 @@ int dlite_draft_block_at(const dlite_dims* dims, const dlite_weights* w, const v
   // [m, B, T, D]: layer l of request b at verify index A_b
   const FeatureSource fs{verify_hidden, static_cast<long>(T) * D, static_cast<long>(dims->B) * T * D, D,
                          accept_len, T};
-  return draft_impl(dims, w, fs, anchor_ids, candidates, max_logit, taps, workspace, workspace_bytes, st);
+  return draft_impl(dims, w, fs, nullptr, anchor_ids, candidates, max_logit, taps, workspace,
+                    workspace_bytes, st);
 }
 
 int dlite_accept_prefix(const int32_t* candidates, const int32_t* target_tokens, int32_t B,

@@ -176,6 +176,8 @@ struct LmArgs {
   const int32_t* anchors; // [B]: requests with an out-of-range anchor get -1
   const int32_t* pos;    // [B] or null: feature positions; outside [0, pos_n) also gives -1
   int pos_n;
+  RowMap omap;           // launch token -> row of cand / max_logit / tap (request = row / K)
+  int32_t* raw;          // [M] or null: the argmax of each launch token, before validity
   int K;                 // tokens per request (token t belongs to request t / K)
   unsigned* counters;
   unsigned* xcd_counters; // counter_lm_xcd() words: arrivals per XCD (64-byte apart)
@@ -189,6 +191,26 @@ int lmhead_groups(int V);
 constexpr int kFuseMaxHelpers = 1024;
 bool seqhead_fused(int B, int K, int r, bool bf16);
 hipError_t launch_seqhead(const ScanArgs& s, const LmArgs& l, hipStream_t st);
+
+// ------------------------------------------------- gated sequential head ----
+constexpr int kGatedMaxRank = 512;
+struct GatedArgs {
+  const void* emb;        // E_R [V, R]
+  const void* w_s;        // [2R, 2R]: rows g then c, columns state then embedding
+  const void* b_s;        // [2R]
+  const void* w_h;        // [R, R + D]: columns state then backbone row
+  const void* b_h;        // [R]
+  const int32_t* tok;     // [B] d_{i-1}; ids outside [0, V) read a zero row
+  const float* s_prev;    // row b at s_prev + b ld_s; null: s_0 = 0
+  float* s_out;           // row b at s_out + b ld_s
+  long ld_s;
+  const float* qh;        // W_h[:, R:] u_i: row b at qh + b ld_q
+  long ld_q;
+  void* r_out;            // [B, R] storage type
+  int B, R, V, D;
+};
+// One step: the state update, then r_i (two launches).
+hipError_t launch_gated_step(const GatedArgs& a, bool bf16, hipStream_t st);
 
 // --------------------------------------------------------------- accept ----
 hipError_t launch_accept(const int32_t* cand, const int32_t* tgt, int B, int K,

@@ -30,14 +30,17 @@ __device__ __forceinline__ void finish_token(const LmArgs& a, int tok, int lane,
   }
   if (lane == 0) {
     const int gt = a.tok0 + tok;
-    const int anchor = a.anchors[gt / a.K];
+    const long orow = a.omap.row(gt);
+    const int b = static_cast<int>(orow / a.K);
+    const int anchor = a.anchors[b];
     bool ok = anchor >= 0 && anchor < a.V;
     if (a.pos) {
-      const int pb = a.pos[gt / a.K];
+      const int pb = a.pos[b];
       ok = ok && pb >= 0 && pb < a.pos_n;
     }
-    a.cand[gt] = ok ? i : -1;
-    if (a.max_logit) a.max_logit[gt] = ok ? v : 0.f;
+    a.cand[orow] = ok ? i : -1;
+    if (a.max_logit) a.max_logit[orow] = ok ? v : 0.f;
+    if (a.raw) a.raw[gt] = i;
   }
 }
 
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_kernel(LmArgs a) {
         if (vr < r1 && tok < a.M) {
           const float v = acc[u][i];
           if (better(v, vr, bv[u], bi[u])) { bv[u] = v; bi[u] = vr; }
-          if (a.tap) a.tap[static_cast<long>(a.tok0 + tok) * a.V + vr] = v;
+          if (a.tap) a.tap[a.omap.row(a.tok0 + tok) * a.V + vr] = v;
         }
       }
     }
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_pipe_kernel(LmArgs a) {
       if (vr < r1 && tok_ok) {
         const float v = acc[i];
         if (better(v, vr, bv, bi)) { bv = v; bi = vr; }
-        if (a.tap) a.tap[static_cast<long>(a.tok0 + c16) * a.V + vr] = v;
+        if (a.tap) a.tap[a.omap.row(a.tok0 + c16) * a.V + vr] = v;
       }
     }
   };
@@ -591,7 +594,7 @@ hipError_t launch_lmhead(const LmArgs& a0, bool bf16, hipStream_t st) {
   GemmArgs g{};
   g.W = a0.W; g.ldw = a0.r; g.N = a0.V; g.K = a0.r;
   g.src = a0.src; g.ld_src = a0.r; g.smap = RowMap{1, 1, 0}; g.M = a0.M; g.tok0 = a0.tok0;
-  g.tap = a0.tap; g.ld_tap = a0.V; g.tmap = RowMap{1, 1, 0};
+  g.tap = a0.tap; g.ld_tap = a0.V; g.tmap = a0.omap;
   g.part_max = a0.part_max; g.part_idx = a0.part_idx; g.G_part = gemm_tile_groups(a0.V);
   if (gemm_tiled(g, bf16)) {
     hipError_t e = launch_gemm_tiled(&g, 1, EPI_ARGMAX, a0.part, st);

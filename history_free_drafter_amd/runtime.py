@@ -50,6 +50,19 @@ class DraftModel:
                              self.workspace, self.ws_bytes, stream)
         return self.candidates
 
+    def set_gated_head(self, head: dict):
+        """Upload the gated head's weights (storage-form arrays keyed as dlite_gated_head)."""
+        self.gh = {k: to_device(v, self.device) for k, v in head.items()}
+        self.ghstruct = _b.make_gated_head(self.gh)
+
+    def draft_gated(self, features: torch.Tensor, anchors: torch.Tensor, taps=None, stream=None,
+                    weights=None, head=None):
+        _b.dlite_draft_block_gated(self.dims, weights if weights is not None else self.wstruct,
+                                   head if head is not None else self.ghstruct, features, anchors,
+                                   self.candidates, self.max_logit, taps, self.workspace,
+                                   self.ws_bytes, stream)
+        return self.candidates
+
     def draft_at(self, verify_hidden: torch.Tensor, accept_len: torch.Tensor,
                  anchors: torch.Tensor, taps=None, stream=None):
         """Draft from the previous verify pass: verify_hidden [m, B, T, D] at index accept_len."""

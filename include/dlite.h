@@ -9,6 +9,8 @@
  *                       ->  accepted prefix length A [B] and next anchor [B].
  *   dlite_draft_block_at the next round's draft step with its features read
  *                       from the verify pass's hidden states at index A.
+ *   dlite_draft_block_gated the draft step with the pages' gated sequential
+ *                       head (token-fed state, one vocabulary pass per step).
  *
  * Sources (page title and section; no code is printed on them):
  *   [W] "DLite 完全拆解" walkthrough (pinghaoyang.com.cn);
@@ -108,6 +110,20 @@ typedef struct dlite_weights {
 } dlite_weights;
 
 /*
+ * Weights of the gated sequential head printed in [W] "官方顺序头具体算了什么"
+ * (R = dims.rank, storage type dims.dtype).  Used by dlite_draft_block_gated
+ * in place of seq_w_down / seq_w_up / lm_head.
+ */
+typedef struct dlite_gated_head {
+  const void *emb;  /* [V, R] embedding E_R of the previous token (d_0 = anchor)  */
+  const void *w_s;  /* [2R, 2R] W_s: rows g then c; columns s_{i-1} then v_i     */
+  const void *b_s;  /* [2R] b_s                                                 */
+  const void *w_h;  /* [R, R + D] W_h: columns s_i then u_i (the backbone row)   */
+  const void *b_h;  /* [R] b_h                                                  */
+  const void *w_o;  /* [V, R] W_o: vocabulary projection of r_i                  */
+} dlite_gated_head;
+
+/*
  * Optional fp32 copies of intermediate tensors, for checking.  Any member may
  * be NULL.  z, x, state and logits are predicated stores of the kernels that
  * run either way; hidden (which the fast path never forms in fp32: the final
@@ -162,6 +178,34 @@ int dlite_draft_block(const dlite_dims *dims, const dlite_weights *weights,
                       int32_t *candidates, float *max_logit,
                       const dlite_taps *taps, void *workspace,
                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dlite_draft_block_gated — the draft step with the walkthrough's own gated
+ * sequential head in place of the fixed recurrence.
+ *
+ * [W] "官方顺序头具体算了什么": with d_0 = anchor and s_0 = 0, for i = 1..K
+ *   v_i = E_R(d_{i-1}),  [g_i ; c_i] = W_s [s_{i-1} ; v_i] + b_s,
+ *   s_i = sigmoid(g_i) * s_{i-1} + (1 - sigmoid(g_i)) * tanh(c_i),
+ *   r_i = W_h [s_i ; u_i] + b_h,  logits_i = W_o r_i,
+ *   d_i = candidates[b, i-1] = argmax logits_i (lowest index on ties),
+ * where u_i is the final-normed backbone row of placeholder i (the same h_k
+ * the fixed head reads).  The backbone is the one of dlite_draft_block.  The
+ * K vocabulary passes are dependent (each choice feeds the next step).
+ *
+ * head        weights of the head (host struct, device tensors); weights'
+ *             seq_w_down / seq_w_up / lm_head are not read and may be NULL
+ * rank        a multiple of 8, at most 512 (else DLITE_ERR_UNSUPPORTED)
+ * taps        state: s_i; logits: logits_i; others as dlite_draft_block
+ * An out-of-range anchor id reads a zero row of E_R and of the token
+ * embedding; that request's candidates are -1.  All other arguments, the
+ * workspace (dlite_workspace_bytes covers both heads) and the errors are as
+ * dlite_draft_block.
+ */
+int dlite_draft_block_gated(const dlite_dims *dims, const dlite_weights *weights,
+                            const dlite_gated_head *head, const void *features,
+                            const int32_t *anchor_ids, int32_t *candidates, float *max_logit,
+                            const dlite_taps *taps, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /*
  * dlite_draft_block_at — the draft step of the next round, fed straight from

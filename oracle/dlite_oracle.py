@@ -242,7 +242,8 @@ def gated_heads(h: np.ndarray, anchors: np.ndarray, head: dict, forced=None) -> 
 # ------------------------------------------------------------------- step ---
 
 
-def draft_block(dims, weights: dict, H: np.ndarray, anchor_rows: np.ndarray) -> dict:
+def draft_block(dims, weights: dict, H: np.ndarray, anchor_rows: np.ndarray,
+                with_head: bool = True) -> dict:
     """The whole draft step for a batch: K greedy candidates per request.
 
     dims: object with B, m, D, n_layers, n_q, n_kv, d_h, K, rms_eps, rope_theta.
@@ -269,6 +270,8 @@ def draft_block(dims, weights: dict, H: np.ndarray, anchor_rows: np.ndarray) -> 
         x_layers.append(x.copy())
     # READING: a final RMSNorm before the head; only placeholder rows are drafted.
     h = rms_norm(x[:, 1:], weights["final_norm"], dims.rms_eps)
+    if not with_head:   # the backbone only (for another sequential head)
+        return dict(z=z, x_layers=x_layers, h=h)
     s = np.stack([sequential_head(h[b], weights["seq_w_down"], weights["seq_w_up"])
                   for b in range(B)])
     logits, cand, margin = lm_head_argmax(s, weights["lm_head"])

@@ -133,7 +133,7 @@ def _store(a32: np.ndarray, dtype: str) -> np.ndarray:
 # ------------------------------------------------------------------ draws ---
 
 def _streams(w: Workload) -> Dict[str, np.random.SeedSequence]:
-    names = ["weights", "features", "anchors", "match", "tokens", "tok_emb", "verify"]
+    names = ["weights", "features", "anchors", "match", "tokens", "tok_emb", "verify", "gated"]
     kids = np.random.SeedSequence(w.seed).spawn(len(names))
     return dict(zip(names, kids))
 
@@ -217,6 +217,27 @@ def make_weights(w: Workload, with_tok_table: bool = True) -> dict:
     if with_tok_table:
         out["tok_emb"] = tok_emb_table(w)
     return out
+
+
+def make_gated_head(w: Workload) -> dict:
+    """Weights of the gated sequential head (R = rank), storage form.
+
+    emb [V, R] ~ N(0, 1) (the previous token's R-wide embedding);
+    w_s [2R, 2R] (rows: g then c; columns: state then embedding), b_s [2R],
+    w_h [R, R + D] (columns: state then backbone row), b_h [R], w_o [V, R]:
+    ~ N(0, weight_std).
+    """
+    rng = np.random.Generator(np.random.PCG64(_streams(w)["gated"]))
+    s, R, D, V = w.weight_std, w.rank, w.D, w.vocab
+    st = lambda a: _store(a, w.dtype)
+    return {
+        "emb": st(_normal(rng, (V, R), 1.0)),
+        "w_s": st(_normal(rng, (2 * R, 2 * R), s)),
+        "b_s": st(_normal(rng, (2 * R,), s)),
+        "w_h": st(_normal(rng, (R, R + D), s)),
+        "b_h": st(_normal(rng, (R,), s)),
+        "w_o": st(_normal(rng, (V, R), s)),
+    }
 
 
 def make_features(w: Workload) -> np.ndarray:

@@ -122,6 +122,26 @@ def test_draft_block_at_validation_codes():
                                     None, None, fake, need, None) == -1
 
 
+def test_draft_block_gated_validation_codes():
+    lib = B.load_library()
+    wl = WORKLOADS["tiny_f32"]
+    d = _dims(wl)
+    need = B.dlite_workspace_bytes(d)
+    w, keep = _fake_weights(wl.n_layers)
+    fake = 0x200000
+    head = B.DliteGatedHead(*[fake] * 6)
+    call = lambda dims, hd, nbytes: lib.dlite_draft_block_gated(
+        dims, ctypes.byref(w), hd, fake, fake, fake, None, None, fake, nbytes, None)
+    assert call(ctypes.byref(d), None, need) == -1
+    assert call(ctypes.byref(d), ctypes.byref(B.DliteGatedHead(*[fake] * 5, None)), need) == -1
+    assert call(ctypes.byref(d), ctypes.byref(B.DliteGatedHead(fake + 4, *[fake] * 5)), need) == -5
+    assert call(ctypes.byref(d), ctypes.byref(head), need - 1) == -4
+    # the fixed head's weights are not needed by the gated head
+    nohead = B.DliteWeights(*[fake] * 4, w.layers, fake, None, None, None)
+    assert lib.dlite_draft_block_gated(ctypes.byref(d), ctypes.byref(nohead), ctypes.byref(head),
+                                       fake, fake, fake, None, None, fake, need - 1, None) == -4
+
+
 def test_accept_validation_codes():
     lib = B.load_library()
     f = 0x300000

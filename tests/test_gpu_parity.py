@@ -17,7 +17,7 @@ import oracle
 from history_free_drafter_amd import binding as B
 from history_free_drafter_amd.runtime import DraftModel, to_device
 from synth import (WORKLOADS, as_f64, custom, make_anchors, make_features,
-                   make_target_tokens, make_verify_hidden, make_weights)
+                   make_gated_head, make_target_tokens, make_verify_hidden, make_weights)
 from tests._util import f64_weights
 
 pytestmark = pytest.mark.gpu
@@ -213,6 +213,85 @@ def test_out_of_range_anchor_gives_minus_one():
     assert (gpu["cand"][1] == -1).all()
     good = ref["margin"][0] >= MARGIN[w.dtype]
     np.testing.assert_array_equal(gpu["cand"][0][good], ref["cand"][0][good])
+
+
+# ------------------------------------------------- gated sequential head ---
+# dlite_draft_block_gated: the walkthrough's own head.  Each step's token
+# feeds the next, so the oracle follows the GPU's tokens (teacher forcing):
+# every step's state and logits are then comparable, and each GPU token must
+# be the oracle's argmax wherever the oracle's margin is clear.
+
+
+def _run_gpu_gated(w, weights, head, H, anchors, model=None, taps=True):
+    dev = "cuda"
+    model = model or DraftModel(_dims_dict(w), weights, dev)
+    model.set_gated_head(head)
+    tb = {}
+    if taps:
+        f = lambda *s: torch.full(s, float("nan"), dtype=torch.float32, device=dev)
+        tb = dict(state=f(w.B, w.K, w.rank), logits=f(w.B, w.K, w.vocab))
+    model.draft_gated(to_device(H, dev), torch.from_numpy(anchors).to(dev),
+                      taps=B.make_taps(**tb) if taps else None)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in tb.items()}
+    out["cand"] = model.candidates.cpu().numpy()
+    out["max_logit"] = model.max_logit.cpu().numpy()
+    return out, model
+
+
+def _check_gated(w, gpu, h, anchors, head, rows=None):
+    rows = np.arange(w.B) if rows is None else np.asarray(rows)
+    hf = {k: as_f64(v) for k, v in head.items()}
+    ref = oracle.gated_heads(h[rows], anchors[rows], hf, forced=gpu["cand"][rows])
+    tol = TOL[w.dtype]
+    rep = dict(state=_rel(gpu["state"][rows], ref["s"]),
+               logits=_rel(gpu["logits"][rows], ref["logits"], axis=-1))
+    assert all(v <= tol for v in rep.values()), rep
+    clear = ref["margin"] >= MARGIN[w.dtype]
+    mism = (gpu["cand"][rows] != ref["cand"]) & clear
+    assert not mism.any(), f"{int(mism.sum())} token mismatches at clear margins"
+    Bi, Ki = np.meshgrid(np.arange(len(rows)), np.arange(w.K), indexing="ij")
+    np.testing.assert_array_equal(gpu["max_logit"][rows], gpu["logits"][rows][Bi, Ki, gpu["cand"][rows]])
+    return rep, float(1.0 - clear.mean())
+
+
+@pytest.mark.parametrize("key", ["small_bf16", "small_f32", "batch40_bf16", "k16_m64_bf16",
+                                 "rank512_bf16", "tiled_k64_bf16", "batch5_f32"])
+def test_gated_head_matches_oracle(key):
+    _announce(f"gated {key}")
+    w, weights, H, a, ref = _prepared(key)
+    head = make_gated_head(w)
+    gpu, _ = _run_gpu_gated(w, weights, head, H, a)
+    rep, exempt = _check_gated(w, gpu, ref["h"], a, head)
+    print(key, rep, f"exempt={exempt:.3f}", flush=True)
+    assert exempt < 0.5
+
+
+@pytest.mark.parametrize("key", ["qwen3_8b_b1", "qwen3_8b_b64_m36"])
+def test_gated_head_full_size_sampled(key):
+    """Full shapes; at 64 requests eight sampled requests are checked."""
+    _announce(f"gated full {key}")
+    w, weights, H, a, ref = _prepared(key)
+    head = make_gated_head(w)
+    gpu, _ = _run_gpu_gated(w, weights, head, H, a)
+    rows = np.arange(w.B) if w.B <= 8 else np.linspace(0, w.B - 1, 8).astype(int)
+    rep, exempt = _check_gated(w, gpu, ref["h"], a, head, rows)
+    print(key, rep, f"exempt={exempt:.3f}", flush=True)
+
+
+def test_gated_head_out_of_range_anchor_and_determinism():
+    _announce("gated bad anchor + repeat small_bf16")
+    w, weights, H, a, ref = _prepared("small_bf16")
+    head = make_gated_head(w)
+    g1, model = _run_gpu_gated(w, weights, head, H, a, taps=False)
+    g2, _ = _run_gpu_gated(w, weights, head, H, a, model=model, taps=False)
+    np.testing.assert_array_equal(g1["cand"], g2["cand"])
+    np.testing.assert_array_equal(g1["max_logit"], g2["max_logit"])
+    bad = a.copy()
+    bad[1] = w.vocab + 5
+    g3, _ = _run_gpu_gated(w, weights, head, H, bad, model=model, taps=False)
+    assert (g3["cand"][1] == -1).all() and (g3["max_logit"][1] == 0).all()
+    np.testing.assert_array_equal(g3["cand"][0], g1["cand"][0])
 
 
 # ------------------------------------------ draft from the verify pass ---
