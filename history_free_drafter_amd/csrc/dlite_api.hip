@@ -410,7 +410,26 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
     // tokens feed the next step (stage events: the first step)
     float* Sst = tp.state ? tp.state : Sf;
     int32_t* GT = reinterpret_cast<int32_t*>(ws + p.GT);
-    for (int i = 0; i < K; ++i) {
+    const bool fused = gatedhead_fused(B, K, r, bf16) &&
+                       gatedhead_exchange_bytes(B, r) <= scan_scratch_floats(B, r) * sizeof(float);
+    if (fused) {
+      // all K positions in one persistent launch, W_o held on chip
+      uint64_t* xw = reinterpret_cast<uint64_t*>(U);   // zeroed by the feature kernel
+      GatedFuseArgs gf{};
+      gf.emb = gh->emb; gf.w_s = gh->w_s; gf.b_s = gh->b_s; gf.w_h = gh->w_h; gf.b_h = gh->b_h;
+      gf.anchors = anchor_ids; gf.qh = P; gf.s_out = Sst;
+      gf.sx = xw; gf.rx = xw + static_cast<size_t>(B) * r; gf.dx = xw + static_cast<size_t>(B) * (r + r / 2);
+      gf.arrive = counters + counter_gated();
+      gf.la = la;
+      gf.la.W = gh->w_o; gf.la.M = B; gf.la.tok0 = 0;
+      gf.B = B; gf.K = K; gf.D = D;
+      DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
+      DLITE_LAUNCH(launch_gatedhead(gf, st));
+      DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st));
+      DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, true, st));
+      DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, false, st));
+    }
+    for (int i = 0; i < K && !fused; ++i) {
       GatedArgs ga{};
       ga.emb = gh->emb; ga.w_s = gh->w_s; ga.b_s = gh->b_s; ga.w_h = gh->w_h; ga.b_h = gh->b_h;
       ga.tok = i == 0 ? anchor_ids : GT;

@@ -21,7 +21,8 @@ size_t scan_scratch_floats(int B, int r);   // size of ScanArgs::U
 inline int counter_seq_done() { return 64; }
 inline int counter_gemm() { return counter_seq_done() + 64; }
 inline int counter_lm_xcd() { return counter_gemm() + 2 * 128; }   // [8 XCDs] x 16 words
-inline int counter_words() { return counter_lm_xcd() + 8 * 16; }
+inline int counter_gated() { return counter_lm_xcd() + 8 * 16; }
+inline int counter_words() { return counter_gated() + 8 * 16; }
 enum Status { STATUS_BARRIER_TIMEOUT = 1 };
 
 // Partial sums of squares per activation row: one slot per producing
@@ -211,6 +212,24 @@ struct GatedArgs {
 };
 // One step: the state update, then r_i (two launches).
 hipError_t launch_gated_step(const GatedArgs& a, bool bf16, hipStream_t st);
+
+// All K positions in one persistent launch for a few requests (bf16, R = 512,
+// B <= 8): W_o stays on chip across the positions.
+struct GatedFuseArgs {
+  const void* emb; const void* w_s; const void* b_s; const void* w_h; const void* b_h;
+  const int32_t* anchors;   // [B] d_0
+  const float* qh;          // [B K, R] W_h[:, R:] u
+  float* s_out;             // [B K, R] states
+  uint64_t* sx;             // [B, R]   tagged state words (team exchange)
+  uint64_t* rx;             // [B, R/2] tagged r_i words (two bf16 each)
+  uint64_t* dx;             // [B]      tagged d_i words
+  unsigned* arrive;         // 8 XCD arrival counters, 16 words apart (zero at launch)
+  LmArgs la;                // W = W_o; outputs, partials and counters
+  int B, K, D;
+};
+bool gatedhead_fused(int B, int K, int r, bool bf16);
+size_t gatedhead_exchange_bytes(int B, int r);
+hipError_t launch_gatedhead(const GatedFuseArgs& f, hipStream_t st);
 
 // --------------------------------------------------------------- accept ----
 hipError_t launch_accept(const int32_t* cand, const int32_t* tgt, int B, int K,

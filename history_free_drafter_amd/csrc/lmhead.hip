@@ -544,6 +544,376 @@ size_t seqhead_lds(int M, int r) {
   return static_cast<size_t>(TL) * RK * 1024 + static_cast<size_t>(M) * (r + kStatePad) * 2;
 }
 
+// --------------------------------------------- fused gated head (few requests) --
+//
+// The walkthrough's gated head ("官方顺序头具体算了什么") runs one vocabulary
+// pass per position, each over the same 155.6 MB W_o.  For a few requests
+// this launch keeps W_o on chip for all K positions instead of streaming it K
+// times: helper workgroup h owns a contiguous range of 16-row tiles and holds
+// TR of them per wave in registers and TL per workgroup in LDS for the whole
+// launch; only the remainder (touched into L2 before the first position) is
+// re-read at each position.  Sixteen team workgroups run the state updates.
+// Per position i (tag i + 1):
+//   team     d_{i-1} (the anchor at i = 0) -> v_i = E_R(d_{i-1});
+//            [g; c] = W_s [s_{i-1}; v_i] + b_s and the gate for its 32 state
+//            elements, published as tagged words; all R read back;
+//            r_i = W_h[:, :R] s_i + qh_i + b_h for its 32 elements, published
+//            as tagged words (two bf16 each);
+//   helpers  wait for every r_i word, multiply their tiles, publish
+//            (max, index) partials and count themselves in (one counter per
+//            XCD, never reset within the launch);
+//   team     member b < B waits for all arrivals of the position, reduces
+//            request b's partials in fixed order, writes its candidate and
+//            publishes d_i as a tagged word for the whole team.
+// A word is rewritten only for a later position, after all its readers have
+// passed the dependency that the later position needs, so tags alone order
+// everything.  The launch is cooperative (every workgroup resident: the team
+// and the helpers wait on each other); every wait is bounded and flags the
+// status word on time-out, so the kernel always drains.
+constexpr int kGTeam = 16;       // team workgroups (blocks 0 .. 15)
+constexpr int kGR = 512;         // state width of the fused path
+
+__device__ __forceinline__ float dot8(const uint4& w, const float* x) {
+  return __uint_as_float(w.x << 16) * x[0] + __uint_as_float(w.x & 0xffff0000u) * x[1] +
+         __uint_as_float(w.y << 16) * x[2] + __uint_as_float(w.y & 0xffff0000u) * x[3] +
+         __uint_as_float(w.z << 16) * x[4] + __uint_as_float(w.z & 0xffff0000u) * x[5] +
+         __uint_as_float(w.w << 16) * x[6] + __uint_as_float(w.w & 0xffff0000u) * x[7];
+}
+
+__device__ __forceinline__ uint64_t wait_tag(const uint64_t* p, unsigned tag, unsigned* status) {
+  uint64_t w = scan_detail::ld_tagged(p);
+  unsigned spins = 0;
+  while (static_cast<unsigned>(w >> 32) != tag) {
+    __builtin_amdgcn_s_sleep(2);
+    if (++spins > scan_detail::kSpinLimit) {
+      atomicOr(status, static_cast<unsigned>(STATUS_BARRIER_TIMEOUT));
+      break;
+    }
+    w = scan_detail::ld_tagged(p);
+  }
+  return w;
+}
+
+__device__ __forceinline__ void put_tag(uint64_t* p, uint32_t v, unsigned tag) {
+  __hip_atomic_store(p, static_cast<uint64_t>(v) | (static_cast<uint64_t>(tag) << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The argmax of request b at position i: wait until the helpers' arrival
+// counters (one per XCD) add up to G (i + 1), fold the G partials (each
+// thread a strided share in index order, then the waves in order: the same
+// result for any arrival order), write the candidate and publish d_i.
+__device__ __forceinline__ void gated_finish(const GatedFuseArgs& f, unsigned char* smem, int b, int i,
+                                             unsigned* status) {
+  const LmArgs& a = f.la;
+  const int G = a.G, K = f.K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* rv = reinterpret_cast<float*>(smem + static_cast<size_t>(f.B) * 3 * kGR * 4 + 64);   // after xs, ss, dsh
+  int* ri = reinterpret_cast<int*>(rv + kWaves);
+  if (threadIdx.x == 0) {
+    const unsigned want = static_cast<unsigned>(G) * static_cast<unsigned>(i + 1);
+    unsigned spins = 0;
+    for (;;) {
+      unsigned n = 0;
+      for (int q = 0; q < 8; ++q)
+        n += __hip_atomic_load(f.arrive + q * 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (n >= want) break;
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > scan_detail::kSpinLimit) {
+        atomicOr(status, static_cast<unsigned>(STATUS_BARRIER_TIMEOUT));
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  float v = -INFINITY;
+  int ix = 0x7fffffff;
+  for (int e = threadIdx.x; e < G; e += blockDim.x) {
+    const float pv = __hip_atomic_load(a.part_max + static_cast<long>(b) * G + e, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    const int pi = __hip_atomic_load(a.part_idx + static_cast<long>(b) * G + e, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    if (better(pv, pi, v, ix)) { v = pv; ix = pi; }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(ix, o, kWave);
+    if (better(ov, oi, v, ix)) { v = ov; ix = oi; }
+  }
+  if (lane == 0) { rv[wave] = v; ri[wave] = ix; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kWaves; ++w)
+      if (better(rv[w], ri[w], v, ix)) { v = rv[w]; ix = ri[w]; }
+    const int anchor = a.anchors[b];
+    bool ok = anchor >= 0 && anchor < a.V;
+    if (a.pos) ok = ok && a.pos[b] >= 0 && a.pos[b] < a.pos_n;
+    const long orow = static_cast<long>(b) * K + i;
+    a.cand[orow] = ok ? ix : -1;
+    if (a.max_logit) a.max_logit[orow] = ok ? v : 0.f;
+    put_tag(f.dx + b, static_cast<uint32_t>(ix), static_cast<unsigned>(i + 1));
+  }
+  __syncthreads();
+}
+
+// Team member m: state elements [32 m, 32 m + 32), wave w the four from
+// 32 m + 4 w; its rows of W_s (g and c) and W_h (state columns) stay in
+// registers, lane l holding columns 8 l .. 8 l + 7 of each half.
+__device__ __forceinline__ void gated_team(const GatedFuseArgs& f, unsigned char* smem, int m) {
+  constexpr int R = kGR, R2 = 2 * kGR;
+  const int B = f.B, K = f.K, V = f.la.V, D = f.D;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j0 = m * 32 + wave * 4;
+  unsigned* status = f.la.counters + CNT_STATUS;
+  const uint16_t* Ws = static_cast<const uint16_t*>(f.w_s);
+  const uint16_t* Wh = static_cast<const uint16_t*>(f.w_h);
+  const uint16_t* E = static_cast<const uint16_t*>(f.emb);
+  uint4 wg[4][2], wc[4][2], wh[4];
+  float bg[4], bc[4], bh[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint16_t* rg = Ws + static_cast<long>(j0 + q) * R2 + lane * 8;
+    const uint16_t* rc = Ws + static_cast<long>(R + j0 + q) * R2 + lane * 8;
+    wg[q][0] = *reinterpret_cast<const uint4*>(rg);
+    wg[q][1] = *reinterpret_cast<const uint4*>(rg + R);
+    wc[q][0] = *reinterpret_cast<const uint4*>(rc);
+    wc[q][1] = *reinterpret_cast<const uint4*>(rc + R);
+    wh[q] = *reinterpret_cast<const uint4*>(Wh + static_cast<long>(j0 + q) * (R + D) + lane * 8);
+    bg[q] = bf16_to_f32(static_cast<const uint16_t*>(f.b_s)[j0 + q]);
+    bc[q] = bf16_to_f32(static_cast<const uint16_t*>(f.b_s)[R + j0 + q]);
+    bh[q] = bf16_to_f32(static_cast<const uint16_t*>(f.b_h)[j0 + q]);
+  }
+  float* xs = reinterpret_cast<float*>(smem);      // [B][2R]: s_{i-1}, v_i
+  float* ss = xs + B * R2;                         // [B][R]:  s_i
+  int* dsh = reinterpret_cast<int*>(ss + B * R);   // [B]:     d_{i-1}
+  auto pick = [](const float (&v)[4], int q) { return q == 0 ? v[0] : q == 1 ? v[1] : q == 2 ? v[2] : v[3]; };
+
+  for (int i = 0; i < K; ++i) {
+    const unsigned tag = static_cast<unsigned>(i + 1);
+    if (static_cast<int>(threadIdx.x) < B)
+      dsh[threadIdx.x] = i == 0 ? f.anchors[threadIdx.x]
+                                : static_cast<int>(static_cast<uint32_t>(wait_tag(f.dx + threadIdx.x, tag - 1, status)));
+    __syncthreads();
+    for (int e = threadIdx.x; e < B * R; e += blockDim.x) {
+      const int b = e / R, k = e % R;
+      const int d = dsh[b];
+      xs[b * R2 + k] = i == 0 ? 0.f : ss[e];
+      xs[b * R2 + R + k] = (d >= 0 && d < V) ? bf16_to_f32(E[static_cast<long>(d) * R + k]) : 0.f;
+    }
+    __syncthreads();
+    // gate of this wave's four elements, every request
+    for (int b = 0; b < B; ++b) {
+      const float* x = xs + b * R2;
+      float x0[8], x1[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) { x0[t] = x[lane * 8 + t]; x1[t] = x[R + lane * 8 + t]; }
+      float dg[4], dc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        dg[q] = wave_sum(dot8(wg[q][0], x0) + dot8(wg[q][1], x1));
+        dc[q] = wave_sum(dot8(wc[q][0], x0) + dot8(wc[q][1], x1));
+      }
+      if (lane < 4) {
+        const int j = j0 + lane;
+        const float g = pick(dg, lane) + pick(bg, lane), c = pick(dc, lane) + pick(bc, lane);
+        const float fg = 1.0f / (1.0f + expf(-g));
+        const float sn = fg * x[j] + (1.0f - fg) * tanhf(c);
+        f.s_out[(static_cast<long>(b) * K + i) * R + j] = sn;
+        put_tag(f.sx + b * R + j, __float_as_uint(sn), tag);
+      }
+    }
+    // the whole s_i from the team's words
+    for (int e = threadIdx.x; e < B * R; e += blockDim.x)
+      ss[e] = __uint_as_float(static_cast<uint32_t>(wait_tag(f.sx + e, tag, status)));
+    __syncthreads();
+    // r_i of this wave's four elements, published in pairs
+    for (int b = 0; b < B; ++b) {
+      float s8[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) s8[t] = ss[b * R + lane * 8 + t];
+      float dr[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dr[q] = wave_sum(dot8(wh[q], s8));
+      if (lane < 2) {
+        const float* qrow = f.qh + (static_cast<long>(b) * K + i) * R + j0;
+        const float ra = pick(dr, 2 * lane) + qrow[2 * lane] + pick(bh, 2 * lane);
+        const float rb = pick(dr, 2 * lane + 1) + qrow[2 * lane + 1] + pick(bh, 2 * lane + 1);
+        const uint32_t pk = static_cast<uint32_t>(f32_to_bf16(ra)) | (static_cast<uint32_t>(f32_to_bf16(rb)) << 16);
+        put_tag(f.rx + b * (R / 2) + j0 / 2 + lane, pk, tag);
+      }
+    }
+    // member m < B: the argmax of request m once every helper has counted in
+    if (m < B) gated_finish(f, smem, m, i, status);
+  }
+}
+
+template <int RK>   // k-steps of 32 (R / 32)
+__global__ __launch_bounds__(kWaves * 64) void gatedhead_kernel(GatedFuseArgs f) {
+  constexpr int TR = kFuseRegs / (4 * RK);
+  constexpr int TL = kFuseLdsTiles / (RK * 1024);
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float sv[kWaves][16];
+  __shared__ int si[kWaves][16];
+
+  if (static_cast<int>(blockIdx.x) < kGTeam) {
+    gated_team(f, smem, static_cast<int>(blockIdx.x));
+    return;
+  }
+  const LmArgs& a = f.la;
+  unsigned* status = a.counters + CNT_STATUS;
+  const int h = static_cast<int>(blockIdx.x) - kGTeam;
+  const int G = static_cast<int>(gridDim.x) - kGTeam;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, grp = lane >> 4;
+  constexpr int r = RK * 32;
+  const int V = a.V, B = f.B, K = f.K;
+  const int NT = (V + 15) / 16;
+  const int t0 = static_cast<int>(static_cast<long>(h) * NT / G);
+  const int t1 = static_cast<int>(static_cast<long>(h + 1) * NT / G);
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  auto frag_ptr = [&](int t, int s) {
+    int row = t * 16 + c16;
+    row = row < V ? row : V - 1;
+    return W + static_cast<long>(row) * r + s * 32 + grp * 8;
+  };
+  uint4* lds_w = reinterpret_cast<uint4*>(smem);                                   // [TL][RK][64]
+  uint16_t* lds_r = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(TL) * RK * 1024);  // [B][r + pad]
+
+  const int treg = t0 + wave * TR;
+  uint4 wr[TR][RK];
+#pragma unroll
+  for (int i = 0; i < TR; ++i)
+#pragma unroll
+    for (int s = 0; s < RK; ++s) wr[i][s] = ld_stream(frag_ptr(treg + i, s));
+  const int tlds = t0 + kWaves * TR;
+  for (int j = wave; j < TL; j += kWaves)
+#pragma unroll
+    for (int s = 0; s < RK; ++s) load_lds16(frag_ptr(tlds + j, s), lds_w + (j * RK + s) * 64);
+  const int tstream = tlds + TL;
+  unsigned touch = 0;
+  for (int t = tstream + wave; t < t1; t += kWaves) {
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(W + static_cast<long>(t) * 16 * r);
+    const int lines = (t * 16 + 16 <= V ? 16 : V - t * 16) * r / 64;
+    for (int l = lane; l < lines; l += 64) touch ^= base[l * 32];
+  }
+  const bool tok_ok = c16 < B;
+
+  for (int i = 0; i < K; ++i) {
+    const unsigned tag = static_cast<unsigned>(i + 1);
+    for (int e = threadIdx.x; e < B * (r / 2); e += blockDim.x) {
+      const uint64_t w = wait_tag(f.rx + e, tag, status);
+      const int b = e / (r / 2), jj = e % (r / 2);
+      *reinterpret_cast<uint32_t*>(lds_r + b * (r + kStatePad) + 2 * jj) = static_cast<uint32_t>(w);
+    }
+    if (i == 0) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): resident tiles have landed
+    __syncthreads();
+
+    // state fragment: columns of absent requests read request 0's row (their
+    // logits are never taken)
+    auto bfrag = [&](int s) {
+      return *reinterpret_cast<const uint4*>(lds_r + (tok_ok ? c16 : 0) * (r + kStatePad) + s * 32 + grp * 8);
+    };
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    auto take = [&](int t, const floatx4& acc) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int vr = t * 16 + grp * 4 + q;
+        if (t < t1 && vr < V && tok_ok) {
+          const float v = acc[q];
+          if (better(v, vr, bv, bi)) { bv = v; bi = vr; }
+          if (a.tap) a.tap[(static_cast<long>(c16) * K + i) * V + vr] = v;
+        }
+      }
+    };
+    // the register tiles hold nearly the whole register file: the state
+    // fragments are read from LDS four k-steps at a time (the empty asm with
+    // a memory clobber keeps the compiler from hoisting all of them at once)
+    {
+      floatx4 acc[TR];
+#pragma unroll
+      for (int q = 0; q < TR; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s0 = 0; s0 < RK; s0 += 4) {
+        asm volatile("" ::: "memory");
+        uint4 b4[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b4[s] = bfrag(s0 + s);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int q = 0; q < TR; ++q) acc[q] = mma_step(wr[q][s0 + s], b4[s], acc[q], uint16_t());
+      }
+#pragma unroll
+      for (int q = 0; q < TR; ++q) take(treg + q, acc[q]);
+    }
+    for (int j = wave; j < TL; j += kWaves) {
+      floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+      int toff = j * RK * 64 + lane;   // opaque: one base per tile, k-steps as immediate offsets
+      asm volatile("" : "+v"(toff));
+#pragma unroll
+      for (int s0 = 0; s0 < RK; s0 += 4) {
+        asm volatile("" ::: "memory");
+        uint4 af[4], b4[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          af[s] = lds_w[toff + (s0 + s) * 64];
+          b4[s] = bfrag(s0 + s);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mma_step(af[s], b4[s], acc, uint16_t());
+      }
+      take(tlds + j, acc);
+    }
+    for (int t = tstream + wave; t < t1; t += kWaves) {
+      floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s0 = 0; s0 < RK; s0 += 4) {
+        asm volatile("" ::: "memory");
+        uint4 nx[4], b4[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          nx[s] = *reinterpret_cast<const uint4*>(frag_ptr(t, s0 + s));
+          b4[s] = bfrag(s0 + s);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mma_step(nx[s], b4[s], acc, uint16_t());
+      }
+      take(t, acc);
+    }
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (grp == 0) { sv[wave][c16] = bv; si[wave][c16] = bi; }
+    __syncthreads();
+    if (static_cast<int>(threadIdx.x) < B) {
+      float v = sv[0][threadIdx.x];
+      int ix = si[0][threadIdx.x];
+      for (int w = 1; w < kWaves; ++w)
+        if (better(sv[w][threadIdx.x], si[w][threadIdx.x], v, ix)) { v = sv[w][threadIdx.x]; ix = si[w][threadIdx.x]; }
+      publish_partial(a, static_cast<long>(threadIdx.x) * G + h, v, ix);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(f.arrive + static_cast<int>(blockIdx.x & 7) * 16, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (touch == 0x9e3779b9u && B < 0) a.cand[0] = 0;   // keeps the touch loads
+}
+
+template <int RK>
+size_t gatedhead_lds(int B, int r) {
+  constexpr int TL = kFuseLdsTiles / (RK * 1024);
+  const size_t helper = static_cast<size_t>(TL) * RK * 1024 + static_cast<size_t>(B) * (r + kStatePad) * 2;
+  const size_t team = static_cast<size_t>(B) * (3 * r) * 4 + 64 + 2 * kWaves * 4;
+  return helper > team ? helper : team;
+}
+
 }  // namespace
 
 int lmhead_groups(int V) {
@@ -587,6 +957,37 @@ hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, hipStream_t st) 
   if (RK == 16) hipLaunchKernelGGL(seqhead_kernel<16>, dim3(grid), dim3(kWaves * 64), sm, st, f);
   else hipLaunchKernelGGL(seqhead_kernel<10>, dim3(grid), dim3(kWaves * 64), sm, st, f);
   return hipGetLastError();
+}
+
+bool gatedhead_fused(int B, int K, int r, bool bf16) {
+  if (!bf16 || r != kGR || B < 1 || B > 8 || K < 1) return false;
+  int dev = 0, coop = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  if (cus - kGTeam < 64 || cus - kGTeam > kFuseMaxHelpers) return false;
+  return gatedhead_lds<16>(B, r) + 2048 <= 160 * 1024;
+}
+
+size_t gatedhead_exchange_bytes(int B, int r) {
+  return static_cast<size_t>(B) * (r + r / 2 + 1) * sizeof(uint64_t);
+}
+
+hipError_t launch_gatedhead(const GatedFuseArgs& f0, hipStream_t st) {
+  if (!gatedhead_fused(f0.B, f0.K, f0.la.r, true)) return hipErrorInvalidValue;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  GatedFuseArgs f = f0;
+  f.la.G = cus - kGTeam;
+  const size_t sm = gatedhead_lds<16>(f.B, f.la.r);
+  const void* fn = reinterpret_cast<const void*>(&gatedhead_kernel<16>);
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
+  if (e != hipSuccess) return e;
+  void* args[] = {&f};
+  return hipLaunchCooperativeKernel(fn, dim3(cus), dim3(kWaves * 64), args, static_cast<unsigned>(sm), st);
 }
 
 hipError_t launch_lmhead(const LmArgs& a0, bool bf16, hipStream_t st) {
