@@ -410,7 +410,7 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
     // tokens feed the next step (stage events: the first step)
     float* Sst = tp.state ? tp.state : Sf;
     int32_t* GT = reinterpret_cast<int32_t*>(ws + p.GT);
-    const bool fused = gatedhead_fused(B, K, r, bf16) &&
+    const bool fused = gatedhead_fused(B, K, r, d.vocab, bf16) &&
                        gatedhead_exchange_bytes(B, r) <= scan_scratch_floats(B, r) * sizeof(float);
     if (fused) {
       // all K positions in one persistent launch, W_o held on chip
@@ -419,7 +419,7 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
       gf.emb = gh->emb; gf.w_s = gh->w_s; gf.b_s = gh->b_s; gf.w_h = gh->w_h; gf.b_h = gh->b_h;
       gf.anchors = anchor_ids; gf.qh = P; gf.s_out = Sst;
       gf.sx = xw; gf.rx = xw + static_cast<size_t>(B) * r; gf.dx = xw + static_cast<size_t>(B) * (r + r / 2);
-      gf.arrive = counters + counter_gated();
+      gf.px = xw + static_cast<size_t>(B) * (r + r / 2 + 1);
       gf.la = la;
       gf.la.W = gh->w_o; gf.la.M = B; gf.la.tok0 = 0;
       gf.B = B; gf.K = K; gf.D = D;

@@ -21,8 +21,7 @@ size_t scan_scratch_floats(int B, int r);   // size of ScanArgs::U
 inline int counter_seq_done() { return 64; }
 inline int counter_gemm() { return counter_seq_done() + 64; }
 inline int counter_lm_xcd() { return counter_gemm() + 2 * 128; }   // [8 XCDs] x 16 words
-inline int counter_gated() { return counter_lm_xcd() + 8 * 16; }
-inline int counter_words() { return counter_gated() + 8 * 16; }
+inline int counter_words() { return counter_lm_xcd() + 8 * 16; }
 enum Status { STATUS_BARRIER_TIMEOUT = 1 };
 
 // Partial sums of squares per activation row: one slot per producing
@@ -223,11 +222,11 @@ struct GatedFuseArgs {
   uint64_t* sx;             // [B, R]   tagged state words (team exchange)
   uint64_t* rx;             // [B, R/2] tagged r_i words (two bf16 each)
   uint64_t* dx;             // [B]      tagged d_i words
-  unsigned* arrive;         // 8 XCD arrival counters, 16 words apart (zero at launch)
-  LmArgs la;                // W = W_o; outputs, partials and counters
+  uint64_t* px;             // [B, G]   tagged (max, index) words of the helpers
+  LmArgs la;                // W = W_o; outputs and the status word
   int B, K, D;
 };
-bool gatedhead_fused(int B, int K, int r, bool bf16);
+bool gatedhead_fused(int B, int K, int r, int V, bool bf16);
 size_t gatedhead_exchange_bytes(int B, int r);
 hipError_t launch_gatedhead(const GatedFuseArgs& f, hipStream_t st);
 

@@ -559,12 +559,11 @@ size_t seqhead_lds(int M, int r) {
 //            elements, published as tagged words; all R read back;
 //            r_i = W_h[:, :R] s_i + qh_i + b_h for its 32 elements, published
 //            as tagged words (two bf16 each);
-//   helpers  wait for every r_i word, multiply their tiles, publish
-//            (max, index) partials and count themselves in (one counter per
-//            XCD, never reset within the launch);
-//   team     member b < B waits for all arrivals of the position, reduces
-//            request b's partials in fixed order, writes its candidate and
-//            publishes d_i as a tagged word for the whole team.
+//   helpers  wait for every r_i word, multiply their tiles, publish one
+//            tagged (max, index) word per request;
+//   team     member b < B waits for request b's G words, reduces them in
+//            fixed order, writes its candidate and publishes d_i as a tagged
+//            word for the whole team.
 // A word is rewritten only for a later position, after all its readers have
 // passed the dependency that the later position needs, so tags alone order
 // everything.  The launch is cooperative (every workgroup resident: the team
@@ -578,6 +577,30 @@ __device__ __forceinline__ float dot8(const uint4& w, const float* x) {
          __uint_as_float(w.y << 16) * x[2] + __uint_as_float(w.y & 0xffff0000u) * x[3] +
          __uint_as_float(w.z << 16) * x[4] + __uint_as_float(w.z & 0xffff0000u) * x[5] +
          __uint_as_float(w.w << 16) * x[6] + __uint_as_float(w.w & 0xffff0000u) * x[7];
+}
+
+// N (8 or 4) sums over the 64 lanes at once: butterfly steps that halve the
+// number of values per lane (lanes above the step's bit keep the upper
+// half), then a plain butterfly over the remaining lanes.  Lane l ends with
+// the total of value l >> (6 - log2 N): 10 (N = 8) or 6 (N = 4) lane swaps
+// instead of 6 N.
+template <int N>
+__device__ __forceinline__ float wave_sums(float (&v)[N], int lane) {
+  static_assert(N == 8 || N == 4, "N = 8 or 4");
+#pragma unroll
+  for (int o = 32, n = N; n > 1; o >>= 1, n >>= 1) {
+    const bool hi = (lane & o) != 0;
+#pragma unroll
+    for (int k = 0; k < n / 2; ++k) {
+      const float send = hi ? v[k] : v[k + n / 2];
+      const float keep = hi ? v[k + n / 2] : v[k];
+      v[k] = keep + __shfl_xor(send, o, kWave);
+    }
+  }
+  float t = v[0];
+#pragma unroll
+  for (int o = 32 / N; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
+  return t;
 }
 
 __device__ __forceinline__ uint64_t wait_tag(const uint64_t* p, unsigned tag, unsigned* status) {
@@ -599,10 +622,11 @@ __device__ __forceinline__ void put_tag(uint64_t* p, uint32_t v, unsigned tag) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The argmax of request b at position i: wait until the helpers' arrival
-// counters (one per XCD) add up to G (i + 1), fold the G partials (each
-// thread a strided share in index order, then the waves in order: the same
-// result for any arrival order), write the candidate and publish d_i.
+// The argmax of request b at position i: every helper's (max, index) for
+// the position arrives as one tagged word (value in the high half, index in
+// the low 24 bits, tag in the top 8); fold them (each thread a strided
+// share in index order, then the waves in order: the same result for any
+// arrival order), write the candidate and publish d_i.
 __device__ __forceinline__ void gated_finish(const GatedFuseArgs& f, unsigned char* smem, int b, int i,
                                              unsigned* status) {
   const LmArgs& a = f.la;
@@ -610,29 +634,23 @@ __device__ __forceinline__ void gated_finish(const GatedFuseArgs& f, unsigned ch
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* rv = reinterpret_cast<float*>(smem + static_cast<size_t>(f.B) * 3 * kGR * 4 + 64);   // after xs, ss, dsh
   int* ri = reinterpret_cast<int*>(rv + kWaves);
-  if (threadIdx.x == 0) {
-    const unsigned want = static_cast<unsigned>(G) * static_cast<unsigned>(i + 1);
+  const unsigned tag = static_cast<unsigned>(i + 1) & 0xffu;
+  float v = -INFINITY;
+  int ix = 0x7fffffff;
+  for (int e = threadIdx.x; e < G; e += blockDim.x) {
+    const uint64_t* p = f.px + static_cast<long>(b) * G + e;
+    uint64_t w = scan_detail::ld_tagged(p);
     unsigned spins = 0;
-    for (;;) {
-      unsigned n = 0;
-      for (int q = 0; q < 8; ++q)
-        n += __hip_atomic_load(f.arrive + q * 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (n >= want) break;
+    while ((static_cast<uint32_t>(w) >> 24) != tag) {
       __builtin_amdgcn_s_sleep(2);
       if (++spins > scan_detail::kSpinLimit) {
         atomicOr(status, static_cast<unsigned>(STATUS_BARRIER_TIMEOUT));
         break;
       }
+      w = scan_detail::ld_tagged(p);
     }
-  }
-  __syncthreads();
-  float v = -INFINITY;
-  int ix = 0x7fffffff;
-  for (int e = threadIdx.x; e < G; e += blockDim.x) {
-    const float pv = __hip_atomic_load(a.part_max + static_cast<long>(b) * G + e, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-    const int pi = __hip_atomic_load(a.part_idx + static_cast<long>(b) * G + e, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+    const float pv = __uint_as_float(static_cast<uint32_t>(w >> 32));
+    const int pi = static_cast<int>(static_cast<uint32_t>(w) & 0xffffffu);
     if (better(pv, pi, v, ix)) { v = pv; ix = pi; }
   }
 #pragma unroll
@@ -708,15 +726,18 @@ __device__ __forceinline__ void gated_team(const GatedFuseArgs& f, unsigned char
       float x0[8], x1[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) { x0[t] = x[lane * 8 + t]; x1[t] = x[R + lane * 8 + t]; }
-      float dg[4], dc[4];
+      float d8[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        dg[q] = wave_sum(dot8(wg[q][0], x0) + dot8(wg[q][1], x1));
-        dc[q] = wave_sum(dot8(wc[q][0], x0) + dot8(wc[q][1], x1));
+        d8[q] = dot8(wg[q][0], x0) + dot8(wg[q][1], x1);
+        d8[4 + q] = dot8(wc[q][0], x0) + dot8(wc[q][1], x1);
       }
-      if (lane < 4) {
-        const int j = j0 + lane;
-        const float g = pick(dg, lane) + pick(bg, lane), c = pick(dc, lane) + pick(bc, lane);
+      // lane 8 q holds the g sum of element q, lane 8 q + 32 its c sum
+      const float sum = wave_sums<8>(d8, lane);
+      const float csum = __shfl_xor(sum, 32, kWave);
+      if (lane < 32 && (lane & 7) == 0) {
+        const int q = lane >> 3, j = j0 + q;
+        const float g = sum + pick(bg, q), c = csum + pick(bc, q);
         const float fg = 1.0f / (1.0f + expf(-g));
         const float sn = fg * x[j] + (1.0f - fg) * tanhf(c);
         f.s_out[(static_cast<long>(b) * K + i) * R + j] = sn;
@@ -732,15 +753,20 @@ __device__ __forceinline__ void gated_team(const GatedFuseArgs& f, unsigned char
       float s8[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) s8[t] = ss[b * R + lane * 8 + t];
-      float dr[4];
+      float d4[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dr[q] = wave_sum(dot8(wh[q], s8));
-      if (lane < 2) {
+      for (int q = 0; q < 4; ++q) d4[q] = dot8(wh[q], s8);
+      // lane 16 q holds element q's sum; pairs (0, 1) and (2, 3) meet at
+      // lanes 0 and 32
+      const float sum = wave_sums<4>(d4, lane);
+      const float odd = __shfl_xor(sum, 16, kWave);
+      if ((lane & 31) == 0) {
+        const int q = lane >> 4;   // 0 or 2
         const float* qrow = f.qh + (static_cast<long>(b) * K + i) * R + j0;
-        const float ra = pick(dr, 2 * lane) + qrow[2 * lane] + pick(bh, 2 * lane);
-        const float rb = pick(dr, 2 * lane + 1) + qrow[2 * lane + 1] + pick(bh, 2 * lane + 1);
+        const float ra = sum + qrow[q] + pick(bh, q);
+        const float rb = odd + qrow[q + 1] + pick(bh, q + 1);
         const uint32_t pk = static_cast<uint32_t>(f32_to_bf16(ra)) | (static_cast<uint32_t>(f32_to_bf16(rb)) << 16);
-        put_tag(f.rx + b * (R / 2) + j0 / 2 + lane, pk, tag);
+        put_tag(f.rx + b * (R / 2) + j0 / 2 + q / 2, pk, tag);
       }
     }
     // member m < B: the argmax of request m once every helper has counted in
@@ -792,7 +818,7 @@ __global__ __launch_bounds__(kWaves * 64) void gatedhead_kernel(GatedFuseArgs f)
     for (int s = 0; s < RK; ++s) load_lds16(frag_ptr(tlds + j, s), lds_w + (j * RK + s) * 64);
   const int tstream = tlds + TL;
   unsigned touch = 0;
-  for (int t = tstream + wave; t < t1; t += kWaves) {
+  for (int t = tstream + (kWaves - 1 - wave); t < t1; t += kWaves) {
     const uint32_t* base = reinterpret_cast<const uint32_t*>(W + static_cast<long>(t) * 16 * r);
     const int lines = (t * 16 + 16 <= V ? 16 : V - t * 16) * r / 64;
     for (int l = lane; l < lines; l += 64) touch ^= base[l * 32];
@@ -866,7 +892,9 @@ __global__ __launch_bounds__(kWaves * 64) void gatedhead_kernel(GatedFuseArgs f)
       }
       take(tlds + j, acc);
     }
-    for (int t = tstream + wave; t < t1; t += kWaves) {
+    // streamed tiles from the last wave down: wave 0 already has the
+    // ninth LDS tile
+    for (int t = tstream + (kWaves - 1 - wave); t < t1; t += kWaves) {
       floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s0 = 0; s0 < RK; s0 += 4) {
@@ -895,13 +923,12 @@ __global__ __launch_bounds__(kWaves * 64) void gatedhead_kernel(GatedFuseArgs f)
       int ix = si[0][threadIdx.x];
       for (int w = 1; w < kWaves; ++w)
         if (better(sv[w][threadIdx.x], si[w][threadIdx.x], v, ix)) { v = sv[w][threadIdx.x]; ix = si[w][threadIdx.x]; }
-      publish_partial(a, static_cast<long>(threadIdx.x) * G + h, v, ix);
+      // (a helper without tiles reports index 0 at -inf: never better)
+      const uint32_t lo = (static_cast<uint32_t>(ix < V ? ix : 0) & 0xffffffu) | ((tag & 0xffu) << 24);
+      __hip_atomic_store(f.px + static_cast<long>(threadIdx.x) * G + h,
+                         (static_cast<uint64_t>(__float_as_uint(v)) << 32) | lo, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
-    __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(f.arrive + static_cast<int>(blockIdx.x & 7) * 16, 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
   }
   if (touch == 0x9e3779b9u && B < 0) a.cand[0] = 0;   // keeps the touch loads
 }
@@ -959,8 +986,8 @@ hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, hipStream_t st) 
   return hipGetLastError();
 }
 
-bool gatedhead_fused(int B, int K, int r, bool bf16) {
-  if (!bf16 || r != kGR || B < 1 || B > 8 || K < 1) return false;
+bool gatedhead_fused(int B, int K, int r, int V, bool bf16) {
+  if (!bf16 || r != kGR || B < 1 || B > 8 || K < 1 || K > 255 || V < 1 || V >= (1 << 24)) return false;
   int dev = 0, coop = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return false;
@@ -970,11 +997,11 @@ bool gatedhead_fused(int B, int K, int r, bool bf16) {
 }
 
 size_t gatedhead_exchange_bytes(int B, int r) {
-  return static_cast<size_t>(B) * (r + r / 2 + 1) * sizeof(uint64_t);
+  return static_cast<size_t>(B) * (r + r / 2 + 1 + kFuseMaxHelpers) * sizeof(uint64_t);
 }
 
 hipError_t launch_gatedhead(const GatedFuseArgs& f0, hipStream_t st) {
-  if (!gatedhead_fused(f0.B, f0.K, f0.la.r, true)) return hipErrorInvalidValue;
+  if (!gatedhead_fused(f0.B, f0.K, f0.la.r, f0.la.V, true)) return hipErrorInvalidValue;
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
