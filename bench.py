@@ -59,12 +59,13 @@ def parse():
 
 # ------------------------------------------------------- algorithmic costs ---
 
-def stage_costs(w, head="fixed"):
+def stage_costs(w, head="fixed", layers=None):
     """Algorithmic HBM bytes and flops per stage launch group (each weight read
     once; token table: B rows; activations counted once in and once out).
     With the gated head, "scan" and "lm_head" are one position's state update
     and vocabulary pass (the stage events time the first position); the step
-    runs them K times (stage_reps)."""
+    runs them K times (stage_reps).  Per-layer stages count the layers in
+    `layers` (default: all; the stage events time the first layer only)."""
     e = 2 if w.dtype == "bf16" else 4
     B, m, K, D, F, r, V = w.B, w.m, w.K, w.D, w.ffn, w.rank, w.vocab
     S, L = m + 1 + K, 1 + K
@@ -72,7 +73,7 @@ def stage_costs(w, head="fixed"):
     c = {k: [0.0, 0.0] for k in ("features", "qkv", "attention", "oproj", "gate_up", "down",
                                   "final_norm", "seq_proj", "scan", "lm_head")}
     c["features"] = [B * m * D * e + m * D * e + D * e + B * D * e + D * e + B * S * D * 4, 0.0]
-    for l in range(w.n_layers):
+    for l in (range(w.n_layers) if layers is None else layers):
         Lr = L - 1 if l == w.n_layers - 1 else L
         c["qkv"][0] += (Hq + 2 * Hkv) * D * e + D * e + B * S * D * 4 + B * (Lr * Hq + S * 2 * Hkv) * 4
         c["qkv"][1] += 2.0 * D * (B * Lr * Hq + B * S * 2 * Hkv)
@@ -285,7 +286,7 @@ def main():
     td = torch.from_numpy(tgt).cuda()
     torch.cuda.synchronize()
 
-    costs = stage_costs(w, args.head)
+    costs = stage_costs(w, args.head, layers=[0])   # what one timed launch group covers
     # dominant kernel: the stage with the largest algorithmic time at peak
     def t_roof(s):
         return max(costs[s][0] / HBM_PEAK, costs[s][1] / MFMA_BF16_PEAK)

@@ -81,8 +81,9 @@ def _w(name, B, m, D, L, nq, nkv, dh, F, K, r, V, dt, i, match, step=0.0):
                     20261016 + i, match, step)
 
 
-# The five workloads: a tiny fp32 block, Qwen3-4B and Qwen3-8B shaped single
-# requests, a 32-request two-layer batch and a 64-request all-layer batch.
+# The workloads: a tiny fp32 block, Qwen3-4B and Qwen3-8B shaped single
+# requests, a 32-request two-layer batch, a 64-request all-layer batch, and
+# the 8B single request with the five-layer backbone the paper trains.
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     _w("tiny_f32", 1, 4, 256, 1, 4, 2, 64, 512, 7, 32, 4096, F32, 1,
        "const:0.8", 0.25),
@@ -94,6 +95,8 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
        BF16, 4, "uniform:0.5:0.95"),
     _w("qwen3_8b_b64_m36", 64, 36, 4096, 1, 32, 8, 128, 12288, 7, 512, 151936,
        BF16, 5, "pow:0.9"),
+    _w("qwen3_8b_b1_l5", 1, 14, 4096, 5, 32, 8, 128, 12288, 7, 512, 151936,
+       BF16, 6, "pow:0.85"),
 ]}
 
 
