@@ -332,3 +332,124 @@ def prefix_survival(c: np.ndarray) -> np.ndarray:
 def expected_commit(c: np.ndarray) -> np.ndarray:
     """tau = E[A + 1] = 1 + sum_j P(A >= j) ([W] "分布重叠怎样影响平均推进量")."""
     return 1.0 + prefix_survival(c).sum(axis=-1)
+
+
+# ------------------------------------------------- sampling at temperature ---
+# Random numbers: Philox4x32-10 (J. Salmon, M. Moraes, R. Dror, D. Shaw,
+# "Parallel random numbers: as easy as 1, 2, 3", SC 2011), written from its
+# published definition: ten rounds, each two 32 x 32 -> 64-bit products of
+# counter words 0 and 2 with the round multipliers, the high halves xor-ed
+# with the other counter words and the key, the key bumped by the Weyl
+# constants.  A uniform in (0, 1) is (x0 + 1/2) / 2^32 (exact in fp64).
+
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 of counter words ctr[0..3] and key words key[0..1]
+    (scalars or equal-shape uint arrays); returns the four output words."""
+    m = 0xFFFFFFFF
+    c = [np.asarray(x, dtype=np.uint64) & m for x in ctr]
+    k = [np.asarray(x, dtype=np.uint64) & m for x in key]
+    for _ in range(10):
+        p0 = c[0] * _PHILOX_M[0]
+        p1 = c[2] * _PHILOX_M[1]
+        c = [(p1 >> 32) ^ c[1] ^ k[0], p1 & m, (p0 >> 32) ^ c[3] ^ k[1], p0 & m]
+        k = [(k[0] + _PHILOX_W[0]) & m, (k[1] + _PHILOX_W[1]) & m]
+    return [x.astype(np.uint32) for x in c]
+
+
+def uniform01(seed: int, stream: int, a, b) -> np.ndarray:
+    """Uniform in (0, 1) for counter (a, b, stream, 0) under key (seed low, seed high)."""
+    a = np.asarray(a)
+    b = np.broadcast_to(np.asarray(b), a.shape)
+    x = philox4x32_10((a, b, np.full(a.shape, stream), np.zeros(a.shape)),
+                      (np.full(a.shape, seed & 0xFFFFFFFF), np.full(a.shape, (seed >> 32) & 0xFFFFFFFF)))
+    return (x[0].astype(np.float64) + 0.5) / 4294967296.0
+
+
+def softmax_t(logits: np.ndarray, T: float) -> np.ndarray:
+    """softmax(logits / T) in fp64 along the last axis."""
+    z = np.asarray(logits, dtype=np.float64) / T
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def sample_tokens(logits: np.ndarray, T: float, seed: int, stream: int):
+    """One token per row of logits [N, V] drawn from softmax(logits / T).
+
+    [W] "贪心模式与随机模式要分别说明": at a positive temperature the draft
+    samples its candidates (and, in match mode, the target its tokens).
+    READING: drawn by the Gumbel-max rule, argmax_v (l_v / T - log(-log u_v))
+    with u_v = uniform01(seed, stream, v, row), which is distributed exactly as
+    softmax(l / T) (ties to the lowest index).  Returns tokens [N] and the gap
+    between the two best perturbed scores (for comparisons at near ties).
+    """
+    x = np.asarray(logits, dtype=np.float64)
+    N, V = x.shape
+    v, n = np.meshgrid(np.arange(V), np.arange(N))
+    u = uniform01(seed, stream, v, n)
+    score = x / T - np.log(-np.log(u))
+    tok = np.argmax(score, axis=1)
+    top2 = np.partition(score, -2, axis=1)[:, -2:]
+    return tok.astype(np.int64), top2[:, 1] - top2[:, 0]
+
+
+def inverse_cdf(w: np.ndarray, u: float):
+    """The first index whose running sum of the weights w exceeds u * sum(w)
+    (the last positive weight if rounding leaves none); also the distance of
+    u * sum(w) to the nearest running sum (for comparisons near a boundary)."""
+    c = np.cumsum(np.asarray(w, dtype=np.float64))
+    t = u * c[-1]
+    idx = int(np.searchsorted(c, t, side="right"))
+    if idx >= len(c):
+        idx = int(np.nonzero(np.asarray(w) > 0)[0][-1])
+    return idx, float(np.min(np.abs(c - t)))
+
+
+def accept_sampled(cand: np.ndarray, draft_logits: np.ndarray, target_logits: np.ndarray,
+                   T: float, seed: int) -> dict:
+    """Speculative rejection sampling of one round per request.
+
+    [W] "贪心模式与随机模式要分别说明": with p the target's and q the draft's
+    conditional distribution at a candidate position and d ~ q the candidate,
+    d is accepted with probability min(1, p(d) / q(d)); at the first rejection
+    the token is drawn from the normalised positive residual [p - q]_+, so the
+    committed token is distributed as p; the leading run of accepted
+    candidates is committed (the first-failure rule of the greedy case).
+    READING: when all K pass, the extra token is drawn from the target's
+    distribution after the last candidate; p = softmax(target / T),
+    q = softmax(draft / T) in fp64; the acceptance test is u q(d) < p(d) with
+    u = uniform01(seed, 1, i, b); the residual (or extra) draw is
+    inverse_cdf(weights, uniform01(seed, 2, i, b)) at the deciding position i.
+    cand [B, K]; draft_logits [B, K, V]; target_logits [B, K + 1, V].
+    Returns A [B], next token [B], and per request the margin of its last
+    decision (for comparisons near a threshold).
+    """
+    B, K = cand.shape
+    A = np.zeros(B, dtype=np.int64)
+    nxt = np.zeros(B, dtype=np.int64)
+    margin = np.full(B, np.inf)
+    for b in range(B):
+        for i in range(K + 1):
+            p = softmax_t(target_logits[b, i], T)
+            if i == K:
+                w = p
+            else:
+                q = softmax_t(draft_logits[b, i], T)
+                d = int(cand[b, i])
+                u = float(uniform01(seed, 1, i, b))
+                margin[b] = min(margin[b], abs(u * q[d] - p[d]) / max(p[d], q[d], 1e-300))
+                if u * q[d] < p[d]:
+                    A[b] += 1
+                    continue
+                w = np.maximum(p - q, 0.0)
+                if not (w > 0).any():
+                    w = p
+            tok, gap = inverse_cdf(w, float(uniform01(seed, 2, i, b)))
+            nxt[b] = tok
+            margin[b] = min(margin[b], gap / max(w.sum(), 1e-300))
+            break
+    return dict(A=A, next=nxt, margin=margin)
