@@ -45,6 +45,9 @@ def parse():
                    help="time budget of the CPU oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stages", action="store_true", help="also time every stage separately")
+    p.add_argument("--temperature", type=float, default=0.0,
+                   help="> 0: the candidates are drawn at this temperature from the draft's logits "
+                        "and verified by rejection sampling against synthetic target logits")
     p.add_argument("--head", choices=["fixed", "gated"], default="fixed",
                    help="sequential head: the fixed token-free recurrence (one vocabulary "
                         "pass) or the walkthrough's gated head (one vocabulary pass per position)")
@@ -180,7 +183,7 @@ class HipEvents:
 
 # ------------------------------------------------------------- CPU baseline ---
 
-def cpu_baseline(w, weights, H, anchors, budget_s, head=None):
+def cpu_baseline(w, weights, H, anchors, budget_s, head=None, sampling=None):
     """The fp64 oracle timed on the host cores on a bounded sample (with the
     gated head's weights: the backbone, then the gated head)."""
     import oracle
@@ -202,6 +205,16 @@ def cpu_baseline(w, weights, H, anchors, budget_s, head=None):
         else:
             ref = oracle.draft_block(w, Wf, Hf, rows, with_head=False)
             ref.update(oracle.gated_heads(ref["h"], anchors, hf))
+        if sampling is not None:   # draw the candidates, verify by rejection sampling
+            T, tl = sampling
+            c, _ = oracle.sample_tokens(ref["logits"].reshape(w.B * w.K, w.vocab), T, 1234 + n, 0)
+            oracle.accept_sampled(c.reshape(w.B, w.K), ref["logits"], tl, T, 1234 + n)
+            tgt = tgt if tgt is not None else np.zeros((w.B, w.K + 1), dtype=np.int64)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+            continue
         if tgt is None:
             tgt = make_target_tokens(w, ref["cand"])
         oracle.accept_prefix(ref["cand"], tgt)
@@ -212,7 +225,8 @@ def cpu_baseline(w, weights, H, anchors, budget_s, head=None):
     value = n * w.B * w.K / el
     res = {"value": value, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
            "sample": f"{n} full draft+accept step(s) of {w.name} (B={w.B}"
-                     f"{', gated head' if hf is not None else ''}), fp64 numpy, {el:.1f} s"}
+                     f"{', gated head' if hf is not None else ''}"
+                     f"{', sampled at T=%g' % sampling[0] if sampling is not None else ''}), fp64 numpy, {el:.1f} s"}
     return res, ref, tgt
 
 
@@ -247,11 +261,18 @@ def main():
     H, anchors = make_features(w), make_anchors(w)
     gated = args.head == "gated"
     head = make_gated_head(w) if gated else None
+    sampled = args.temperature > 0
+    if sampled:
+        if gated:
+            raise SystemExit("--temperature applies to the fixed head (the gated head drafts greedily)")
+        from synth import make_sampling_case
+        _, tl = make_sampling_case(w.seed, w.B, w.K, w.vocab, mix=0.9)   # target logits
 
     cpu, ref, tgt = None, None, None
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
-        cpu, ref, tgt = cpu_baseline(w, weights, H, anchors, args.cpu_seconds, head)
+        cpu, ref, tgt = cpu_baseline(w, weights, H, anchors, args.cpu_seconds, head,
+                                     (args.temperature, tl) if sampled else None)
     else:
         rng = np.random.default_rng(0)
         tgt = make_target_tokens(w, rng.integers(0, w.vocab, size=(w.B, w.K)))
@@ -284,6 +305,13 @@ def main():
     Hd = to_device(H, "cuda")
     ad = torch.from_numpy(anchors).cuda()
     td = torch.from_numpy(tgt).cuda()
+    if sampled:
+        tlog = torch.from_numpy(tl).cuda()                      # target logits, resident
+        dlog = torch.empty((w.B, w.K, w.vocab), dtype=torch.float32, device="cuda")
+        taps_s = B.make_taps(logits=dlog)
+        rows = w.B * (2 * w.K + 1)
+        sws = torch.empty(B.dlite_sampling_workspace_bytes(rows), dtype=torch.uint8, device="cuda")
+        scand = torch.empty((w.B, w.K), dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
 
     costs = stage_costs(w, args.head, layers=[0])   # what one timed launch group covers
@@ -296,6 +324,12 @@ def main():
     ev = HipEvents()
 
     def step(i):
+        if sampled:
+            model.draft(Hd, ad, taps=taps_s, weights=copies[i % len(copies)])
+            B.dlite_sample_tokens(dlog, w.B * w.K, w.vocab, args.temperature, 1234 + i, 0, scand, sws)
+            B.dlite_accept_sampled(scand, dlog, tlog, w.B, w.K, w.vocab, args.temperature, 1234 + i,
+                                   model.accept_len, model.next_anchor, sws)
+            return
         if gated:
             model.draft_gated(Hd, ad, weights=copies[i % len(copies)], head=heads[i % len(heads)])
         else:
@@ -373,6 +407,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "m": w.m, "D": w.D, "n_layers": w.n_layers,
                    "heads": f"{w.n_q}q/{w.n_kv}kv x{w.d_h}", "ffn": w.ffn, "K": w.K,
                    "rank": w.rank, "vocab": w.vocab, "head": args.head,
+                   "temperature": args.temperature,
                    "weight_copies": len(copies),
                    "parallelism": "single GPU"},
         "roofline": {"bound": bound, "kernel": dom, "achieved": round(achieved, 1),
@@ -389,7 +424,7 @@ def main():
                  "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4)},
         "tau_hat_last_step": float(np.mean(A + 1)),
     }
-    if ref is not None:
+    if ref is not None and not sampled:
         clear = ref["margin"] >= 1e-2
         if gated:   # a token differing at a near tie changes every later position
             clear = np.cumprod(clear, axis=1).astype(bool)

@@ -18,7 +18,8 @@ DLITE_F32, DLITE_BF16 = 0, 1
 ERRORS = {-1: "DLITE_ERR_NULL", -2: "DLITE_ERR_SHAPE", -3: "DLITE_ERR_DTYPE",
           -4: "DLITE_ERR_WORKSPACE", -5: "DLITE_ERR_UNSUPPORTED", -6: "DLITE_ERR_HIP"}
 EXPORTS = ["dlite_workspace_bytes", "dlite_draft_block", "dlite_draft_block_at",
-           "dlite_draft_block_gated",
+           "dlite_draft_block_gated", "dlite_sampling_workspace_bytes", "dlite_sample_tokens",
+           "dlite_accept_sampled",
            "dlite_accept_prefix", "dlite_set_stage_events", "dlite_last_error", "dlite_version"]
 STAGES = ["features", "qkv", "attention", "oproj", "gate_up", "down", "final_norm",
           "seq_proj", "scan", "lm_head"]
@@ -82,6 +83,15 @@ def load_library(path: str = LIB_PATH):
                                          c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                          POINTER(DliteTaps), c_void_p, c_size_t, c_void_p]
     lib.dlite_draft_block_at.restype = c_int
+    lib.dlite_sampling_workspace_bytes.argtypes = [c_int32]
+    lib.dlite_sampling_workspace_bytes.restype = c_size_t
+    lib.dlite_sample_tokens.argtypes = [c_void_p, c_int32, c_int32, ctypes.c_float, ctypes.c_uint64,
+                                        ctypes.c_uint32, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dlite_sample_tokens.restype = c_int
+    lib.dlite_accept_sampled.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                         ctypes.c_float, ctypes.c_uint64, c_void_p, c_void_p, c_void_p,
+                                         c_size_t, c_void_p]
+    lib.dlite_accept_sampled.restype = c_int
     lib.dlite_accept_prefix.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                         c_void_p, c_void_p]
     lib.dlite_accept_prefix.restype = c_int
@@ -197,6 +207,31 @@ def dlite_draft_block_at(dims, weights, verify_hidden, T, accept_len, anchor_ids
         _ptr(anchor_ids), _ptr(candidates), _ptr(max_logit),
         ctypes.byref(taps) if taps is not None else None, _ptr(workspace), ws_bytes,
         _stream(stream))
+    _check(rc)
+
+
+def dlite_sampling_workspace_bytes(rows: int) -> int:
+    n = load_library().dlite_sampling_workspace_bytes(rows)
+    if n == 0:
+        raise DliteError(-2, load_library().dlite_last_error().decode())
+    return n
+
+
+def dlite_sample_tokens(logits, N, V, temperature, seed, stream_id, tokens, workspace, stream=None):
+    """Enqueue temperature sampling of N rows; see include/dlite.h."""
+    rc = load_library().dlite_sample_tokens(
+        _ptr(logits), N, V, temperature, seed, stream_id, _ptr(tokens), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+
+
+def dlite_accept_sampled(candidates, draft_logits, target_logits, B, K, V, temperature, seed,
+                         accept_len, next_token, workspace, stream=None):
+    """Enqueue speculative rejection sampling of one round; see include/dlite.h."""
+    rc = load_library().dlite_accept_sampled(
+        _ptr(candidates), _ptr(draft_logits), _ptr(target_logits), B, K, V, temperature, seed,
+        _ptr(accept_len), _ptr(next_token), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc)
 
 

@@ -536,6 +536,54 @@ int dlite_draft_block_at(const dlite_dims* dims, const dlite_weights* w, const v
                     workspace_bytes, st);
 }
 
+size_t dlite_sampling_workspace_bytes(int32_t rows) {
+  if (rows < 1) {
+    fail(DLITE_ERR_SHAPE, "rows=%d must be positive", rows);
+    return 0;
+  }
+  ok();
+  return align256(sampling_scratch_bytes(rows));
+}
+
+int dlite_sample_tokens(const float* logits, int32_t N, int32_t V, float temperature, uint64_t seed,
+                        uint32_t stream_id, int32_t* tokens, void* workspace, size_t workspace_bytes,
+                        hipStream_t st) {
+  if (!logits) return fail(DLITE_ERR_NULL, "logits is NULL");
+  if (!tokens) return fail(DLITE_ERR_NULL, "tokens is NULL");
+  if (!workspace) return fail(DLITE_ERR_NULL, "workspace is NULL");
+  if (N < 1 || N > 65535) return fail(DLITE_ERR_SHAPE, "N=%d not in [1, 65535]", N);
+  if (V < 1) return fail(DLITE_ERR_SHAPE, "V=%d must be positive", V);
+  if (!(temperature > 0.f) || !(temperature < INFINITY))
+    return fail(DLITE_ERR_SHAPE, "temperature must be positive and finite");
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(DLITE_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  if (workspace_bytes < sampling_scratch_bytes(N))
+    return fail(DLITE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, sampling_scratch_bytes(N));
+  DLITE_LAUNCH(launch_sample_tokens(logits, N, V, temperature, seed, stream_id, tokens, workspace, st));
+  return ok();
+}
+
+int dlite_accept_sampled(const int32_t* candidates, const float* draft_logits, const float* target_logits,
+                         int32_t B, int32_t K, int32_t V, float temperature, uint64_t seed, int32_t* accept_len,
+                         int32_t* next_token, void* workspace, size_t workspace_bytes, hipStream_t st) {
+  if (!candidates) return fail(DLITE_ERR_NULL, "candidates is NULL");
+  if (!draft_logits) return fail(DLITE_ERR_NULL, "draft_logits is NULL");
+  if (!target_logits) return fail(DLITE_ERR_NULL, "target_logits is NULL");
+  if (!accept_len) return fail(DLITE_ERR_NULL, "accept_len is NULL");
+  if (!next_token) return fail(DLITE_ERR_NULL, "next_token is NULL");
+  if (!workspace) return fail(DLITE_ERR_NULL, "workspace is NULL");
+  if (B < 1 || K < 1 || K > 64 || static_cast<long>(B) * (2 * K + 1) > 65535)
+    return fail(DLITE_ERR_SHAPE, "B=%d, K=%d: need K in [1, 64] and B (2K + 1) <= 65535", B, K);
+  if (V < 1) return fail(DLITE_ERR_SHAPE, "V=%d must be positive", V);
+  if (!(temperature > 0.f) || !(temperature < INFINITY))
+    return fail(DLITE_ERR_SHAPE, "temperature must be positive and finite");
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(DLITE_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  const size_t need = sampling_scratch_bytes(static_cast<long>(B) * (2 * K + 1));
+  if (workspace_bytes < need) return fail(DLITE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  DLITE_LAUNCH(launch_accept_sampled(candidates, draft_logits, target_logits, B, K, V, temperature, seed, accept_len,
+                                     next_token, workspace, st));
+  return ok();
+}
+
 int dlite_accept_prefix(const int32_t* candidates, const int32_t* target_tokens, int32_t B,
                         int32_t K, int32_t* accept_len, int32_t* next_anchor, hipStream_t st) {
   if (!candidates) return fail(DLITE_ERR_NULL, "candidates is NULL");

@@ -230,6 +230,14 @@ bool gatedhead_fused(int B, int K, int r, int V, bool bf16);
 size_t gatedhead_exchange_bytes(int B, int r);
 hipError_t launch_gatedhead(const GatedFuseArgs& f, hipStream_t st);
 
+// ------------------------------------------------ sampling at temperature ----
+size_t sampling_scratch_bytes(long rows);
+hipError_t launch_sample_tokens(const float* logits, int N, int V, float T, unsigned long long seed,
+                                unsigned stream, int32_t* tokens, void* scratch, hipStream_t st);
+hipError_t launch_accept_sampled(const int32_t* cand, const float* draft, const float* target, int B, int K, int V,
+                                 float T, unsigned long long seed, int32_t* A, int32_t* next, void* scratch,
+                                 hipStream_t st);
+
 // --------------------------------------------------------------- accept ----
 hipError_t launch_accept(const int32_t* cand, const int32_t* tgt, int B, int K,
                          int32_t* A, int32_t* next, hipStream_t st);

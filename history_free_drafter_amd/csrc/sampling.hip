@@ -1,0 +1,361 @@
+// Sampling at a positive temperature and speculative rejection sampling
+// (DLite walkthrough, section "贪心模式与随机模式要分别说明").
+//
+// Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011), a counter-based generator: the
+// value for counter (a, b, stream, 0) under key (seed low, seed high) is
+// computed where it is needed, so no generator state exists.  A uniform in
+// (0, 1) is (x0 + 1/2) / 2^32 in fp64.
+//
+// Draws from softmax(l / T) use the Gumbel-max rule, argmax_v (l_v / T -
+// log(-log u_v)), with the (value, index) reduction of the vocabulary pass.
+// Verification follows the page: candidate d ~ q is kept when u q(d) < p(d);
+// at the first rejection the token is drawn from the positive residual
+// [p - q]_+ (inverse CDF), after K acceptances from the target's last row.
+// Three passes over the vocabulary, each spread over 64 chunks: log-sum-exp
+// partials of every row, the deciding row's chunk sums, and the draw (chunk,
+// then index inside it).
+// Probabilities, exponentials and logarithms are fp64: the decisions are the
+// ones an exact evaluation would make except within rounding of a threshold.
+#include "kernels.hpp"
+
+namespace dlite {
+
+namespace {
+
+constexpr int kSampleChunks = 64;   // vocabulary chunks per row
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint2 k) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = make_uint4(hi1 ^ c.y ^ k.x, lo1, hi0 ^ c.w ^ k.y, lo0);
+    k.x += 0x9E3779B9u;
+    k.y += 0xBB67AE85u;
+  }
+  return c;
+}
+
+__device__ __forceinline__ double uniform01(unsigned long long seed, unsigned stream, unsigned a, unsigned b) {
+  const uint4 x = philox4x32_10(make_uint4(a, b, stream, 0u),
+                                make_uint2(static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32)));
+  return (static_cast<double>(x.x) + 0.5) * (1.0 / 4294967296.0);
+}
+
+struct Best {
+  double v;
+  int i;
+};
+__device__ __forceinline__ bool better_d(double v, int i, double bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// Block-wide (value, index) maximum in a fixed order; result in thread 0.
+__device__ Best block_best(double v, int i, Best* sh) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(i, o, kWave);
+    if (better_d(ov, oi, v, i)) { v = ov; i = oi; }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) sh[wave] = Best{v, i};
+  __syncthreads();
+  Best b = sh[0];
+  if (threadIdx.x == 0)
+    for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w)
+      if (better_d(sh[w].v, sh[w].i, b.v, b.i)) b = sh[w];
+  __syncthreads();
+  return b;
+}
+
+// Pass 1 of a draw: the best perturbed score of chunk c of row n.
+__global__ __launch_bounds__(kThreads) void sample_partial_kernel(const float* logits, int V, double invT,
+                                                                  unsigned long long seed, unsigned stream,
+                                                                  Best* part) {
+  __shared__ Best sh[kThreads / 64];
+  const int c = blockIdx.x, n = blockIdx.y;
+  const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
+  const int v1 = static_cast<int>(static_cast<long>(c + 1) * V / kSampleChunks);
+  const float* row = logits + static_cast<long>(n) * V;
+  double bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kThreads) {
+    const double u = uniform01(seed, stream, static_cast<unsigned>(v), static_cast<unsigned>(n));
+    const double s = static_cast<double>(row[v]) * invT - log(-log(u));
+    if (s > bv) { bv = s; bi = v; }   // v ascends within a thread: ties keep the lower
+  }
+  const Best b = block_best(bv, bi, sh);
+  if (threadIdx.x == 0) part[static_cast<long>(n) * kSampleChunks + c] = b;
+}
+
+// Pass 2: the chunks of a row in order.
+__global__ __launch_bounds__(64) void sample_final_kernel(const Best* part, int N, int32_t* tokens) {
+  const int n = blockIdx.x * 64 + static_cast<int>(threadIdx.x);
+  if (n >= N) return;
+  Best b = part[static_cast<long>(n) * kSampleChunks];
+  for (int c = 1; c < kSampleChunks; ++c) {
+    const Best o = part[static_cast<long>(n) * kSampleChunks + c];
+    if (better_d(o.v, o.i, b.v, b.i)) b = o;
+  }
+  tokens[n] = b.i;
+}
+
+// log-sum-exp partials of l / T: (chunk maximum, sum of exp(x - maximum)).
+struct Lse {
+  double m, s;
+};
+
+__global__ __launch_bounds__(kThreads) void lse_partial_kernel(const float* draft, const float* target, int BK,
+                                                               int V, double invT, Lse* part) {
+  __shared__ double sh[kThreads / 64];
+  const int c = blockIdx.x, row = blockIdx.y;
+  const float* x = row < BK ? draft + static_cast<long>(row) * V : target + static_cast<long>(row - BK) * V;
+  const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
+  const int v1 = static_cast<int>(static_cast<long>(c + 1) * V / kSampleChunks);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double m = -INFINITY;
+  for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kThreads) m = fmax(m, static_cast<double>(x[v]) * invT);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = fmax(m, __shfl_xor(m, o, kWave));
+  if (lane == 0) sh[wave] = m;
+  __syncthreads();
+  for (int w = 0; w < kThreads / 64; ++w) m = fmax(m, sh[w]);
+  __syncthreads();
+  double s = 0.0;
+  for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kThreads) s += exp(static_cast<double>(x[v]) * invT - m);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, kWave);
+  if (lane == 0) sh[wave] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int w = 0; w < kThreads / 64; ++w) t += sh[w];
+    part[static_cast<long>(row) * kSampleChunks + c] = Lse{m, t};
+  }
+}
+
+constexpr int kMaxRows = 2 * 64 + 1;   // rows of one request: K draft + K + 1 target (K <= 64)
+
+// log-sum-exp of the 2K + 1 rows of request b from the chunk partials
+// (draft rows b K + i, then target rows b (K + 1) + i): one wave per row, a
+// lane per chunk (64 chunks), wave reductions in a fixed order.
+static_assert(kSampleChunks == 64, "one lane per chunk");
+__device__ void request_lse(const Lse* part, int b, int B, int K, double* lse) {
+  const int BK = B * K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = static_cast<int>(blockDim.x >> 6);
+  for (int j = wave; j < 2 * K + 1; j += nw) {
+    const long row = j < K ? static_cast<long>(b) * K + j : BK + static_cast<long>(b) * (K + 1) + (j - K);
+    const Lse pc = part[row * kSampleChunks + lane];
+    double M = pc.m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) M = fmax(M, __shfl_xor(M, o, kWave));
+    double S = pc.s > 0.0 ? pc.s * exp(pc.m - M) : 0.0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) S += __shfl_xor(S, o, kWave);
+    if (lane == 0) lse[j] = M + log(S);
+  }
+}
+
+// The acceptance tests in position order (one thread): the number kept, and
+// whether the deciding draw is from the residual (else from the target's
+// row K).
+__device__ int decide(const int32_t* cand, const float* draft, const float* target, const double* lse, int b,
+                      int K, int V, double invT, unsigned long long seed, bool* resid) {
+  for (int i = 0; i < K; ++i) {
+    const int d = cand[static_cast<long>(b) * K + i];
+    bool keep = false;
+    if (d >= 0 && d < V) {
+      const double q = exp(static_cast<double>(draft[(static_cast<long>(b) * K + i) * V + d]) * invT - lse[i]);
+      const double p =
+          exp(static_cast<double>(target[(static_cast<long>(b) * (K + 1) + i) * V + d]) * invT - lse[K + i]);
+      const double u = uniform01(seed, 1u, static_cast<unsigned>(i), static_cast<unsigned>(b));
+      keep = u * q < p;
+    }
+    if (!keep) {
+      *resid = true;
+      return i;
+    }
+  }
+  *resid = false;
+  return K;
+}
+
+// Pass 2: per (chunk, request), the deciding row's chunk sums of the
+// residual weights and of the target probabilities (the fallback when the
+// residual vanishes).
+__global__ __launch_bounds__(kThreads) void chunk_sum_kernel(const int32_t* cand, const float* draft,
+                                                             const float* target, const Lse* part, int B, int K,
+                                                             int V, double invT, unsigned long long seed,
+                                                             double* csum) {
+  __shared__ double lse[kMaxRows];
+  __shared__ double shr[kThreads / 64], shp[kThreads / 64];
+  __shared__ int di;
+  __shared__ int dres;
+  const int c = blockIdx.x, b = blockIdx.y;
+  request_lse(part, b, B, K, lse);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bool r = false;
+    di = decide(cand, draft, target, lse, b, K, V, invT, seed, &r);
+    dres = r;
+  }
+  __syncthreads();
+  const int i = di;
+  const bool res = dres != 0;
+  const float* tp = target + (static_cast<long>(b) * (K + 1) + i) * V;
+  const float* dp = draft + (static_cast<long>(b) * K + (res ? i : 0)) * V;
+  const double lp = lse[K + i], lq = res ? lse[i] : 0.0;
+  const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
+  const int v1 = static_cast<int>(static_cast<long>(c + 1) * V / kSampleChunks);
+  double sr = 0.0, sp = 0.0;
+  for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kThreads) {
+    const double p = exp(static_cast<double>(tp[v]) * invT - lp);
+    sp += p;
+    if (res) {
+      const double q = exp(static_cast<double>(dp[v]) * invT - lq);
+      sr += p > q ? p - q : 0.0;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    sr += __shfl_xor(sr, o, kWave);
+    sp += __shfl_xor(sp, o, kWave);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { shr[wave] = sr; shp[wave] = sp; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tr = 0.0, tq = 0.0;
+    for (int w = 0; w < kThreads / 64; ++w) { tr += shr[w]; tq += shp[w]; }
+    csum[(static_cast<long>(b) * kSampleChunks + c) * 2] = tr;
+    csum[(static_cast<long>(b) * kSampleChunks + c) * 2 + 1] = tq;
+  }
+}
+
+// Pass 3: per request, the chunk whose running range holds the draw, then
+// the index inside it: each thread a contiguous piece of the chunk, the
+// pieces' sums scanned in thread order, the piece holding the draw rescanned.
+__global__ __launch_bounds__(kThreads) void pick_kernel(const int32_t* cand, const float* draft,
+                                                        const float* target, const Lse* part,
+                                                        const double* csum, int B, int K, int V, double invT,
+                                                        unsigned long long seed, int32_t* A_out,
+                                                        int32_t* next_out) {
+  __shared__ double lse[kMaxRows];
+  __shared__ double pre[kThreads + 1];
+  __shared__ int di, dres, chunk;
+  __shared__ double tloc;
+  const int b = blockIdx.x;
+  request_lse(part, b, B, K, lse);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bool r = false;
+    const int i = decide(cand, draft, target, lse, b, K, V, invT, seed, &r);
+    const double* cs = csum + static_cast<long>(b) * kSampleChunks * 2;
+    double Z = 0.0;
+    for (int c = 0; c < kSampleChunks; ++c) Z += cs[c * 2 + (r ? 0 : 1)];
+    if (r && !(Z > 0.0)) {   // the residual vanishes (p == q): draw from p
+      r = false;
+      Z = 0.0;
+      for (int c = 0; c < kSampleChunks; ++c) Z += cs[c * 2 + 1];
+    }
+    const int sel = r ? 0 : 1;
+    const double t = uniform01(seed, 2u, static_cast<unsigned>(i), static_cast<unsigned>(b)) * Z;
+    double run = 0.0;
+    int ch = -1, lastpos = 0;
+    for (int c = 0; c < kSampleChunks; ++c) {
+      const double x = cs[c * 2 + sel];
+      if (x > 0.0) lastpos = c;
+      if (ch < 0 && t < run + x) { ch = c; tloc = t - run; }
+      run += x;
+    }
+    if (ch < 0) { ch = lastpos; tloc = cs[ch * 2 + sel]; }   // rounding past the end: the last chunk with mass
+    di = i;
+    dres = r;
+    chunk = ch;
+    A_out[b] = i;
+  }
+  __syncthreads();
+  const int i = di;
+  const bool res = dres != 0;
+  const float* tp = target + (static_cast<long>(b) * (K + 1) + i) * V;
+  const float* dp = draft + (static_cast<long>(b) * K + (res ? i : 0)) * V;
+  const double lp = lse[K + i], lq = res ? lse[i] : 0.0;
+  auto weight = [&](int v) {
+    const double p = exp(static_cast<double>(tp[v]) * invT - lp);
+    if (!res) return p;
+    const double q = exp(static_cast<double>(dp[v]) * invT - lq);
+    return p > q ? p - q : 0.0;
+  };
+  const int c = chunk;
+  const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
+  const int v1 = static_cast<int>(static_cast<long>(c + 1) * V / kSampleChunks);
+  const int per = (v1 - v0 + kThreads - 1) / kThreads;
+  const int a0 = v0 + static_cast<int>(threadIdx.x) * per;
+  const int a1 = a0 + per < v1 ? a0 + per : v1;
+  double mine = 0.0;
+  for (int v = a0; v < a1; ++v) mine += weight(v);
+  pre[threadIdx.x + 1] = mine;
+  if (threadIdx.x == 0) pre[0] = 0.0;
+  __syncthreads();
+  // inclusive scan of pre[1..kThreads] (Hillis-Steele, fixed order)
+  for (int o = 1; o < kThreads; o <<= 1) {
+    const double add = static_cast<int>(threadIdx.x) >= o ? pre[threadIdx.x + 1 - o] : 0.0;
+    __syncthreads();
+    pre[threadIdx.x + 1] += add;
+    __syncthreads();
+  }
+  const double total = pre[kThreads];
+  double t = tloc;
+  if (!(t < total)) t = nextafter(total, 0.0);   // rounding between the two sums of the chunk
+  const double lo = pre[threadIdx.x], hi = pre[threadIdx.x + 1];
+  if (lo <= t && t < hi) {
+    double run = lo;
+    int pick = -1, lastpos = a0;
+    for (int v = a0; v < a1; ++v) {
+      const double w = weight(v);
+      if (w > 0.0) lastpos = v;
+      run += w;
+      if (run > t) { pick = v; break; }
+    }
+    next_out[b] = pick >= 0 ? pick : lastpos;
+  }
+}
+
+}  // namespace
+
+size_t sampling_scratch_bytes(long rows) {
+  // partials of every row, then two chunk sums per chunk of at most `rows`
+  // requests (accept: rows = B (2K + 1) >= B)
+  return static_cast<size_t>(rows) * kSampleChunks * 16 * 2;
+}
+
+hipError_t launch_sample_tokens(const float* logits, int N, int V, float T, unsigned long long seed,
+                                unsigned stream, int32_t* tokens, void* scratch, hipStream_t st) {
+  Best* part = static_cast<Best*>(scratch);
+  hipLaunchKernelGGL(sample_partial_kernel, dim3(kSampleChunks, N), dim3(kThreads), 0, st, logits, V,
+                     1.0 / static_cast<double>(T), seed, stream, part);
+  hipLaunchKernelGGL(sample_final_kernel, dim3((N + 63) / 64), dim3(64), 0, st, part, N, tokens);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_sampled(const int32_t* cand, const float* draft, const float* target, int B, int K, int V,
+                                 float T, unsigned long long seed, int32_t* A, int32_t* next, void* scratch,
+                                 hipStream_t st) {
+  if (K > 64) return hipErrorInvalidValue;
+  Lse* part = static_cast<Lse*>(scratch);
+  double* csum = reinterpret_cast<double*>(part + static_cast<long>(B) * (2 * K + 1) * kSampleChunks);
+  const double invT = 1.0 / static_cast<double>(T);
+  hipLaunchKernelGGL(lse_partial_kernel, dim3(kSampleChunks, B * (2 * K + 1)), dim3(kThreads), 0, st, draft,
+                     target, B * K, V, invT, part);
+  hipLaunchKernelGGL(chunk_sum_kernel, dim3(kSampleChunks, B), dim3(kThreads), 0, st, cand, draft, target, part, B,
+                     K, V, invT, seed, csum);
+  hipLaunchKernelGGL(pick_kernel, dim3(B), dim3(kThreads), 0, st, cand, draft, target, part, csum, B, K, V, invT,
+                     seed, A, next);
+  return hipGetLastError();
+}
+
+}  // namespace dlite

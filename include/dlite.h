@@ -257,6 +257,63 @@ int dlite_accept_prefix(const int32_t *candidates, const int32_t *target_tokens,
                         int32_t *next_anchor, hipStream_t stream);
 
 /*
+ * Sampling at a positive temperature ([W] "贪心模式与随机模式要分别说明").
+ *
+ * Random numbers come from Philox4x32-10 (Salmon et al., "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011): the uniform for counter
+ * (a, b, stream, 0) under key (seed low 32 bits, seed high 32 bits) is
+ * (x0 + 1/2) / 2^32.  The same (seed, stream) always gives the same draws.
+ * Probabilities are evaluated in fp64 from the fp32 logits scaled by
+ * 1 / (double)temperature.
+ *
+ * dlite_sampling_workspace_bytes(rows): scratch for rows = N of
+ * dlite_sample_tokens or rows = B (2K + 1) of dlite_accept_sampled; 0 with an
+ * error for rows < 1.
+ */
+size_t dlite_sampling_workspace_bytes(int32_t rows);
+
+/*
+ * dlite_sample_tokens — one token per row drawn from softmax(logits / T):
+ * tokens[n] = argmax_v (logits[n, v] / T - log(-log u(v, n))), u from counter
+ * (v, n, stream_id) (the Gumbel-max rule; ties to the lowest index).  With the
+ * draft's logits (taps.logits of dlite_draft_block, rows b K + i) it samples
+ * the candidates; with the target's logits it gives match mode's target
+ * tokens (then dlite_accept_prefix applies the greedy prefix rule).
+ *
+ * logits [N, V] fp32 (device); N in 1 .. 65535; temperature > 0 and finite;
+ * tokens [N] int32 (out); workspace: dlite_sampling_workspace_bytes(N) bytes,
+ * 16-byte aligned.
+ */
+int dlite_sample_tokens(const float *logits, int32_t N, int32_t V, float temperature, uint64_t seed,
+                        uint32_t stream_id, int32_t *tokens, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * dlite_accept_sampled — speculative rejection sampling of one round.
+ *
+ * With p_i = softmax(target_logits[b, i] / T), q_i = softmax(draft_logits[b,
+ * i] / T) and d_i = candidates[b, i] (drawn from q_i): for i = 0, 1, .. the
+ * candidate is kept when u q_i(d_i) < p_i(d_i), u from counter (i, b, 1); at
+ * the first rejection next_token is drawn from the normalised residual
+ * [p_i - q_i]_+ (from p_i if that vanishes), else, after K acceptances, from
+ * p_K (the target's distribution after the last candidate); the draw is the
+ * inverse CDF at u from counter (i, b, 2).  accept_len[b] = number kept, so
+ * the committed token at every position is distributed as the target's
+ * ([W]: the accepted mass min(p, q) plus the residual mass [p - q]_+ is p).
+ * A candidate outside [0, V) is rejected.
+ *
+ * candidates [B, K] int32; draft_logits [B, K, V] fp32 (the logits the
+ * candidates were drawn from); target_logits [B, K + 1, V] fp32 (the
+ * target's at the verify inputs [a, d_1 .. d_K]); K in 1 .. 64;
+ * accept_len, next_token [B] int32 (out); workspace:
+ * dlite_sampling_workspace_bytes(B (2K + 1)) bytes, 16-byte aligned.
+ */
+int dlite_accept_sampled(const int32_t *candidates, const float *draft_logits, const float *target_logits,
+                         int32_t B, int32_t K, int32_t V, float temperature, uint64_t seed,
+                         int32_t *accept_len, int32_t *next_token, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
  * Instrumentation for timing one stage of the draft step with HIP events.
  * After this call, every dlite_draft_block call made from the same thread
  * records `before` on its stream immediately before the first kernel of

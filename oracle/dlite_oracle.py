@@ -393,6 +393,8 @@ def sample_tokens(logits: np.ndarray, T: float, seed: int, stream: int):
     u = uniform01(seed, stream, v, n)
     score = x / T - np.log(-np.log(u))
     tok = np.argmax(score, axis=1)
+    if V == 1:   # a single token: no runner-up
+        return tok.astype(np.int64), np.full(N, np.inf)
     top2 = np.partition(score, -2, axis=1)[:, -2:]
     return tok.astype(np.int64), top2[:, 1] - top2[:, 0]
 

@@ -313,3 +313,20 @@ def make_target_tokens(w: Workload, cand: np.ndarray, c: Optional[np.ndarray] = 
     t[:, :K] = np.where(hit, cand, other)
     t[:, K] = rng.integers(0, w.vocab, size=B)
     return t.astype(np.int32)
+
+
+def make_sampling_case(seed: int, B: int, K: int, V: int, scale: float = 2.0, mix: float = 0.7):
+    """Logits for sampling tests: draft [B, K, V] and target [B, K + 1, V] fp32.
+
+    Draft rows ~ scale * N(0, 1); target rows at the candidate positions are
+    mix * draft + sqrt(1 - mix^2) * scale * N(0, 1) (overlapping but different
+    distributions, so both acceptances and rejections occur); the target's
+    last row is independent.
+    """
+    rng = np.random.default_rng(seed)
+    draft = (scale * rng.standard_normal((B, K, V))).astype(np.float32)
+    target = np.empty((B, K + 1, V), dtype=np.float32)
+    noise = scale * rng.standard_normal((B, K + 1, V))
+    target[:, :K] = mix * draft + np.sqrt(1.0 - mix * mix) * noise[:, :K]
+    target[:, K] = noise[:, K]
+    return draft, target

@@ -142,6 +142,25 @@ def test_draft_block_gated_validation_codes():
                                        fake, fake, fake, None, None, fake, need - 1, None) == -4
 
 
+def test_sampling_validation_codes():
+    lib = B.load_library()
+    f, ws = 0x300000, 0x400000
+    need = B.dlite_sampling_workspace_bytes(7)
+    assert lib.dlite_sample_tokens(None, 7, 10, 1.0, 1, 0, f, ws, need, None) == -1
+    assert lib.dlite_sample_tokens(f, 7, 10, 1.0, 1, 0, None, ws, need, None) == -1
+    assert lib.dlite_sample_tokens(f, 0, 10, 1.0, 1, 0, f, ws, need, None) == -2
+    assert lib.dlite_sample_tokens(f, 7, 10, 0.0, 1, 0, f, ws, need, None) == -2
+    assert lib.dlite_sample_tokens(f, 7, 10, float("nan"), 1, 0, f, ws, need, None) == -2
+    assert lib.dlite_sample_tokens(f, 7, 10, 1.0, 1, 0, f, ws + 8, need, None) == -5
+    assert lib.dlite_sample_tokens(f, 7, 10, 1.0, 1, 0, f, ws, need - 1, None) == -4
+    need2 = B.dlite_sampling_workspace_bytes(4 * 15)
+    assert lib.dlite_accept_sampled(f, f, f, 4, 7, 10, 1.0, 1, f, None, ws, need2, None) == -1
+    assert lib.dlite_accept_sampled(f, f, f, 4, 65, 10, 1.0, 1, f, f, ws, need2, None) == -2
+    assert lib.dlite_accept_sampled(f, f, f, 4, 7, 10, -1.0, 1, f, f, ws, need2, None) == -2
+    assert lib.dlite_accept_sampled(f, f, f, 4, 7, 10, 1.0, 1, f, f, ws, need2 - 1, None) == -4
+    assert B.load_library().dlite_sampling_workspace_bytes(0) == 0
+
+
 def test_accept_validation_codes():
     lib = B.load_library()
     f = 0x300000
