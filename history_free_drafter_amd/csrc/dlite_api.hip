@@ -127,7 +127,10 @@ Plan make_plan(const dlite_dims& d) {
   p.AO = take(B * L * Hq * es);
   p.ACT = take(B * L * F * es);
   p.P = take(B * K * r * 4);
-  p.U = take(scan_scratch_floats(d.B, d.rank) * 4);
+  // scan exchange slots, then (fused head) the helpers' tagged words: both
+  // zeroed by the feature kernel
+  p.U = take(scan_scratch_floats(d.B, d.rank) * 4 +
+             (seqhead_fused(d.B, d.K, d.rank, d.dtype == DLITE_BF16) ? seqhead_fold_bytes(d.B * d.K) : 0));
   p.Sf = take(B * K * r * 4);
   p.Sb = take(B * K * r * es);
   p.GR = take(B * r * es);        // gated head: r_i of the current step
@@ -297,7 +300,8 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   fa.anchors = anchor_ids; fa.X = X; fa.XB = XB; fa.ssq = SSQ; fa.tap_z = tp.z;
   fa.counters = counters; fa.n_counters = counter_words();
   fa.clear = reinterpret_cast<uint4*>(U);
-  fa.n_clear = static_cast<long>(scan_scratch_floats(B, r) * sizeof(float) / 16);
+  const size_t fold_bytes = seqhead_fused(B, K, r, bf16) ? seqhead_fold_bytes(B * K) : 0;
+  fa.n_clear = static_cast<long>((scan_scratch_floats(B, r) * sizeof(float) + fold_bytes) / 16);
   fa.B = B; fa.m = m; fa.K = K; fa.D = D; fa.V = d.vocab; fa.n_layers = d.n_layers;
   fa.eps = d.rms_eps;
   DLITE_LAUNCH(mark(DLITE_STAGE_FEATURES, true, st));
@@ -453,7 +457,10 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
     }
   } else if (seqhead_fused(B, K, r, bf16)) {
     DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
-    DLITE_LAUNCH(launch_seqhead(sa, la, st));
+    DLITE_LAUNCH(launch_seqhead(sa, la,
+                                reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(U) +
+                                                            scan_scratch_floats(B, r) * sizeof(float)),
+                                st));
     DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, true, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, false, st));

@@ -190,7 +190,9 @@ int lmhead_groups(int V);
 // kFuseMaxHelpers partials per token in LmArgs::part_max / part_idx.
 constexpr int kFuseMaxHelpers = 1024;
 bool seqhead_fused(int B, int K, int r, bool bf16);
-hipError_t launch_seqhead(const ScanArgs& s, const LmArgs& l, hipStream_t st);
+// px: seqhead_fold_bytes(B K) of zeroed scratch (the helpers' tagged words).
+size_t seqhead_fold_bytes(int M);
+hipError_t launch_seqhead(const ScanArgs& s, const LmArgs& l, uint64_t* px, hipStream_t st);
 
 // ------------------------------------------------- gated sequential head ----
 constexpr int kGatedMaxRank = 512;

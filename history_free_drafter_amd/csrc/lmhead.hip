@@ -350,7 +350,65 @@ struct FuseArgs {
   LmArgs la;
   int nteam;        // scan teams (one request each): blocks xq * 8 + t, t < nteam, xq < team size
   unsigned* done;   // published-state counter of the team members
+  uint64_t* px;     // [M, G] tagged (max, index) words of the helpers (zero at launch)
 };
+
+// A helper's (max, index) for one token as one word: the value's bits in the
+// high half, the index in the low 24 bits, a tag (1) in the top 8 bits of
+// the low half; a zeroed slot has tag 0.
+__device__ __forceinline__ uint64_t pack_best(float v, int i) {
+  return (static_cast<uint64_t>(__float_as_uint(v)) << 32) | (static_cast<uint32_t>(i) & 0xffffffu) | (1u << 24);
+}
+
+// Team workgroup q of nq folds tokens q, q + nq, ..: waits for the G words of
+// the token (bounded), folds them in index order per thread and then in
+// wave order (the result does not depend on arrival order), writes the
+// candidate.
+__device__ void fold_tokens(const FuseArgs& f, int q, int nq, int G, unsigned char* smem) {
+  const LmArgs& a = f.la;
+  unsigned* status = a.counters + CNT_STATUS;
+  float* rv = reinterpret_cast<float*>(smem);
+  int* ri = reinterpret_cast<int*>(rv + kWaves);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = q; t < a.M; t += nq) {
+    float v = -INFINITY;
+    int ix = 0x7fffffff;
+    for (int e = threadIdx.x; e < G; e += blockDim.x) {
+      const uint64_t* p = f.px + static_cast<long>(t) * G + e;
+      uint64_t w = scan_detail::ld_tagged(p);
+      unsigned spins = 0;
+      while (((static_cast<uint32_t>(w) >> 24) & 0xffu) != 1u) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > scan_detail::kSpinLimit) {
+          atomicOr(status, static_cast<unsigned>(STATUS_BARRIER_TIMEOUT));
+          break;
+        }
+        w = scan_detail::ld_tagged(p);
+      }
+      const float pv = __uint_as_float(static_cast<uint32_t>(w >> 32));
+      const int pi = static_cast<int>(static_cast<uint32_t>(w) & 0xffffffu);
+      if (better(pv, pi, v, ix)) { v = pv; ix = pi; }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float ov = __shfl_xor(v, o, kWave);
+      const int oi = __shfl_xor(ix, o, kWave);
+      if (better(ov, oi, v, ix)) { v = ov; ix = oi; }
+    }
+    if (lane == 0) { rv[wave] = v; ri[wave] = ix; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 1; w < kWaves; ++w)
+        if (better(rv[w], ri[w], v, ix)) { v = rv[w]; ix = ri[w]; }
+      const int b = t / a.K;
+      bool ok = a.anchors[b] >= 0 && a.anchors[b] < a.V;
+      if (a.pos) ok = ok && a.pos[b] >= 0 && a.pos[b] < a.pos_n;
+      a.cand[t] = ok ? ix : -1;
+      if (a.max_logit) a.max_logit[t] = ok ? v : 0.f;
+    }
+    __syncthreads();
+  }
+}
 
 template <int RK>   // k-steps of 32 (r / 32)
 __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
@@ -368,6 +426,9 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
   constexpr int kTeam = (RK * 32) % 256 == 0 ? 16 : 8;   // members per scan team (team_size(r, B), B <= 8)
   if (xq < kTeam && x < nteam) {
     scan_team<uint16_t, kTeam>(f.sa, reinterpret_cast<float*>(smem), x, xq, done);
+    // then the argmax of the tokens from the helpers' words
+    __syncthreads();
+    fold_tokens(f, x * kTeam + xq, kTeam * nteam, static_cast<int>(gridDim.x) - kTeam * nteam, smem);
     return;
   }
 
@@ -523,17 +584,10 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
     int i = si[0][threadIdx.x];
     for (int w = 1; w < kWaves; ++w)
       if (better(sv[w][threadIdx.x], si[w][threadIdx.x], v, i)) { v = sv[w][threadIdx.x]; i = si[w][threadIdx.x]; }
-    publish_partial(a, static_cast<long>(threadIdx.x) * G + h, v, i);
-  }
-  {
-    // helpers only: the team members of XCD x do not publish
-    int nx = 0, busy = 0;
-    for (int q = 0; q < 8; ++q) {
-      const int n = (static_cast<int>(gridDim.x) - q + 7) / 8 - (q < nteam ? kTeam : 0);
-      busy += n > 0;
-      if (q == static_cast<int>(blockIdx.x & 7)) nx = n;
-    }
-    reduce_if_last(a, G, &last, nx, busy);
+    // one word per token for the team to fold (a helper without tiles
+    // reports index 0 at -inf: never better)
+    __hip_atomic_store(f.px + static_cast<long>(threadIdx.x) * G + h, pack_best(v, i < V ? i : 0),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (touch == 0x9e3779b9u && M < 0) a.cand[0] = 0;   // keeps the touch loads
 }
@@ -954,7 +1008,9 @@ bool seqhead_fused(int B, int K, int r, bool bf16) {
   return lds + 2048 <= 160 * 1024;   // + static LDS of the kernel
 }
 
-hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, hipStream_t st) {
+size_t seqhead_fold_bytes(int M) { return static_cast<size_t>(M) * kFuseMaxHelpers * sizeof(uint64_t); }
+
+hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, uint64_t* px, hipStream_t st) {
   using namespace scan_detail;
   if (!seqhead_fused(s0.B, s0.K, s0.r, true) || l0.M != s0.B * s0.K || l0.tok0 != 0) return hipErrorInvalidValue;
   int dev = 0, cus = 0;
@@ -968,6 +1024,7 @@ hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, hipStream_t st) 
   f.sa.tag0 = 0;
   f.nteam = s0.B;
   f.done = s0.counters + counter_seq_done();
+  f.px = px;
   const int team = team_size(s0.r, s0.B);
   const int grid = cus > team * 8 ? cus : team * 8;
   f.la = l0;
