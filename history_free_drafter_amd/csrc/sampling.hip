@@ -91,16 +91,23 @@ __global__ __launch_bounds__(kThreads) void sample_partial_kernel(const float* l
   if (threadIdx.x == 0) part[static_cast<long>(n) * kSampleChunks + c] = b;
 }
 
-// Pass 2: the chunks of a row in order.
-__global__ __launch_bounds__(64) void sample_final_kernel(const Best* part, int N, int32_t* tokens) {
-  const int n = blockIdx.x * 64 + static_cast<int>(threadIdx.x);
+// Pass 2: the chunks of a row (one wave per row, a lane per chunk; the
+// (value, index) order makes the result independent of the reduction order).
+static_assert(kSampleChunks == 64, "one lane per chunk");
+__global__ __launch_bounds__(256) void sample_final_kernel(const Best* part, int N, int32_t* tokens) {
+  const int n = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
   if (n >= N) return;
-  Best b = part[static_cast<long>(n) * kSampleChunks];
-  for (int c = 1; c < kSampleChunks; ++c) {
-    const Best o = part[static_cast<long>(n) * kSampleChunks + c];
-    if (better_d(o.v, o.i, b.v, b.i)) b = o;
+  const int lane = threadIdx.x & 63;
+  const Best o = part[static_cast<long>(n) * kSampleChunks + lane];
+  double v = o.v;
+  int i = o.i;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const double ov = __shfl_xor(v, s, kWave);
+    const int oi = __shfl_xor(i, s, kWave);
+    if (better_d(ov, oi, v, i)) { v = ov; i = oi; }
   }
-  tokens[n] = b.i;
+  if (lane == 0) tokens[n] = i;
 }
 
 // log-sum-exp partials of l / T: (chunk maximum, sum of exp(x - maximum)).
@@ -160,14 +167,19 @@ __device__ void request_lse(const Lse* part, int b, int B, int K, double* lse) {
   }
 }
 
-// The acceptance tests in position order (one thread): the number kept, and
-// whether the deciding draw is from the residual (else from the target's
-// row K).
-__device__ int decide(const int32_t* cand, const float* draft, const float* target, const double* lse, int b,
-                      int K, int V, double invT, unsigned long long seed, bool* resid) {
-  for (int i = 0; i < K; ++i) {
+// The acceptance tests of all positions at once (wave 0, lane i tests
+// position i; K <= 64), then the first rejection by a ballot: the number
+// kept, and whether the deciding draw is from the residual (else from the
+// target's row K).  Result in *out_i / *out_res (shared), valid after a
+// barrier.
+__device__ void decide(const int32_t* cand, const float* draft, const float* target, const double* lse, int b,
+                       int K, int V, double invT, unsigned long long seed, int* out_i, int* out_res) {
+  if (threadIdx.x >= 64) return;
+  const int i = static_cast<int>(threadIdx.x);
+  bool keep = true;
+  if (i < K) {
     const int d = cand[static_cast<long>(b) * K + i];
-    bool keep = false;
+    keep = false;
     if (d >= 0 && d < V) {
       const double q = exp(static_cast<double>(draft[(static_cast<long>(b) * K + i) * V + d]) * invT - lse[i]);
       const double p =
@@ -175,13 +187,13 @@ __device__ int decide(const int32_t* cand, const float* draft, const float* targ
       const double u = uniform01(seed, 1u, static_cast<unsigned>(i), static_cast<unsigned>(b));
       keep = u * q < p;
     }
-    if (!keep) {
-      *resid = true;
-      return i;
-    }
   }
-  *resid = false;
-  return K;
+  const unsigned long long rejected = __ballot(!keep);
+  if (i == 0) {
+    const int first = rejected ? __builtin_ctzll(rejected) : K;
+    *out_i = first < K ? first : K;
+    *out_res = first < K;
+  }
 }
 
 // Pass 2: per (chunk, request), the deciding row's chunk sums of the
@@ -198,11 +210,7 @@ __global__ __launch_bounds__(kThreads) void chunk_sum_kernel(const int32_t* cand
   const int c = blockIdx.x, b = blockIdx.y;
   request_lse(part, b, B, K, lse);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    bool r = false;
-    di = decide(cand, draft, target, lse, b, K, V, invT, seed, &r);
-    dres = r;
-  }
+  decide(cand, draft, target, lse, b, K, V, invT, seed, &di, &dres);
   __syncthreads();
   const int i = di;
   const bool res = dres != 0;
@@ -251,32 +259,40 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(const int32_t* cand, con
   const int b = blockIdx.x;
   request_lse(part, b, B, K, lse);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    bool r = false;
-    const int i = decide(cand, draft, target, lse, b, K, V, invT, seed, &r);
+  decide(cand, draft, target, lse, b, K, V, invT, seed, &di, &dres);
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    // wave 0, lane = chunk: the chunk sums scanned in chunk order, the chunk
+    // holding the draw found by a ballot
+    const int lane = static_cast<int>(threadIdx.x);
+    const int i = di;
     const double* cs = csum + static_cast<long>(b) * kSampleChunks * 2;
-    double Z = 0.0;
-    for (int c = 0; c < kSampleChunks; ++c) Z += cs[c * 2 + (r ? 0 : 1)];
-    if (r && !(Z > 0.0)) {   // the residual vanishes (p == q): draw from p
-      r = false;
-      Z = 0.0;
-      for (int c = 0; c < kSampleChunks; ++c) Z += cs[c * 2 + 1];
-    }
-    const int sel = r ? 0 : 1;
+    const double xr = cs[lane * 2], xp = cs[lane * 2 + 1];
+    auto scan = [&](double x) {   // inclusive, fixed order
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+      }
+      return x;
+    };
+    const double ir = scan(xr), ip = scan(xp);
+    bool r = dres != 0;
+    double Z = __shfl(ir, 63, kWave);
+    if (r && !(Z > 0.0)) r = false;   // the residual vanishes (p == q): draw from p
+    const double incl = r ? ir : ip, x = r ? xr : xp;
+    Z = __shfl(incl, 63, kWave);
     const double t = uniform01(seed, 2u, static_cast<unsigned>(i), static_cast<unsigned>(b)) * Z;
-    double run = 0.0;
-    int ch = -1, lastpos = 0;
-    for (int c = 0; c < kSampleChunks; ++c) {
-      const double x = cs[c * 2 + sel];
-      if (x > 0.0) lastpos = c;
-      if (ch < 0 && t < run + x) { ch = c; tloc = t - run; }
-      run += x;
+    const unsigned long long hit = __ballot(t < incl && x > 0.0);
+    const unsigned long long pos = __ballot(x > 0.0);
+    // rounding past the end: the last chunk with mass, drawn at its top
+    const int ch = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : 0);
+    if (lane == ch) tloc = hit ? fmax(t - (incl - x), 0.0) : x;
+    if (lane == 0) {
+      dres = r;
+      chunk = ch;
+      A_out[b] = i;
     }
-    if (ch < 0) { ch = lastpos; tloc = cs[ch * 2 + sel]; }   // rounding past the end: the last chunk with mass
-    di = i;
-    dres = r;
-    chunk = ch;
-    A_out[b] = i;
   }
   __syncthreads();
   const int i = di;
@@ -338,7 +354,7 @@ hipError_t launch_sample_tokens(const float* logits, int N, int V, float T, unsi
   Best* part = static_cast<Best*>(scratch);
   hipLaunchKernelGGL(sample_partial_kernel, dim3(kSampleChunks, N), dim3(kThreads), 0, st, logits, V,
                      1.0 / static_cast<double>(T), seed, stream, part);
-  hipLaunchKernelGGL(sample_final_kernel, dim3((N + 63) / 64), dim3(64), 0, st, part, N, tokens);
+  hipLaunchKernelGGL(sample_final_kernel, dim3((N + 3) / 4), dim3(256), 0, st, part, N, tokens);
   return hipGetLastError();
 }
 
