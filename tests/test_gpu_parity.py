@@ -103,10 +103,12 @@ def _compare(w, gpu, ref, check_taps=True):
 def _small(name, **kw):
     base = dict(B=2, m=3, D=128, n_layers=2, n_q=4, n_kv=2, d_h=64, ffn=96, K=5,
                 rank=32, vocab=1000, seed=11, dtype="bf16")
+    std = kw.pop("weight_std", None)
     base.update(kw)
-    w = custom(name=name, **base)
-    # O(1) activations at small widths: weights ~ N(0, 1/D)
-    return custom(name=name, **{**base, "weight_std": 1.0 / np.sqrt(base["D"])})
+    # O(1) activations at small widths: weights ~ N(0, 1/D) unless given (a
+    # rank-512 fixed recurrence over many steps needs smaller weights to stay
+    # bounded)
+    return custom(name=name, **{**base, "weight_std": std or 1.0 / np.sqrt(base["D"])})
 
 
 SMALL = [
@@ -141,6 +143,13 @@ SMALL = [
     # the exchange slots with step tags offset past the first launch's
     _small("scan_chunks_bf16", B=300, m=1, D=64, n_q=1, n_kv=1, ffn=32, K=2, rank=32,
            vocab=200, n_layers=1),
+    # the fused scan + vocabulary kernel with two scan teams (12 tokens folded
+    # by 32 team workgroups) and, for the gated head, the fused launch with
+    # several requests
+    _small("fused_two_teams_bf16", B=2, m=3, D=64, n_q=1, n_kv=1, ffn=32, K=6, rank=512,
+           vocab=3001, n_layers=1, weight_std=0.04),
+    _small("fused_gated_b6_bf16", B=6, m=2, D=64, n_q=1, n_kv=1, ffn=32, K=2, rank=512,
+           vocab=2500, n_layers=1, weight_std=0.07),
 ]
 
 
@@ -256,7 +265,8 @@ def _check_gated(w, gpu, h, anchors, head, rows=None):
 
 
 @pytest.mark.parametrize("key", ["small_bf16", "small_f32", "batch40_bf16", "k16_m64_bf16",
-                                 "rank512_bf16", "tiled_k64_bf16", "batch5_f32"])
+                                 "rank512_bf16", "tiled_k64_bf16", "batch5_f32",
+                                 "fused_two_teams_bf16", "fused_gated_b6_bf16"])
 def test_gated_head_matches_oracle(key):
     _announce(f"gated {key}")
     w, weights, H, a, ref = _prepared(key)
