@@ -150,6 +150,10 @@ SMALL = [
            vocab=3001, n_layers=1, weight_std=0.04),
     _small("fused_gated_b6_bf16", B=6, m=2, D=64, n_q=1, n_kv=1, ffn=32, K=2, rank=512,
            vocab=2500, n_layers=1, weight_std=0.07),
+    # 14 tokens at rank 512 do not fit the fused kernel's LDS: the stand-alone
+    # scan with teams of 16 and the streaming vocabulary pass
+    _small("scan_team16_bf16", B=2, m=3, D=64, n_q=1, n_kv=1, ffn=32, K=7, rank=512,
+           vocab=3001, n_layers=1, weight_std=0.04),
 ]
 
 
