@@ -908,20 +908,20 @@ __global__ __launch_bounds__(kWaves * 64) void gatedhead_kernel(GatedFuseArgs f)
       }
     };
     // the register tiles hold nearly the whole register file: the state
-    // fragments are read from LDS four k-steps at a time (the empty asm with
+    // fragments are read from LDS two k-steps at a time (the empty asm with
     // a memory clobber keeps the compiler from hoisting all of them at once)
     {
       floatx4 acc[TR];
 #pragma unroll
       for (int q = 0; q < TR; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s0 = 0; s0 < RK; s0 += 4) {
+      for (int s0 = 0; s0 < RK; s0 += 2) {
         asm volatile("" ::: "memory");
-        uint4 b4[4];
+        uint4 b4[2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) b4[s] = bfrag(s0 + s);
+        for (int s = 0; s < 2; ++s) b4[s] = bfrag(s0 + s);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int q = 0; q < TR; ++q) acc[q] = mma_step(wr[q][s0 + s], b4[s], acc[q], uint16_t());
       }
@@ -933,16 +933,16 @@ __global__ __launch_bounds__(kWaves * 64) void gatedhead_kernel(GatedFuseArgs f)
       int toff = j * RK * 64 + lane;   // opaque: one base per tile, k-steps as immediate offsets
       asm volatile("" : "+v"(toff));
 #pragma unroll
-      for (int s0 = 0; s0 < RK; s0 += 4) {
+      for (int s0 = 0; s0 < RK; s0 += 2) {
         asm volatile("" ::: "memory");
-        uint4 af[4], b4[4];
+        uint4 af[2], b4[2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 2; ++s) {
           af[s] = lds_w[toff + (s0 + s) * 64];
           b4[s] = bfrag(s0 + s);
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mma_step(af[s], b4[s], acc, uint16_t());
+        for (int s = 0; s < 2; ++s) acc = mma_step(af[s], b4[s], acc, uint16_t());
       }
       take(tlds + j, acc);
     }
@@ -951,16 +951,16 @@ __global__ __launch_bounds__(kWaves * 64) void gatedhead_kernel(GatedFuseArgs f)
     for (int t = tstream + (kWaves - 1 - wave); t < t1; t += kWaves) {
       floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s0 = 0; s0 < RK; s0 += 4) {
+      for (int s0 = 0; s0 < RK; s0 += 2) {
         asm volatile("" ::: "memory");
-        uint4 nx[4], b4[4];
+        uint4 nx[2], b4[2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 2; ++s) {
           nx[s] = *reinterpret_cast<const uint4*>(frag_ptr(t, s0 + s));
           b4[s] = bfrag(s0 + s);
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mma_step(nx[s], b4[s], acc, uint16_t());
+        for (int s = 0; s < 2; ++s) acc = mma_step(nx[s], b4[s], acc, uint16_t());
       }
       take(t, acc);
     }
