@@ -302,6 +302,20 @@ def accept_prefix(cand: np.ndarray, target: np.ndarray):
     return A.astype(np.int64), nxt.astype(np.int64)
 
 
+def accept_window(cand: np.ndarray, target: np.ndarray, W: int):
+    """Greedy verification of a window of W inputs (anchor included).
+
+    [W] "草稿块长与验证块长不是一个参数": a verify window shorter than the
+    block still lets the drafter predict all K candidates; only the first
+    W - 1 are sent to the target and the tail is dropped.  cand [B, K];
+    target [B, W] (the target's tokens at the W window inputs).  Returns A
+    [B] in 0 .. W - 1 and the next anchor target[b, A].
+    """
+    cand = np.asarray(cand)
+    target = np.asarray(target)
+    return accept_prefix(cand[:, :W - 1], target[:, :W])
+
+
 def boundary_features(verify_hidden: np.ndarray, A: np.ndarray) -> np.ndarray:
     """The next round's boundary features, taken from the verify pass at index A.
 

@@ -98,6 +98,30 @@ def test_boundary_features_reject_out_of_range():
         oracle.boundary_features(vh, np.array([-1, 0]))
 
 
+@pytest.mark.parametrize("W", [1, 2, 4, 8])
+def test_verify_window_drops_the_tail(W):
+    """A window of W inputs verifies the first W - 1 of the K drafted
+    candidates (block 8 = anchor + 7 candidates: W = 8 is the full block)."""
+    rng = np.random.default_rng(W)
+    B, K = 500, 7
+    cand = rng.integers(0, 3, size=(B, K))
+    full_t = rng.integers(0, 3, size=(B, K + 1))
+    A, nxt = oracle.accept_window(cand, full_t[:, :W], W)
+    for b in range(B):   # first failure among the first W - 1, by scanning
+        a = next((i for i in range(W - 1) if cand[b, i] != full_t[b, i]), W - 1)
+        assert A[b] == a and nxt[b] == full_t[b, a]
+    # the dropped tail never matters
+    other = cand.copy()
+    other[:, W - 1:] = 99
+    A2, n2 = oracle.accept_window(other, full_t[:, :W], W)
+    np.testing.assert_array_equal(A2, A)
+    np.testing.assert_array_equal(n2, nxt)
+    if W == K + 1:
+        A3, n3 = oracle.accept_prefix(cand, full_t)
+        np.testing.assert_array_equal(A3, A)
+        np.testing.assert_array_equal(n3, nxt)
+
+
 def test_round_accounting():
     for row in golden("round_accounting.txt"):
         lhs, rhs = row.split(":")
