@@ -19,7 +19,7 @@ ERRORS = {-1: "DLITE_ERR_NULL", -2: "DLITE_ERR_SHAPE", -3: "DLITE_ERR_DTYPE",
           -4: "DLITE_ERR_WORKSPACE", -5: "DLITE_ERR_UNSUPPORTED", -6: "DLITE_ERR_HIP"}
 EXPORTS = ["dlite_workspace_bytes", "dlite_draft_block", "dlite_draft_block_at",
            "dlite_draft_block_gated", "dlite_sampling_workspace_bytes", "dlite_sample_tokens",
-           "dlite_accept_sampled",
+           "dlite_accept_sampled", "dlite_accept_window",
            "dlite_accept_prefix", "dlite_set_stage_events", "dlite_last_error", "dlite_version"]
 STAGES = ["features", "qkv", "attention", "oproj", "gate_up", "down", "final_norm",
           "seq_proj", "scan", "lm_head"]
@@ -83,6 +83,9 @@ def load_library(path: str = LIB_PATH):
                                          c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                          POINTER(DliteTaps), c_void_p, c_size_t, c_void_p]
     lib.dlite_draft_block_at.restype = c_int
+    lib.dlite_accept_window.argtypes = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p,
+                                        c_void_p, c_void_p]
+    lib.dlite_accept_window.restype = c_int
     lib.dlite_sampling_workspace_bytes.argtypes = [c_int32]
     lib.dlite_sampling_workspace_bytes.restype = c_size_t
     lib.dlite_sample_tokens.argtypes = [c_void_p, c_int32, c_int32, ctypes.c_float, ctypes.c_uint64,
@@ -208,6 +211,13 @@ def dlite_draft_block_at(dims, weights, verify_hidden, T, accept_len, anchor_ids
         ctypes.byref(taps) if taps is not None else None, _ptr(workspace), ws_bytes,
         _stream(stream))
     _check(rc)
+
+
+def dlite_accept_window(candidates, K, target_tokens, B, W, accept_len, next_anchor=None,
+                        stream=None):
+    """Enqueue greedy verification of a W-input window; see include/dlite.h."""
+    _check(load_library().dlite_accept_window(_ptr(candidates), K, _ptr(target_tokens), B, W,
+                                              _ptr(accept_len), _ptr(next_anchor), _stream(stream)))
 
 
 def dlite_sampling_workspace_bytes(rows: int) -> int:

@@ -10,15 +10,19 @@ namespace dlite {
 
 namespace {
 
+// K positions compared; candidate rows ldc apart, target rows ldt apart (a
+// verify window shorter than the drafted block compares only its first
+// candidates).
 __global__ __launch_bounds__(256) void accept_kernel(const int32_t* __restrict__ cand,
                                                      const int32_t* __restrict__ tgt,
-                                                     int B, int K, int32_t* __restrict__ A,
+                                                     int B, int K, int ldc, int ldt,
+                                                     int32_t* __restrict__ A,
                                                      int32_t* __restrict__ next) {
   constexpr int kChunk = 16;
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
-  const int32_t* c = cand + static_cast<long>(b) * K;
-  const int32_t* t = tgt + static_cast<long>(b) * (K + 1);
+  const int32_t* c = cand + static_cast<long>(b) * ldc;
+  const int32_t* t = tgt + static_cast<long>(b) * ldt;
   // positions are compared kChunk at a time: all loads of a chunk are issued
   // before any comparison, so a block costs one memory round trip, not K
   const int bonus = t[K];
@@ -54,8 +58,13 @@ __global__ __launch_bounds__(256) void accept_kernel(const int32_t* __restrict__
 
 hipError_t launch_accept(const int32_t* cand, const int32_t* tgt, int B, int K,
                          int32_t* A, int32_t* next, hipStream_t st) {
+  return launch_accept_window(cand, K, tgt, B, K + 1, A, next, st);
+}
+
+hipError_t launch_accept_window(const int32_t* cand, int K, const int32_t* tgt, int B, int W,
+                                int32_t* A, int32_t* next, hipStream_t st) {
   const dim3 block(256), grid((B + 255) / 256);
-  hipLaunchKernelGGL(accept_kernel, grid, block, 0, st, cand, tgt, B, K, A, next);
+  hipLaunchKernelGGL(accept_kernel, grid, block, 0, st, cand, tgt, B, W - 1, K, W, A, next);
   return hipGetLastError();
 }
 

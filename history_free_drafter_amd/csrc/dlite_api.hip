@@ -543,6 +543,18 @@ int dlite_draft_block_at(const dlite_dims* dims, const dlite_weights* w, const v
                     workspace_bytes, st);
 }
 
+int dlite_accept_window(const int32_t* candidates, int32_t K, const int32_t* target_tokens, int32_t B,
+                        int32_t W, int32_t* accept_len, int32_t* next_anchor, hipStream_t st) {
+  if (!candidates) return fail(DLITE_ERR_NULL, "candidates is NULL");
+  if (!target_tokens) return fail(DLITE_ERR_NULL, "target_tokens is NULL");
+  if (!accept_len) return fail(DLITE_ERR_NULL, "accept_len is NULL");
+  if (B < 1 || B > (1 << 24)) return fail(DLITE_ERR_SHAPE, "B=%d not in [1, 2^24]", B);
+  if (K < 1 || K > 64) return fail(DLITE_ERR_SHAPE, "K=%d not in [1, 64]", K);
+  if (W < 1 || W > K + 1) return fail(DLITE_ERR_SHAPE, "W=%d not in [1, K + 1 = %d]", W, K + 1);
+  DLITE_LAUNCH(launch_accept_window(candidates, K, target_tokens, B, W, accept_len, next_anchor, st));
+  return ok();
+}
+
 size_t dlite_sampling_workspace_bytes(int32_t rows) {
   if (rows < 1) {
     fail(DLITE_ERR_SHAPE, "rows=%d must be positive", rows);

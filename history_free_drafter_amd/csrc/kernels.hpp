@@ -241,6 +241,10 @@ hipError_t launch_accept_sampled(const int32_t* cand, const float* draft, const 
                                  hipStream_t st);
 
 // --------------------------------------------------------------- accept ----
+// Verify window of W inputs (anchor included, W <= K + 1): the first W - 1
+// of the K drafted candidates (rows K apart) against target rows of W.
+hipError_t launch_accept_window(const int32_t* cand, int K, const int32_t* tgt, int B, int W,
+                                int32_t* A, int32_t* next, hipStream_t st);
 hipError_t launch_accept(const int32_t* cand, const int32_t* tgt, int B, int K,
                          int32_t* A, int32_t* next, hipStream_t st);
 

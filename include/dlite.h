@@ -257,6 +257,24 @@ int dlite_accept_prefix(const int32_t *candidates, const int32_t *target_tokens,
                         int32_t *next_anchor, hipStream_t stream);
 
 /*
+ * dlite_accept_window — greedy verification of a window shorter than the
+ * drafted block.
+ *
+ * [W] "草稿块长与验证块长不是一个参数": the drafter predicts its whole block
+ * of K candidates, and a verify window of W inputs (anchor included) sends
+ * only the first W - 1 of them to the target; the rest are dropped.  A is the
+ * number of leading matches among those W - 1 (0 .. W - 1) and next_anchor
+ * the target token at verify index A.  W = K + 1 is dlite_accept_prefix.
+ *
+ * candidates    [B, K] int32 (rows of K; only the first W - 1 are read)
+ * target_tokens [B, W] int32 target greedy token at each of the W inputs
+ * K in 1 .. 64, W in 1 .. K + 1; accept_len [B] (out); next_anchor [B] (out,
+ * may be NULL).  Integer only; bit-exact.
+ */
+int dlite_accept_window(const int32_t *candidates, int32_t K, const int32_t *target_tokens, int32_t B,
+                        int32_t W, int32_t *accept_len, int32_t *next_anchor, hipStream_t stream);
+
+/*
  * Sampling at a positive temperature ([W] "贪心模式与随机模式要分别说明").
  *
  * Random numbers come from Philox4x32-10 (Salmon et al., "Parallel random

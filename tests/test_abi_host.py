@@ -161,6 +161,16 @@ def test_sampling_validation_codes():
     assert B.load_library().dlite_sampling_workspace_bytes(0) == 0
 
 
+def test_accept_window_validation_codes():
+    lib = B.load_library()
+    f = 0x300000
+    assert lib.dlite_accept_window(None, 7, f, 4, 8, f, None, None) == -1
+    assert lib.dlite_accept_window(f, 7, f, 4, 9, f, None, None) == -2
+    assert lib.dlite_accept_window(f, 7, f, 4, 0, f, None, None) == -2
+    assert lib.dlite_accept_window(f, 0, f, 4, 1, f, None, None) == -2
+    assert lib.dlite_accept_window(f, 7, f, 0, 8, f, None, None) == -2
+
+
 def test_accept_validation_codes():
     lib = B.load_library()
     f = 0x300000

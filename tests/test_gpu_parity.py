@@ -444,3 +444,20 @@ def test_accept_random_bit_exact(Bn, K):
     A_ref, nx_ref = oracle.accept_prefix(cand, tgt)
     np.testing.assert_array_equal(A, A_ref)
     np.testing.assert_array_equal(nx, nx_ref)
+
+
+@pytest.mark.parametrize("K,W", [(7, 8), (7, 5), (7, 1), (16, 9), (64, 33)])
+def test_accept_window_bit_exact(K, W):
+    _announce(f"accept window K={K} W={W}")
+    rng = np.random.default_rng(K * 100 + W)
+    Bn = 5000
+    cand = rng.integers(0, 3, size=(Bn, K)).astype(np.int32)
+    tgt = rng.integers(0, 3, size=(Bn, W)).astype(np.int32)
+    A_ref, n_ref = oracle.accept_window(cand, tgt, W)
+    c, t = torch.from_numpy(cand).cuda(), torch.from_numpy(tgt).cuda()
+    A = torch.full((Bn,), -7, dtype=torch.int32, device="cuda")
+    nx = torch.full((Bn,), -7, dtype=torch.int32, device="cuda")
+    B.dlite_accept_window(c, K, t, Bn, W, A, nx)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(A.cpu().numpy(), A_ref)
+    np.testing.assert_array_equal(nx.cpu().numpy(), n_ref)
