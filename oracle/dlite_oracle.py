@@ -440,6 +440,7 @@ def accept_sampled(cand: np.ndarray, draft_logits: np.ndarray, target_logits: np
     q = softmax(draft / T) in fp64; the acceptance test is u q(d) < p(d) with
     u = uniform01(seed, 1, i, b); the residual (or extra) draw is
     inverse_cdf(weights, uniform01(seed, 2, i, b)) at the deciding position i.
+    A candidate outside [0, V) is rejected at its position (READING).
     cand [B, K]; draft_logits [B, K, V]; target_logits [B, K + 1, V].
     Returns A [B], next token [B], and per request the margin of its last
     decision (for comparisons near a threshold).
@@ -456,11 +457,15 @@ def accept_sampled(cand: np.ndarray, draft_logits: np.ndarray, target_logits: np
             else:
                 q = softmax_t(draft_logits[b, i], T)
                 d = int(cand[b, i])
-                u = float(uniform01(seed, 1, i, b))
-                margin[b] = min(margin[b], abs(u * q[d] - p[d]) / max(p[d], q[d], 1e-300))
-                if u * q[d] < p[d]:
-                    A[b] += 1
-                    continue
+                # READING: a candidate that is no vocabulary index (the draft
+                # reports -1 for an invalid request) has no probability under
+                # q or p and is rejected at its position.
+                if 0 <= d < len(p):
+                    u = float(uniform01(seed, 1, i, b))
+                    margin[b] = min(margin[b], abs(u * q[d] - p[d]) / max(p[d], q[d], 1e-300))
+                    if u * q[d] < p[d]:
+                        A[b] += 1
+                        continue
                 w = np.maximum(p - q, 0.0)
                 if not (w > 0).any():
                     w = p

@@ -5,7 +5,7 @@ Philox counters make the draws identical, so tokens, accept lengths and
 next tokens must be equal, except where the oracle's decision lies within
 rounding of a threshold (top-two perturbed scores within 1e-9, or an
 acceptance / inverse-CDF comparison within 1e-9 relative): those cases are
-counted and must stay rare.
+counted, printed and must stay under 1% of the rows.
 """
 import numpy as np
 import pytest
@@ -40,7 +40,8 @@ def test_sample_tokens_match_oracle(N, V, T, seed):
     ref, gap = oracle.sample_tokens(logits, T, seed, 0)
     clear = gap > 1e-9
     np.testing.assert_array_equal(gpu[clear], ref[clear])
-    assert clear.mean() > 0.9
+    print(f"exempt rows {int((~clear).sum())} of {N}", flush=True)
+    assert (~clear).sum() <= 0.01 * N
     assert ((gpu >= 0) & (gpu < V)).all()
 
 
@@ -66,12 +67,15 @@ def test_accept_sampled_matches_oracle(Bn, K, V, T, seed):
     ref_c, gap = oracle.sample_tokens(draft.reshape(Bn * K, V), T, seed, 0)
     clear_c = (gap > 1e-9).reshape(Bn, K).all(axis=1)
     np.testing.assert_array_equal(cand[clear_c], ref_c.reshape(Bn, K)[clear_c])
+    print(f"exempt draft rows {int((~clear_c).sum())} of {Bn}", flush=True)
+    assert (~clear_c).sum() <= 0.01 * Bn
     A, nx = _accept_gpu(cand, draft, target, T, seed)
     ref = oracle.accept_sampled(cand, draft, target, T, seed)     # same candidates on both sides
     clear = ref["margin"] > 1e-9
     np.testing.assert_array_equal(A[clear], ref["A"][clear])
     np.testing.assert_array_equal(nx[clear], ref["next"][clear])
-    assert clear.mean() > 0.9
+    print(f"exempt requests {int((~clear).sum())} of {Bn}", flush=True)
+    assert (~clear).sum() <= 0.01 * Bn
     print("accepted", A.mean(), "rejections", (A < K).mean(), flush=True)
 
 
@@ -108,3 +112,24 @@ def test_match_mode_on_gpu():
     A_ref, nx_ref = oracle.accept_prefix(cand, tt)
     np.testing.assert_array_equal(A.cpu().numpy(), A_ref)
     np.testing.assert_array_equal(nx.cpu().numpy(), nx_ref)
+
+
+@pytest.mark.parametrize("bad", [-1, 5])
+def test_out_of_range_candidate_is_rejected_on_gpu(bad):
+    """Candidates -1 (the draft's mark of an invalid request) and V are
+    rejected at their position on both sides: with p = q every in-range
+    candidate is kept, so A is that position, and the next token equals the
+    oracle's draw from p at that row."""
+    V, K, n, T = 5, 4, 256, 1.0
+    rng = np.random.default_rng(8)
+    rows = rng.normal(size=(K + 1, V)).astype(np.float32)
+    draft = np.ascontiguousarray(np.tile(rows[:K], (n, 1, 1)))
+    target = np.ascontiguousarray(np.tile(rows, (n, 1, 1)))
+    cand = np.tile(np.array([1, 3, bad, 0], dtype=np.int32), (n, 1))
+    A, nx = _accept_gpu(cand, draft, target, T, 21)
+    ref = oracle.accept_sampled(cand, draft, target, T, 21)
+    assert (ref["A"] == 2).all()
+    np.testing.assert_array_equal(A, ref["A"])
+    clear = ref["margin"] > 1e-9
+    np.testing.assert_array_equal(nx[clear], ref["next"][clear])
+    assert (~clear).sum() <= 0.01 * n

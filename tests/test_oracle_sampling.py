@@ -125,3 +125,22 @@ def test_match_mode_passes_with_the_target_probability():
     A, _ = oracle.accept_prefix(cand, tgt)
     p2 = oracle.softmax_t(p_logits, T)[2]
     assert abs(A.mean() - p2) < 5 * np.sqrt(p2 * (1 - p2) / n)
+
+
+@pytest.mark.parametrize("bad", [-1, 5])
+def test_out_of_range_candidate_is_rejected(bad):
+    """A candidate that is no vocabulary index (the draft reports -1 for an
+    invalid request; V is one past the last index) is rejected at its
+    position.  With p = q every in-range candidate is kept (u q < p for every
+    u < 1), so A is exactly the out-of-range position, and the residual
+    [p - q]_+ vanishes, so the next token follows p at that row."""
+    V, K, n, T = 5, 4, 20000, 1.0
+    rng = np.random.default_rng(8)
+    rows = rng.normal(size=(K + 1, V))
+    draft = np.tile(rows[:K], (n, 1, 1))
+    target = np.tile(rows, (n, 1, 1))
+    cand = np.tile(np.array([1, 3, bad, 0]), (n, 1))
+    out = oracle.accept_sampled(cand, draft, target, T, seed=21)
+    assert (out["A"] == 2).all()
+    counts = np.bincount(out["next"], minlength=V)
+    assert stats.chisquare(counts, oracle.softmax_t(rows[2], T) * n).pvalue > 1e-4
