@@ -8,10 +8,13 @@ per second (B*K per step).  Weights are rotated over several device copies so
 that no step finds its weights in the 256 MB last-level cache (MALL) left
 behind by the previous step.
 
-Prints one JSON line.  Also reports, for the dominant kernel, the achieved
-bandwidth (or MFMA rate) from HIP events recorded around it on the library's
-stream during the timed steps, and the fp64 CPU oracle's throughput on a
-bounded sample of the same workload.
+Prints one JSON line.  The timed steps carry no instrumentation.  A separate
+pass then records HIP events around every stage (on the library's stream) to
+find the kernel that takes the most time; its achieved bandwidth (or MFMA
+rate) against the algorithmic bytes (flops) of one launch is the roofline
+entry, with the next two stages beside it.  Also the fp64 CPU oracle's
+throughput on a bounded sample of the same workload, and the draft step's
+status word (a nonzero word fails the run).
 """
 from __future__ import annotations
 
@@ -44,7 +47,6 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="time budget of the CPU oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--stages", action="store_true", help="also time every stage separately")
     p.add_argument("--temperature", type=float, default=0.0,
                    help="> 0: the candidates are drawn at this temperature from the draft's logits "
                         "and verified by rejection sampling against synthetic target logits")
@@ -52,8 +54,8 @@ def parse():
                    help="sequential head: the fixed token-free recurrence (one vocabulary "
                         "pass) or the walkthrough's gated head (one vocabulary pass per position)")
     p.add_argument("--kernel", default=None,
-                   help="stage whose roofline is reported (default: the one with the "
-                        "largest algorithmic time at peak)")
+                   help="stage whose roofline is reported (default: the stage that takes "
+                        "the most time in the per-stage event pass)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (5 times); "
                         "its HBM counters calibrate the kernel traffic figures")
@@ -107,11 +109,37 @@ def stage_reps(w, head="fixed"):
 
 
 def step_costs(w, head="fixed"):
+    """Algorithmic bytes and flops of one whole step: every weight byte once,
+    the boundary features, the anchor ids and their B token-table rows, the
+    target tokens read by accept and the outputs (candidates, winning logits,
+    A, next anchor).  Intermediate activations are not counted (they are
+    traffic the implementation adds, not work the step requires)."""
+    e = 2 if w.dtype == "bf16" else 4
+    B, m, K, D, r, V = w.B, w.m, w.K, w.D, w.rank, w.vocab
+    by = w.weight_bytes()            # includes the B token-table rows
+    if head == "gated":              # the gated head's weights replace the fixed head's
+        # E_R: the B K rows the fed-back tokens select; W_s, b_s, W_h, b_h, W_o
+        by += (-(r * (D + r) + r * r + V * r) + (B * K * r + 4 * r * r + 2 * r + r * (r + D) + r + V * r)) * e
+    by += B * m * D * e + B * 4                  # features, anchor ids
+    by += B * (K + 1) * 4                        # target tokens
+    by += B * K * (4 + 4) + B * 2 * 4            # candidates, max logits, A, next anchor
     c = stage_costs(w, head)
     reps = stage_reps(w, head)
-    by = sum(v[0] * reps.get(k, 1) for k, v in c.items()) + w.B * (w.K + (w.K + 1) + 2) * 4  # + accept
     fl = sum(v[1] * reps.get(k, 1) for k, v in c.items())
     return by, fl
+
+
+def seqhead_is_fused(w, head="fixed"):
+    """Whether the scan and the vocabulary pass run as one kernel (the
+    library's rule: bf16, B*K <= 16, B <= 8, rank 320 or 512)."""
+    return (head == "fixed" and w.dtype == "bf16" and w.B * w.K <= 16 and w.B <= 8
+            and w.rank in (320, 512))
+
+
+def gatedhead_is_fused(w, head="fixed"):
+    """Whether the gated head runs as one cooperative launch (the library's
+    rule on this chip: bf16, rank 512, 1..8 requests)."""
+    return head == "gated" and w.dtype == "bf16" and w.rank == 512 and 1 <= w.B <= 8
 
 
 # -------------------------------------------------------------- HBM traffic ---
@@ -315,12 +343,20 @@ def main():
     torch.cuda.synchronize()
 
     costs = stage_costs(w, args.head, layers=[0])   # what one timed launch group covers
-    # dominant kernel: the stage with the largest algorithmic time at peak
-    def t_roof(s):
-        return max(costs[s][0] / HBM_PEAK, costs[s][1] / MFMA_BF16_PEAK)
-    dom = args.kernel or max(costs, key=t_roof)
-    if dom not in costs:
-        raise SystemExit(f"unknown stage {dom}; stages: {sorted(costs)}")
+    fused = seqhead_is_fused(w, args.head)
+    if fused:   # one kernel: its stage events bracket both
+        costs["scan"] = [costs["scan"][0] + costs["lm_head"][0], costs["scan"][1] + costs["lm_head"][1]]
+        costs["lm_head"] = [0.0, 0.0]
+    kernel_names = {"scan": "seqhead_kernel (fused scan + vocabulary + argmax)"} if fused else {}
+    gfused = gatedhead_is_fused(w, args.head)
+    if gfused:   # all K positions in one launch; W_o and the head's weights read once
+        e_ = 2
+        per_pos = stage_costs(w, "gated")
+        costs["scan"] = [w.vocab * w.rank * e_ + (5 * w.rank * w.rank + 3 * w.rank) * e_
+                         + w.K * w.B * (w.rank * (e_ + 4 + 4 + 4 + e_) + 12),
+                         w.K * (per_pos["scan"][1] + per_pos["lm_head"][1])]
+        costs["lm_head"] = [0.0, 0.0]
+        kernel_names = {"scan": "gatedhead_kernel (fused gated head, all K positions)"}
     ev = HipEvents()
 
     def step(i):
@@ -341,52 +377,73 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    # the headline: K steps with no instrumentation inside the timed region
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g0.record()
     for i in range(args.steps):
-        B.dlite_set_stage_events(dom, pairs[i][0], pairs[i][1])
         step(i)
     g1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    B.dlite_set_stage_events(0, None, None)
     wall_s = t1 - t0
     gpu_ms = g0.elapsed_time(g1)
-    kern_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
-    for a, b in pairs:
-        ev.destroy(a)
-        ev.destroy(b)
+    status = model.status()
+    if status != 0:
+        raise SystemExit(f"draft status word {status:#x}: a bounded wait between workgroups timed out")
 
+    # a separate pass: HIP events around each stage (recorded by the library on
+    # its own stream), 20 steps per stage; per-layer stages time the first layer
+    print("[bench] per-stage events", file=sys.stderr, flush=True)
+    n_ev = max(20, min(args.steps, 50))
+    stage_us = {}
+    for si, name in enumerate(B.STAGES):
+        ps = [(ev.create(), ev.create()) for _ in range(n_ev)]
+        for i, (a, b) in enumerate(ps):
+            B.dlite_set_stage_events(si, a, b)
+            step(i)
+        torch.cuda.synchronize()
+        B.dlite_set_stage_events(0, None, None)
+        stage_us[name] = 1e3 * float(np.mean([ev.elapsed_ms(a, b) for a, b in ps]))
+        for a, b in ps:
+            ev.destroy(a)
+            ev.destroy(b)
+    if model.status() != 0:
+        raise SystemExit("draft status word nonzero in the per-stage pass")
+    # stages that launch nothing here (their events are recorded back to back)
+    if fused or gfused:
+        stage_us["lm_head"] = None          # inside the fused sequential-head kernel
+    stage_us["final_norm"] = None           # folded into the GEMMs (a kernel only for the fp32 tap)
+    stage_us = {k: v for k, v in stage_us.items() if v is not None}
+
+    def roof(st):
+        k_avg = stage_us[st] * 1e-6
+        bound = "hbm" if costs[st][0] / HBM_PEAK >= costs[st][1] / MFMA_BF16_PEAK else "mfma"
+        if bound == "hbm":
+            achieved, peak, unit = costs[st][0] / k_avg / 1e9, HBM_PEAK / 1e9, "GB/s"
+        else:
+            achieved, peak, unit = costs[st][1] / k_avg / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
+        traffic = traffic_record(w.name + ("+gated" if gated else ""), st)
+        return {"bound": bound, "kernel": kernel_names.get(st, st), "stage": st,
+                "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4),
+                "traffic": None if traffic is None else int(traffic),
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "avg_launch_us": round(stage_us[st], 2),
+                "algorithmic_bytes": int(costs[st][0]),
+                "algorithmic_flops": int(costs[st][1])}
+
+    # the dominant kernel is the stage that takes the most time (--kernel: another)
+    dom = args.kernel or max(stage_us, key=stage_us.get)
+    if dom not in costs:
+        raise SystemExit(f"unknown stage {dom}; stages: {sorted(costs)}")
+    others = [s_ for s_ in sorted(stage_us, key=stage_us.get, reverse=True) if s_ != dom][:2]
     ms_per_step = 1e3 * wall_s / args.steps
     value = w.B * w.K / (wall_s / args.steps)
-    k_avg = float(np.mean(kern_ms)) * 1e-3
-    bound = "hbm" if costs[dom][0] / HBM_PEAK >= costs[dom][1] / MFMA_BF16_PEAK else "mfma"
-    if bound == "hbm":
-        achieved, peak, unit = costs[dom][0] / k_avg / 1e9, HBM_PEAK / 1e9, "GB/s"
-    else:
-        achieved, peak, unit = costs[dom][1] / k_avg / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
     sb, sf = step_costs(w, args.head)
     step_s = wall_s / args.steps
-    traffic = traffic_record(w.name + ("+gated" if gated else ""), dom)
-
-    stages = None
-    if args.stages:
-        stages = {}
-        for si, name in enumerate(B.STAGES):
-            ps = [(ev.create(), ev.create()) for _ in range(20)]
-            for i, (a, b) in enumerate(ps):
-                B.dlite_set_stage_events(si, a, b)
-                step(i)
-            torch.cuda.synchronize()
-            B.dlite_set_stage_events(0, None, None)
-            stages[name] = round(1e3 * float(np.mean([ev.elapsed_ms(a, b) for a, b in ps])), 2)
-            for a, b in ps:
-                ev.destroy(a)
-                ev.destroy(b)
 
     # tau-hat of the accepted prefixes and spot parity of the last step's tokens
     A = model.accept_len.cpu().numpy()
@@ -410,18 +467,15 @@ def main():
                    "temperature": args.temperature,
                    "weight_copies": len(copies),
                    "parallelism": "single GPU"},
-        "roofline": {"bound": bound, "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": None if traffic is None else int(traffic),
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "avg_launch_us": round(k_avg * 1e6, 2),
-                     "algorithmic_bytes": int(costs[dom][0]),
-                     "algorithmic_flops": int(costs[dom][1])},
+        "roofline": roof(dom),
+        "roofline_next": [roof(s_) for s_ in others],
         "cpu_baseline": cpu,
         "step": {"algorithmic_bytes": int(sb), "algorithmic_flops": int(sf),
                  "hbm_frac": round(sb / step_s / HBM_PEAK, 4),
                  "mfma_frac": round(sf / step_s / MFMA_BF16_PEAK, 4),
                  "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4)},
+        "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "status": status,
         "tau_hat_last_step": float(np.mean(A + 1)),
     }
     if ref is not None and not sampled:
@@ -429,8 +483,6 @@ def main():
         if gated:   # a token differing at a near tie changes every later position
             clear = np.cumprod(clear, axis=1).astype(bool)
         out["parity_tokens_clear_margin"] = float((cand == ref["cand"])[clear].mean()) if clear.any() else None
-    if stages is not None:
-        out["stages_us"] = stages
     print(json.dumps(out))
 
 

@@ -20,7 +20,8 @@ ERRORS = {-1: "DLITE_ERR_NULL", -2: "DLITE_ERR_SHAPE", -3: "DLITE_ERR_DTYPE",
 EXPORTS = ["dlite_workspace_bytes", "dlite_draft_block", "dlite_draft_block_at",
            "dlite_draft_block_gated", "dlite_sampling_workspace_bytes", "dlite_sample_tokens",
            "dlite_accept_sampled", "dlite_accept_window",
-           "dlite_accept_prefix", "dlite_set_stage_events", "dlite_last_error", "dlite_version"]
+           "dlite_accept_prefix", "dlite_draft_status", "dlite_set_stage_events",
+           "dlite_last_error", "dlite_version"]
 STAGES = ["features", "qkv", "attention", "oproj", "gate_up", "down", "final_norm",
           "seq_proj", "scan", "lm_head"]
 
@@ -98,6 +99,8 @@ def load_library(path: str = LIB_PATH):
     lib.dlite_accept_prefix.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                                         c_void_p, c_void_p]
     lib.dlite_accept_prefix.restype = c_int
+    lib.dlite_draft_status.argtypes = [c_void_p, c_size_t, c_void_p, c_void_p]
+    lib.dlite_draft_status.restype = c_int
     lib.dlite_set_stage_events.argtypes = [c_int, c_void_p, c_void_p]
     lib.dlite_set_stage_events.restype = c_int
     lib.dlite_last_error.argtypes = []
@@ -252,6 +255,15 @@ def dlite_accept_prefix(candidates, target_tokens, B, K, accept_len, next_anchor
                                             _ptr(accept_len), _ptr(next_anchor),
                                             _stream(stream))
     _check(rc)
+
+
+def dlite_draft_status(workspace, status, workspace_bytes=None, stream=None):
+    """Enqueue a copy of the last draft step's status word into status[0] (device uint32/int32)."""
+    ws_bytes = workspace_bytes
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().dlite_draft_status(_ptr(workspace), ws_bytes, _ptr(status),
+                                             _stream(stream)))
 
 
 def dlite_set_stage_events(stage, before, after):

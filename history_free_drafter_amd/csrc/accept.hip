@@ -54,7 +54,18 @@ __global__ __launch_bounds__(256) void accept_kernel(const int32_t* __restrict__
   if (next) next[b] = nv;
 }
 
+// One lane: the status word of the last draft step that used the workspace.
+__global__ __launch_bounds__(64) void status_copy_kernel(const unsigned* __restrict__ word,
+                                                         uint32_t* __restrict__ out) {
+  if (threadIdx.x == 0) out[0] = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
+
+hipError_t launch_status_copy(const unsigned* word, uint32_t* out, hipStream_t st) {
+  launch_k(status_copy_kernel, dim3(1), dim3(64), 0, st, word, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_accept(const int32_t* cand, const int32_t* tgt, int B, int K,
                          int32_t* A, int32_t* next, hipStream_t st) {
@@ -64,7 +75,7 @@ hipError_t launch_accept(const int32_t* cand, const int32_t* tgt, int B, int K,
 hipError_t launch_accept_window(const int32_t* cand, int K, const int32_t* tgt, int B, int W,
                                 int32_t* A, int32_t* next, hipStream_t st) {
   const dim3 block(256), grid((B + 255) / 256);
-  hipLaunchKernelGGL(accept_kernel, grid, block, 0, st, cand, tgt, B, W - 1, K, W, A, next);
+  launch_k(accept_kernel, grid, block, 0, st, cand, tgt, B, W - 1, K, W, A, next);
   return hipGetLastError();
 }
 

@@ -225,11 +225,11 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t st) {
                                      static_cast<int>(sm));
   if (e != hipSuccess) return e;
   if (bf16) {
-    if (a.d_h == 128) hipLaunchKernelGGL((attention_kernel<uint16_t, 128>), grid, block, sm, st, a);
-    else hipLaunchKernelGGL((attention_kernel<uint16_t, 64>), grid, block, sm, st, a);
+    if (a.d_h == 128) launch_k((attention_kernel<uint16_t, 128>), grid, block, sm, st, a);
+    else launch_k((attention_kernel<uint16_t, 64>), grid, block, sm, st, a);
   } else {
-    if (a.d_h == 128) hipLaunchKernelGGL((attention_kernel<float, 128>), grid, block, sm, st, a);
-    else hipLaunchKernelGGL((attention_kernel<float, 64>), grid, block, sm, st, a);
+    if (a.d_h == 128) launch_k((attention_kernel<float, 128>), grid, block, sm, st, a);
+    else launch_k((attention_kernel<float, 64>), grid, block, sm, st, a);
   }
   return hipGetLastError();
 }

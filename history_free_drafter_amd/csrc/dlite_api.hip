@@ -20,11 +20,22 @@ struct StageEvents {
   hipEvent_t before = nullptr, after = nullptr;
 };
 thread_local StageEvents g_ev;
+thread_local StageTimer g_timer;
 
-// Records the instrumentation event for `stage` (layer 0 for per-layer stages).
+// Arms (begin) or disarms (end) the stage timer for `stage` (layer 0 for
+// per-layer stages): the launches in between carry the events.  A stage that
+// launched nothing records both events back to back.
 hipError_t mark(int stage, bool begin, hipStream_t st, int layer = 0) {
   if (g_ev.stage != stage || layer != 0) return hipSuccess;
-  return hipEventRecord(begin ? g_ev.before : g_ev.after, st);
+  if (begin) {
+    g_timer = StageTimer{g_ev.before, g_ev.after, true, false};
+    return hipSuccess;
+  }
+  const bool launched = g_timer.started;
+  g_timer = StageTimer{};
+  if (launched) return hipSuccess;
+  const hipError_t e = hipEventRecord(g_ev.before, st);
+  return e != hipSuccess ? e : hipEventRecord(g_ev.after, st);
 }
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -477,6 +488,10 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
 
 }  // namespace
 
+namespace dlite {
+StageTimer& stage_timer() { return g_timer; }
+}  // namespace dlite
+
 extern "C" {
 
 const char* dlite_last_error(void) { return g_err.c_str(); }
@@ -541,6 +556,18 @@ int dlite_draft_block_at(const dlite_dims* dims, const dlite_weights* w, const v
                          accept_len, T};
   return draft_impl(dims, w, fs, nullptr, anchor_ids, candidates, max_logit, taps, workspace,
                     workspace_bytes, st);
+}
+
+int dlite_draft_status(const void* workspace, size_t workspace_bytes, uint32_t* status, hipStream_t st) {
+  if (!workspace) return fail(DLITE_ERR_NULL, "workspace is NULL");
+  if (!status) return fail(DLITE_ERR_NULL, "status is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(DLITE_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+  // the counters are the workspace's first region in every plan
+  if (workspace_bytes < counter_words() * sizeof(unsigned))
+    return fail(DLITE_ERR_WORKSPACE, "workspace has %zu bytes, no draft step fits", workspace_bytes);
+  DLITE_LAUNCH(launch_status_copy(static_cast<const unsigned*>(workspace) + CNT_STATUS, status, st));
+  return ok();
 }
 
 int dlite_accept_window(const int32_t* candidates, int32_t K, const int32_t* target_tokens, int32_t B,

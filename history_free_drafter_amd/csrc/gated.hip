@@ -143,11 +143,11 @@ hipError_t launch_gated_step(const GatedArgs& a, bool bf16, hipStream_t st) {
   const size_t sm_state = static_cast<size_t>(kChunk) * 2 * a.R * sizeof(float);
   const size_t sm_out = static_cast<size_t>(kChunk) * a.R * sizeof(float);
   if (bf16) {
-    hipLaunchKernelGGL(gated_state_kernel<uint16_t>, grid, block, sm_state, st, a);
-    hipLaunchKernelGGL(gated_out_kernel<uint16_t>, grid, block, sm_out, st, a);
+    launch_k(gated_state_kernel<uint16_t>, grid, block, sm_state, st, a);
+    launch_k(gated_out_kernel<uint16_t>, grid, block, sm_out, st, a);
   } else {
-    hipLaunchKernelGGL(gated_state_kernel<float>, grid, block, sm_state, st, a);
-    hipLaunchKernelGGL(gated_out_kernel<float>, grid, block, sm_out, st, a);
+    launch_k(gated_state_kernel<float>, grid, block, sm_state, st, a);
+    launch_k(gated_out_kernel<float>, grid, block, sm_out, st, a);
   }
   return hipGetLastError();
 }

@@ -404,21 +404,21 @@ size_t plan_scratch_floats(const LaunchPlan& p, const GemmArgs* segs, int nseg, 
 }
 
 template <typename T, int MT, int KW, int NS, int EPI>
-hipError_t launch_k(const SArgs& sa, int G, size_t sm, hipStream_t st) {
+hipError_t launch_variant(const SArgs& sa, int G, size_t sm, hipStream_t st) {
   const void* fn = reinterpret_cast<const void*>(&gemm_stream_kernel<T, MT, KW, NS, EPI>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_stream_kernel<T, MT, KW, NS, EPI>), dim3(G), dim3(kWaves * 64), sm, st, sa);
+  launch_k((gemm_stream_kernel<T, MT, KW, NS, EPI>), dim3(G), dim3(kWaves * 64), sm, st, sa);
   return hipGetLastError();
 }
 
 template <typename T, int MT, int EPI>
 hipError_t launch_kw(const SArgs& sa, const LaunchPlan& p, size_t sm, hipStream_t st) {
-  if (p.KW == 4) return launch_k<T, MT, 4, 2, EPI>(sa, p.G, sm, st);
-  if (p.KW == 8) return launch_k<T, MT, 8, 4, EPI>(sa, p.G, sm, st);
-  if (p.KW == 16 && p.NS == 4) return launch_k<T, MT, 16, 4, EPI>(sa, p.G, sm, st);
+  if (p.KW == 4) return launch_variant<T, MT, 4, 2, EPI>(sa, p.G, sm, st);
+  if (p.KW == 8) return launch_variant<T, MT, 8, 4, EPI>(sa, p.G, sm, st);
+  if (p.KW == 16 && p.NS == 4) return launch_variant<T, MT, 16, 4, EPI>(sa, p.G, sm, st);
   if constexpr (MT == 1 && EPI != EPI_SWIGLU) {
-    if (p.KW == 16 && p.NS == 8) return launch_k<T, MT, 16, 8, EPI>(sa, p.G, sm, st);
+    if (p.KW == 16 && p.NS == 8) return launch_variant<T, MT, 16, 8, EPI>(sa, p.G, sm, st);
   }
   return hipErrorInvalidValue;
 }

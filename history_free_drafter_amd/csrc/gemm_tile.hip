@@ -458,7 +458,7 @@ hipError_t launch_tile_t(const TileArgs& ta, int items, hipStream_t st) {
   const int per_xcd = (items + 7) / 8;
   TileArgs t = ta;
   t.per_xcd = per_xcd;
-  hipLaunchKernelGGL((gemm_tile_kernel<EPI, MODE>), dim3(8 * per_xcd), dim3(MODE == MODE_REDUCE1 ? 64 : 256), sm, st, t);
+  launch_k((gemm_tile_kernel<EPI, MODE>), dim3(8 * per_xcd), dim3(MODE == MODE_REDUCE1 ? 64 : 256), sm, st, t);
   return hipGetLastError();
 }
 
@@ -472,7 +472,7 @@ hipError_t launch_tile_e(const TileArgs& ta, hipStream_t st) {
   if (ta.ksplit > kDirectSum) {
     // many slices: add them with the whole chip first, the epilogue pass reads one
     const long f4 = static_cast<long>(ta.total) * (kTileFloats / 4);
-    hipLaunchKernelGGL(slice_sum_kernel, dim3(static_cast<unsigned>((f4 + 255) / 256)), dim3(256), 0, st,
+    launch_k(slice_sum_kernel, dim3(static_cast<unsigned>((f4 + 255) / 256)), dim3(256), 0, st,
                        ta.part, ta.total, ta.ksplit);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

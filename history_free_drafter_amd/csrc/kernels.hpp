@@ -5,9 +5,48 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <hip/hip_ext.h>
+
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 
 namespace dlite {
+
+// ------------------------------------------------------------- launching --
+// Stage timing of the calling thread (dlite_set_stage_events).  While a stage
+// is armed, every kernel launch carries the stage's stop event and the first
+// one its start event, attached to the dispatch itself (hipExtLaunchKernel),
+// so the events bracket the stage's kernels exactly as a kernel trace does,
+// without marker packets of their own.
+struct StageTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool active = false, started = false;
+};
+StageTimer& stage_timer();
+
+// Launches kernel<<<grid, block, sm, st>>>(args...), with the armed stage's
+// events if any.
+template <typename... Params, typename... Args>
+inline void launch_k(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t sm, hipStream_t st,
+                     Args&&... args) {
+  std::tuple<std::decay_t<Params>...> tup(std::forward<Args>(args)...);
+  void* ptrs[sizeof...(Params) > 0 ? sizeof...(Params) : 1];
+  std::apply([&ptrs](auto&... e) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&e)), ...);
+  }, tup);
+  StageTimer& t = stage_timer();
+  if (t.active) {
+    (void)hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, sm, st,
+                             t.started ? nullptr : t.start, t.stop, 0);
+    t.started = true;
+  } else {
+    (void)hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, sm, st);
+  }
+}
 
 // Workspace counters, zeroed by the first kernel of every draft step.
 // CNT_LM_DONE: XCD groups of a streaming vocabulary launch whose workgroups
@@ -245,6 +284,8 @@ hipError_t launch_accept_sampled(const int32_t* cand, const float* draft, const 
 // of the K drafted candidates (rows K apart) against target rows of W.
 hipError_t launch_accept_window(const int32_t* cand, int K, const int32_t* tgt, int B, int W,
                                 int32_t* A, int32_t* next, hipStream_t st);
+// Copies the workspace status word (counters + CNT_STATUS) to `out` on the stream.
+hipError_t launch_status_copy(const unsigned* word, uint32_t* out, hipStream_t st);
 hipError_t launch_accept(const int32_t* cand, const int32_t* tgt, int B, int K,
                          int32_t* A, int32_t* next, hipStream_t st);
 

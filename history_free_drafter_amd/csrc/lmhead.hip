@@ -1038,8 +1038,8 @@ hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, uint64_t* px, hi
   sm = sm > sm_scan ? sm : sm_scan;
   e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
   if (e != hipSuccess) return e;
-  if (RK == 16) hipLaunchKernelGGL(seqhead_kernel<16>, dim3(grid), dim3(kWaves * 64), sm, st, f);
-  else hipLaunchKernelGGL(seqhead_kernel<10>, dim3(grid), dim3(kWaves * 64), sm, st, f);
+  if (RK == 16) launch_k(seqhead_kernel<16>, dim3(grid), dim3(kWaves * 64), sm, st, f);
+  else launch_k(seqhead_kernel<10>, dim3(grid), dim3(kWaves * 64), sm, st, f);
   return hipGetLastError();
 }
 
@@ -1071,7 +1071,20 @@ hipError_t launch_gatedhead(const GatedFuseArgs& f0, hipStream_t st) {
   e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
   if (e != hipSuccess) return e;
   void* args[] = {&f};
-  return hipLaunchCooperativeKernel(fn, dim3(cus), dim3(kWaves * 64), args, static_cast<unsigned>(sm), st);
+  // a cooperative launch takes no dispatch events: an armed stage is timed
+  // by markers around it
+  StageTimer& t = stage_timer();
+  if (t.active && !t.started) {
+    e = hipEventRecord(t.start, st);
+    if (e != hipSuccess) return e;
+  }
+  e = hipLaunchCooperativeKernel(fn, dim3(cus), dim3(kWaves * 64), args, static_cast<unsigned>(sm), st);
+  if (e != hipSuccess) return e;
+  if (t.active) {
+    t.started = true;
+    e = hipEventRecord(t.stop, st);
+  }
+  return e;
 }
 
 hipError_t launch_lmhead(const LmArgs& a0, bool bf16, hipStream_t st) {
@@ -1086,7 +1099,7 @@ hipError_t launch_lmhead(const LmArgs& a0, bool bf16, hipStream_t st) {
     if (e != hipSuccess) return e;
     LmArgs a = a0;
     a.G = g.G_part;
-    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3((a.M + 3) / 4), dim3(256), 0, st, a);
+    launch_k(lmhead_reduce_kernel, dim3((a.M + 3) / 4), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   const dim3 grid(a0.G), block(kWaves * 64);
@@ -1095,11 +1108,11 @@ hipError_t launch_lmhead(const LmArgs& a0, bool bf16, hipStream_t st) {
     a.tok0 = a0.tok0 + t0;
     a.M = (a0.M - t0) < 32 ? (a0.M - t0) : 32;
     if (bf16) {
-      if (a.M <= 16) hipLaunchKernelGGL((lmhead_pipe_kernel<uint16_t>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((lmhead_kernel<uint16_t, 2>), grid, block, 0, st, a);
+      if (a.M <= 16) launch_k((lmhead_pipe_kernel<uint16_t>), grid, block, 0, st, a);
+      else launch_k((lmhead_kernel<uint16_t, 2>), grid, block, 0, st, a);
     } else {
-      if (a.M <= 16) hipLaunchKernelGGL((lmhead_pipe_kernel<float>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((lmhead_kernel<float, 2>), grid, block, 0, st, a);
+      if (a.M <= 16) launch_k((lmhead_pipe_kernel<float>), grid, block, 0, st, a);
+      else launch_k((lmhead_kernel<float, 2>), grid, block, 0, st, a);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -171,18 +171,18 @@ __global__ __launch_bounds__(kThreads) void hidden_tap_kernel(NormArgs a) {
 hipError_t launch_feature(const FeatureArgs& a, bool bf16, hipStream_t st) {
   const dim3 grid(a.B * (a.m + 1 + a.K)), block(kThreads);
   if (bf16)
-    hipLaunchKernelGGL(feature_kernel<uint16_t>, grid, block, 0, st, a);
+    launch_k(feature_kernel<uint16_t>, grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL(feature_kernel<float>, grid, block, 0, st, a);
+    launch_k(feature_kernel<float>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_hidden_tap(const NormArgs& a, bool bf16, hipStream_t st) {
   const dim3 grid(a.B * a.K), block(kThreads);
   if (bf16)
-    hipLaunchKernelGGL(hidden_tap_kernel<uint16_t>, grid, block, 0, st, a);
+    launch_k(hidden_tap_kernel<uint16_t>, grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL(hidden_tap_kernel<float>, grid, block, 0, st, a);
+    launch_k(hidden_tap_kernel<float>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

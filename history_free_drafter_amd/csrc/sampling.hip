@@ -352,9 +352,9 @@ size_t sampling_scratch_bytes(long rows) {
 hipError_t launch_sample_tokens(const float* logits, int N, int V, float T, unsigned long long seed,
                                 unsigned stream, int32_t* tokens, void* scratch, hipStream_t st) {
   Best* part = static_cast<Best*>(scratch);
-  hipLaunchKernelGGL(sample_partial_kernel, dim3(kSampleChunks, N), dim3(kThreads), 0, st, logits, V,
+  launch_k(sample_partial_kernel, dim3(kSampleChunks, N), dim3(kThreads), 0, st, logits, V,
                      1.0 / static_cast<double>(T), seed, stream, part);
-  hipLaunchKernelGGL(sample_final_kernel, dim3((N + 3) / 4), dim3(256), 0, st, part, N, tokens);
+  launch_k(sample_final_kernel, dim3((N + 3) / 4), dim3(256), 0, st, part, N, tokens);
   return hipGetLastError();
 }
 
@@ -365,11 +365,11 @@ hipError_t launch_accept_sampled(const int32_t* cand, const float* draft, const 
   Lse* part = static_cast<Lse*>(scratch);
   double* csum = reinterpret_cast<double*>(part + static_cast<long>(B) * (2 * K + 1) * kSampleChunks);
   const double invT = 1.0 / static_cast<double>(T);
-  hipLaunchKernelGGL(lse_partial_kernel, dim3(kSampleChunks, B * (2 * K + 1)), dim3(kThreads), 0, st, draft,
+  launch_k(lse_partial_kernel, dim3(kSampleChunks, B * (2 * K + 1)), dim3(kThreads), 0, st, draft,
                      target, B * K, V, invT, part);
-  hipLaunchKernelGGL(chunk_sum_kernel, dim3(kSampleChunks, B), dim3(kThreads), 0, st, cand, draft, target, part, B,
+  launch_k(chunk_sum_kernel, dim3(kSampleChunks, B), dim3(kThreads), 0, st, cand, draft, target, part, B,
                      K, V, invT, seed, csum);
-  hipLaunchKernelGGL(pick_kernel, dim3(B), dim3(kThreads), 0, st, cand, draft, target, part, csum, B, K, V, invT,
+  launch_k(pick_kernel, dim3(B), dim3(kThreads), 0, st, cand, draft, target, part, csum, B, K, V, invT,
                      seed, A, next);
   return hipGetLastError();
 }

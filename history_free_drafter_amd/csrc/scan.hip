@@ -17,7 +17,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
 template <typename T, int TEAM>
 hipError_t launch_team(const ScanArgs& a, size_t sm, hipStream_t st) {
   const int nteam = (a.B + a.rpt - 1) / a.rpt;
-  hipLaunchKernelGGL((scan_kernel<T, TEAM>), dim3(nteam * TEAM), dim3(kThreads), sm, st, a);
+  launch_k((scan_kernel<T, TEAM>), dim3(nteam * TEAM), dim3(kThreads), sm, st, a);
   return hipGetLastError();
 }
 

@@ -42,6 +42,7 @@ class DraftModel:
         self.max_logit = torch.empty((B, K), dtype=torch.float32, device=device)
         self.accept_len = torch.empty((B,), dtype=torch.int32, device=device)
         self.next_anchor = torch.empty((B,), dtype=torch.int32, device=device)
+        self.status_word = torch.zeros((1,), dtype=torch.int32, device=device)
 
     def draft(self, features: torch.Tensor, anchors: torch.Tensor, taps=None, stream=None,
               weights=None):
@@ -49,6 +50,16 @@ class DraftModel:
                              features, anchors, self.candidates, self.max_logit, taps,
                              self.workspace, self.ws_bytes, stream)
         return self.candidates
+
+    def status(self, stream=None) -> int:
+        """Status word of the last draft call (0 = every bounded wait ended
+        normally); synchronises the stream to read it."""
+        _b.dlite_draft_status(self.workspace, self.status_word, self.ws_bytes, stream)
+        if stream is None:
+            torch.cuda.current_stream().synchronize()
+        else:
+            stream.synchronize()
+        return int(self.status_word.item())
 
     def set_gated_head(self, head: dict):
         """Upload the gated head's weights (storage-form arrays keyed as dlite_gated_head)."""

@@ -237,6 +237,30 @@ int dlite_draft_block_at(const dlite_dims *dims, const dlite_weights *weights,
                          hipStream_t stream);
 
 /*
+ * dlite_draft_status — the health word of the last draft step that used
+ * `workspace` (dlite_draft_block, _at or _gated), copied on `stream` into
+ * status[0] (a DEVICE uint32 owned by the caller), so it can be read without
+ * stalling the stream or be captured with the step.
+ *
+ * Several kernels of the step exchange data between workgroups that wait on
+ * each other (the sequential-head scan team, the fused scan + vocabulary and
+ * gated-head kernels).  Every such wait is bounded: rather than hang, a wait
+ * that runs out of its spin budget sets DLITE_STATUS_WAIT_TIMEOUT here and
+ * the kernel finishes.  A nonzero word therefore means that call's candidates
+ * are NOT reliable; the caller must treat it as an error.  The word is zeroed
+ * by the first kernel of every draft step, so it describes exactly one call.
+ *
+ * workspace, workspace_bytes  the buffer passed to that draft call
+ * status                      [1] uint32 (device, out): 0 = every wait ended
+ *                             normally, else a mask of DLITE_STATUS_* bits
+ * Errors as elsewhere (NULL pointers, a workspace that is not 256-byte
+ * aligned or smaller than any draft step's).
+ */
+enum { DLITE_STATUS_WAIT_TIMEOUT = 1 };
+int dlite_draft_status(const void *workspace, size_t workspace_bytes, uint32_t *status,
+                       hipStream_t stream);
+
+/*
  * dlite_accept_prefix — greedy verification of one round.
  *
  * [W] "一次因果前向评估整条候选": only the leading run of matches is committed.
@@ -333,11 +357,14 @@ int dlite_accept_sampled(const int32_t *candidates, const float *draft_logits, c
 
 /*
  * Instrumentation for timing one stage of the draft step with HIP events.
- * After this call, every dlite_draft_block call made from the same thread
- * records `before` on its stream immediately before the first kernel of
- * `stage` and `after` immediately after the stage's last kernel (for
- * per-layer stages: in the first backbone layer).  The events are owned by the
- * caller; pass NULL for both to switch recording off.  Returns
+ * After this call, every draft call made from the same thread attaches
+ * `before` to the dispatch of the first kernel of `stage` and `after` to the
+ * dispatch of its last kernel (hipExtLaunchKernel events: they carry the
+ * kernels' own start and end times, as a kernel trace does; for per-layer
+ * stages, in the first backbone layer).  A stage that launches no kernel in
+ * that call records both events back to back on the stream; the gated head's
+ * cooperative launch is bracketed by event records instead.  The events are
+ * owned by the caller; pass NULL for both to switch recording off.  Returns
  * DLITE_ERR_SHAPE for an unknown stage, DLITE_ERR_NULL if exactly one event is
  * NULL.
  */

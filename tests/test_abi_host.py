@@ -180,3 +180,13 @@ def test_accept_validation_codes():
     assert lib.dlite_accept_prefix(f, f, 0, 7, f, None, None) == -2
     assert lib.dlite_accept_prefix(f, f, 4, 0, f, None, None) == -2
     assert lib.dlite_accept_prefix(f, f, 4, 65, f, None, None) == -2
+
+
+def test_draft_status_validation_codes():
+    lib = B.load_library()
+    f = 0x300000
+    n = B.dlite_workspace_bytes(_dims(WORKLOADS["tiny_f32"]))
+    assert lib.dlite_draft_status(None, n, f, None) == -1
+    assert lib.dlite_draft_status(f, n, None, None) == -1
+    assert lib.dlite_draft_status(f + 16, n, f, None) == -5
+    assert lib.dlite_draft_status(f, 64, f, None) == -4

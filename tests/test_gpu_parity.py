@@ -50,6 +50,7 @@ def _run_gpu(w, weights, H, anchors, taps=True, model=None, ws_fill=None):
         model.workspace.fill_(ws_fill)
     model.draft(Hd, ad, taps=B.make_taps(**tb) if taps else None)
     torch.cuda.synchronize()
+    assert model.status() == 0, "a bounded wait timed out"
     out = {k: v.cpu().numpy() for k, v in tb.items()}
     out["cand"] = model.candidates.cpu().numpy()
     out["max_logit"] = model.max_logit.cpu().numpy()
@@ -246,6 +247,7 @@ def _run_gpu_gated(w, weights, head, H, anchors, model=None, taps=True):
     model.draft_gated(to_device(H, dev), torch.from_numpy(anchors).to(dev),
                       taps=B.make_taps(**tb) if taps else None)
     torch.cuda.synchronize()
+    assert model.status() == 0, "a bounded wait timed out"
     out = {k: v.cpu().numpy() for k, v in tb.items()}
     out["cand"] = model.candidates.cpu().numpy()
     out["max_logit"] = model.max_logit.cpu().numpy()
@@ -326,6 +328,7 @@ def _run_gpu_at(w, weights, vh, A, anchors, taps=True, model=None):
                   logits=f(w.B, w.K, w.vocab))
     model.draft_at(vd, Ad, ad, taps=B.make_taps(**tb) if taps else None)
     torch.cuda.synchronize()
+    assert model.status() == 0, "a bounded wait timed out"
     out = {k: v.cpu().numpy() for k, v in tb.items()}
     out["cand"] = model.candidates.cpu().numpy()
     out["max_logit"] = model.max_logit.cpu().numpy()
@@ -361,6 +364,7 @@ def test_draft_from_verify_is_the_draft_of_the_gathered_features(key):
     Hd = Hd.permute(1, 0, 2).contiguous()
     model.draft(Hd, torch.from_numpy(a).cuda())
     torch.cuda.synchronize()
+    assert model.status() == 0
     np.testing.assert_array_equal(at["cand"], model.candidates.cpu().numpy())
     np.testing.assert_array_equal(at["max_logit"], model.max_logit.cpu().numpy())
 
@@ -393,6 +397,7 @@ def test_accept_then_draft_from_verify_without_host_sync():
     A_d, next_d = model.accept(torch.from_numpy(t.astype(np.int32)).cuda())
     model.draft_at(vd, A_d, next_d)            # no synchronisation in between
     torch.cuda.synchronize()
+    assert model.status() == 0
     gpu_c = model.candidates.cpu().numpy()
     A_ref, next_ref = oracle.accept_prefix(ref["cand"], t)
     ref2 = _run_oracle(w, weights, oracle.boundary_features(vh, A_ref), next_ref.astype(np.int32))
