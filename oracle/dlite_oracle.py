@@ -60,6 +60,33 @@ def local_positions(m: int, K: int) -> np.ndarray:
                            np.arange(1, K + 1, dtype=np.int64)])
 
 
+def group_positions(m: int, G: int, n_valid: int, K: int):
+    """Local positions and key validity of the m + G + K slots of one request
+    whose local input is a token group of G slots, n_valid of them real.
+
+    [W] "局部位置编码切断草稿端的全局位置增长": the official position builder
+    allows a fixed-length local token group and takes the start of the valid
+    group as the coordinate origin, so the span depends only on the group and
+    block lengths.  READING: the group holds the last G tokens up to and
+    including the anchor, padded at the front when fewer exist; valid group
+    token j sits at j - (G - n_valid) (the anchor at n_valid - 1), the feature
+    slots share the anchor's position (Figure 3: "the same boundary"), and
+    placeholder k sits at n_valid - 1 + k.  Padding slots are no keys (their
+    position is irrelevant and set to 0).  G = 1 is Figure 3's layout.
+    Slot order: [features 0..m-1, group 0..G-1, placeholders 1..K].
+    Returns (pos [S] int64, key_valid [S] bool).
+    """
+    if not 1 <= n_valid <= G:
+        raise ValueError("the group must hold the anchor (1 <= n_valid <= G)")
+    pad = G - n_valid
+    pos = np.concatenate([np.full(m, n_valid - 1, dtype=np.int64),
+                          np.maximum(np.arange(G, dtype=np.int64) - pad, 0),
+                          n_valid - 1 + np.arange(1, K + 1, dtype=np.int64)])
+    valid = np.ones(m + G + K, dtype=bool)
+    valid[m:m + pad] = False
+    return pos, valid
+
+
 def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
     """Rotary embedding, rotate-half pairing (i, i + d/2).
 
@@ -76,7 +103,8 @@ def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
     return np.concatenate([x1 * cos - x2 * sin, x1 * sin + x2 * cos], axis=-1)
 
 
-def block_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+def block_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                    key_valid: np.ndarray = None) -> np.ndarray:
     """Non-causal attention of the local queries over every slot of the block.
 
     [W] "锚点是已经确定、尚待目标前向处理的输入": inside the short block the
@@ -84,11 +112,14 @@ def block_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
     [W] "本轮临时 K/V 仍然需要计算": Q for the anchor and placeholders, K and V
     for the context features and the local inputs; nothing persists.
     Grouped heads: query head h reads key/value head floor(h / G).
-    q: [Lq, n_q, d]; k, v: [S, n_kv, d]  ->  [Lq, n_q, d].
+    q: [Lq, n_q, d]; k, v: [S, n_kv, d]  ->  [Lq, n_q, d].  key_valid [S]
+    (optional): slots that are keys (padding of a local token group is not).
     """
     n_q, d = q.shape[1], q.shape[2]
     G = n_q // k.shape[1]
     out = np.empty_like(q)
+    if key_valid is not None:        # only the slots that are keys take part
+        k, v = k[key_valid], v[key_valid]
     for h in range(n_q):
         kh, vh = k[:, h // G, :], v[:, h // G, :]
         sc = (q[:, h, :] @ kh.T) / np.sqrt(d)                      # [Lq, S]
@@ -119,12 +150,14 @@ def swiglu_ffn(n: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray) -> np.n
 
 
 def backbone_layer(ctx: np.ndarray, x: np.ndarray, pos: np.ndarray, lw: dict,
-                   dims) -> np.ndarray:
+                   dims, key_valid: np.ndarray = None) -> np.ndarray:
     """One history-free backbone layer for one request.
 
     ctx: [m, D] context slots (fixed across layers, READING of [W] "本轮临时
     K/V 仍然需要计算": context features only supply K and V);
-    x: [1 + K, D] residual stream of the anchor and placeholders.
+    x: [L, D] residual stream of the local rows: the anchor (or the local
+    token group) and the placeholders; pos [m + L] their local positions;
+    key_valid [m + L] (optional) which slots are keys.
     Returns the updated local residual stream.
     """
     n_q, n_kv, d_h, eps = dims.n_q, dims.n_kv, dims.d_h, dims.rms_eps
@@ -139,7 +172,7 @@ def backbone_layer(ctx: np.ndarray, x: np.ndarray, pos: np.ndarray, lw: dict,
     v = (n_slots @ wv.T).reshape(-1, n_kv, d_h)
     q = rope(q, pos[m:], dims.rope_theta)
     k = rope(k, pos, dims.rope_theta)
-    o = block_attention(q, k, v).reshape(x.shape[0], n_q * d_h)
+    o = block_attention(q, k, v, key_valid).reshape(x.shape[0], n_q * d_h)
     x = x + o @ lw["wo"].T
     n2 = rms_norm(x, lw["ffn_norm"], eps)
     return x + swiglu_ffn(n2, lw["w_gate_up"], lw["w_down"])
@@ -190,7 +223,16 @@ def sigmoid(x: np.ndarray) -> np.ndarray:
     return 1.0 / (1.0 + np.exp(-x))
 
 
-def gated_head(h: np.ndarray, anchor: int, head: dict, forced=None) -> dict:
+def gated_state_step(s: np.ndarray, v: np.ndarray, head: dict) -> np.ndarray:
+    """One gated state update ([W] "官方顺序头具体算了什么"):
+    [g; c] = W_s [s; v] + b_s, s' = sigmoid(g) * s + (1 - sigmoid(g)) * tanh(c)."""
+    R = s.shape[0]
+    gc = head["w_s"] @ np.concatenate([s, v]) + head["b_s"]
+    f = sigmoid(gc[:R])
+    return f * s + (1.0 - f) * np.tanh(gc[R:])
+
+
+def gated_head(h: np.ndarray, anchor: int, head: dict, forced=None, warmup=None) -> dict:
     """The walkthrough's own sequential head for one request, greedy.
 
     [W] "官方顺序头具体算了什么": the previous token enters through an R-wide
@@ -205,25 +247,30 @@ def gated_head(h: np.ndarray, anchor: int, head: dict, forced=None) -> dict:
     u_i = h_i, the final-normed backbone row of placeholder i; an anchor id
     outside [0, V) reads a zero embedding row (its candidates are reported
     as -1 by the caller).
+    Warm-up ([W], same section: when the configuration allows, one token
+    before the anchor warms the state up over a fixed length).  READING: with
+    warmup = w in [0, V), one state update with v = E_R(w) from s = 0 and no
+    output precedes position 1 (so s_0 is that state); warmup None or outside
+    [0, V) (no token before the anchor) leaves s_0 = 0.
     h: [K, D]; head: emb [V, R], w_s [2R, 2R], b_s [2R], w_h [R, R + D],
     b_h [R], w_o [V, R].  forced: optional [K] tokens fed back in place of
     the chosen ones (to follow a run that chose differently at a near tie).
     Returns s [K, R], r [K, R], logits [K, V], cand [K], margin [K].
     """
     K = h.shape[0]
-    emb, w_s, b_s = head["emb"], head["w_s"], head["b_s"]
+    emb = head["emb"]
     w_h, b_h, w_o = head["w_h"], head["b_h"], head["w_o"]
     R = emb.shape[1]
     V = w_o.shape[0]
     s = np.zeros(R)
+    if warmup is not None and 0 <= int(warmup) < emb.shape[0]:
+        s = gated_state_step(s, emb[int(warmup)], head)
     out = dict(s=np.empty((K, R)), r=np.empty((K, R)), logits=np.empty((K, V)),
                cand=np.empty(K, dtype=np.int64), margin=np.empty(K))
     d_prev = int(anchor)
     for i in range(K):
         v = emb[d_prev] if 0 <= d_prev < emb.shape[0] else np.zeros(R)
-        gc = w_s @ np.concatenate([s, v]) + b_s
-        f = sigmoid(gc[:R])
-        s = f * s + (1.0 - f) * np.tanh(gc[R:])
+        s = gated_state_step(s, v, head)
         r = w_h @ np.concatenate([s, h[i]]) + b_h
         logits, tok, margin = lm_head_argmax(r, w_o)
         out["s"][i], out["r"][i], out["logits"][i] = s, r, logits
@@ -232,9 +279,12 @@ def gated_head(h: np.ndarray, anchor: int, head: dict, forced=None) -> dict:
     return out
 
 
-def gated_heads(h: np.ndarray, anchors: np.ndarray, head: dict, forced=None) -> dict:
-    """gated_head for every request: h [B, K, D], anchors [B] ids, forced [B, K] or None."""
-    runs = [gated_head(h[b], int(anchors[b]), head, None if forced is None else forced[b])
+def gated_heads(h: np.ndarray, anchors: np.ndarray, head: dict, forced=None,
+                warmups=None) -> dict:
+    """gated_head for every request: h [B, K, D], anchors [B] ids, forced
+    [B, K] or None, warmups [B] ids (the token before each anchor) or None."""
+    runs = [gated_head(h[b], int(anchors[b]), head, None if forced is None else forced[b],
+                       None if warmups is None else int(warmups[b]))
             for b in range(h.shape[0])]
     return {k: np.stack([o[k] for o in runs]) for k in runs[0]}
 
@@ -243,14 +293,22 @@ def gated_heads(h: np.ndarray, anchors: np.ndarray, head: dict, forced=None) -> 
 
 
 def draft_block(dims, weights: dict, H: np.ndarray, anchor_rows: np.ndarray,
-                with_head: bool = True) -> dict:
+                with_head: bool = True, group_rows: np.ndarray = None,
+                group_valid: np.ndarray = None) -> dict:
     """The whole draft step for a batch: K greedy candidates per request.
 
     dims: object with B, m, D, n_layers, n_q, n_kv, d_h, K, rms_eps, rope_theta.
     weights: fp64 arrays keyed as in the library's weight layout (layers list).
     H: [B, m, D] boundary features; anchor_rows: [B, D] = tok_emb[anchor].
-    Returns dict with z [B,m,D], x_layers (list of [B,1+K,D]), h [B,K,D],
-    s [B,K,r], logits [B,K,V], cand [B,K], margin [B,K].
+    Local token group (optional, [W] "锚点是已经确定、尚待目标前向处理的输入":
+    the draft input holds the anchor or a fixed-length local token group):
+    group_rows [B, G, D] = tok_emb of the last G tokens ending at the anchor
+    (rows of padding slots are ignored), group_valid [B] = real tokens per
+    request (a suffix of the group); anchor_rows is then not read.  The group
+    rows are local rows like the anchor (they query and are updated in every
+    layer); positions follow group_positions.
+    Returns dict with z [B,m,D], x_layers (list of [B,L,D], L = 1 + K or
+    G + K), h [B,K,D], s [B,K,r], logits [B,K,V], cand [B,K], margin [B,K].
 
     [W] "从目标隐藏状态到并行草稿表示" (Figure 3) and the generation loop in
     "一轮执行后，缓存、锚点与隐藏状态怎样对齐": features + anchor + placeholders
@@ -258,18 +316,29 @@ def draft_block(dims, weights: dict, H: np.ndarray, anchor_rows: np.ndarray,
     """
     B, m, K = dims.B, dims.m, dims.K
     z = feature_slots(H, weights["depth_emb"], weights["feat_norm"], dims.rms_eps)
-    pos = local_positions(m, K)
-    # [W] "锚点是已经确定…": the anchor enters through its embedding;
-    # READING: one shared learned placeholder vector for all K slots.
-    x = np.empty((B, 1 + K, dims.D))
-    x[:, 0] = anchor_rows
-    x[:, 1:] = weights["ph_emb"][None, None, :]
+    if group_rows is None:
+        G = 1
+        pos = [local_positions(m, K)] * B
+        valid = [None] * B
+        lead = np.asarray(anchor_rows)[:, None, :]
+    else:
+        G = group_rows.shape[1]
+        pv = [group_positions(m, G, int(group_valid[b]), K) for b in range(B)]
+        pos = [p for p, _ in pv]
+        valid = [v for _, v in pv]
+        lead = np.where(np.stack([v[m:m + G] for v in valid])[:, :, None], group_rows, 0.0)
+    # [W] "锚点是已经确定…": the anchor (or the token group) enters through
+    # its embedding; READING: one shared learned placeholder vector for all K
+    # slots.
+    x = np.empty((B, G + K, dims.D))
+    x[:, :G] = lead
+    x[:, G:] = weights["ph_emb"][None, None, :]
     x_layers = []
     for lw in weights["layers"]:
-        x = np.stack([backbone_layer(z[b], x[b], pos, lw, dims) for b in range(B)])
+        x = np.stack([backbone_layer(z[b], x[b], pos[b], lw, dims, valid[b]) for b in range(B)])
         x_layers.append(x.copy())
     # READING: a final RMSNorm before the head; only placeholder rows are drafted.
-    h = rms_norm(x[:, 1:], weights["final_norm"], dims.rms_eps)
+    h = rms_norm(x[:, G:], weights["final_norm"], dims.rms_eps)
     if not with_head:   # the backbone only (for another sequential head)
         return dict(z=z, x_layers=x_layers, h=h)
     s = np.stack([sequential_head(h[b], weights["seq_w_down"], weights["seq_w_up"])

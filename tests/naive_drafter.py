@@ -57,12 +57,25 @@ def _silu(t):
     return t / (1.0 + math.exp(-t))
 
 
-def _position(slot, m):
-    """Figure 3: features (slots 0..m-1) and the anchor (slot m) at 0,
-    placeholder k (slot m + k) at k."""
-    if slot <= m:
-        return 0
-    return slot - m
+def _position(slot, m, G=1, n_valid=1):
+    """Local position of a slot.  Figure 3 (G = 1): features (slots 0..m-1)
+    and the anchor (slot m) at 0, placeholder k (slot m + k) at k.  With a
+    token group of G slots (n_valid real, padded at the front), the origin is
+    the first real group token: group slot j at j - (G - n_valid), the
+    features at the anchor's position n_valid - 1, placeholder k at
+    n_valid - 1 + k."""
+    pad = G - n_valid
+    if slot < m:
+        return n_valid - 1
+    if slot < m + G:
+        j = slot - m
+        return j - pad if j >= pad else 0
+    return n_valid - 1 + (slot - m - G + 1)
+
+
+def _is_key(slot, m, G=1, n_valid=1):
+    """Padding slots of the token group are not keys."""
+    return not (m <= slot < m + G - n_valid)
 
 
 def _rotate(vec, p, theta):
@@ -78,13 +91,13 @@ def _rotate(vec, p, theta):
     return out
 
 
-def _layer(ctx, x, lw, dims):
+def _layer(ctx, x, lw, dims, G=1, n_valid=1):
     """One pre-norm layer for one request: ctx [m][D] (keys/values only),
-    x [1+K][D] local residual rows (anchor, placeholders)."""
+    x [G+K][D] local residual rows (anchor or token group, placeholders)."""
     m = len(ctx)
     n_q, n_kv, dh = dims.n_q, dims.n_kv, dims.d_h
     eps, theta = dims.rms_eps, dims.rope_theta
-    G = n_q // n_kv
+    per_kv = n_q // n_kv            # query heads per key/value head
     slots = list(ctx) + list(x)
     S = len(slots)
     wqkv = lw["wqkv"]
@@ -97,7 +110,8 @@ def _layer(ctx, x, lw, dims):
     for s in range(S):
         kf = _matvec(k_rows, normed[s])
         vf = _matvec(v_rows, normed[s])
-        keys.append([_rotate(kf[g * dh:(g + 1) * dh], _position(s, m), theta) for g in range(n_kv)])
+        keys.append([_rotate(kf[g * dh:(g + 1) * dh], _position(s, m, G, n_valid), theta)
+                     for g in range(n_kv)])
         vals.append([vf[g * dh:(g + 1) * dh] for g in range(n_kv)])
     new_x = []
     for j in range(len(x)):
@@ -105,16 +119,16 @@ def _layer(ctx, x, lw, dims):
         qf = _matvec(q_rows, normed[slot])
         attn = []
         for h in range(n_q):
-            qh = _rotate(qf[h * dh:(h + 1) * dh], _position(slot, m), theta)
-            g = h // G
+            qh = _rotate(qf[h * dh:(h + 1) * dh], _position(slot, m, G, n_valid), theta)
+            g = h // per_kv
             scores = []
             for s in range(S):
                 dot = 0.0
                 for t in range(dh):
                     dot += qh[t] * keys[s][g][t]
                 scores.append(dot / math.sqrt(dh))
-            mx = max(scores)
-            ex = [math.exp(v - mx) for v in scores]
+            mx = max(scores[s] for s in range(S) if _is_key(s, m, G, n_valid))
+            ex = [math.exp(scores[s] - mx) if _is_key(s, m, G, n_valid) else 0.0 for s in range(S)]
             tot = sum(ex)
             for t in range(dh):
                 acc = 0.0
@@ -132,12 +146,13 @@ def _layer(ctx, x, lw, dims):
     return new_x
 
 
-def naive_draft(dims, weights, H, anchor_rows):
+def naive_draft(dims, weights, H, anchor_rows, group_rows=None, group_valid=None):
     """The whole draft step with scalar loops.
 
     weights: fp64 arrays keyed as the main oracle's (layers list); H [B][m][D];
-    anchor_rows [B][D].  Returns dict of nested lists: z, x_layers, h, s,
-    logits, cand.
+    anchor_rows [B][D]; or a local token group: group_rows [B][G][D] with
+    group_valid [B] real tokens at the end of each group.  Returns dict of
+    nested lists: z, x_layers, h, s, logits, cand.
     """
     B, m, K = dims.B, dims.m, dims.K
     eps = dims.rms_eps
@@ -157,11 +172,18 @@ def naive_draft(dims, weights, H, anchor_rows):
             row = [float(H[b][l][i]) + dep[l][i] for i in range(len(dep[l]))]
             ctx.append(_rmsnorm_row(row, fgain, eps))
         out["z"].append(ctx)
-        x = [[float(v) for v in anchor_rows[b]]] + [list(ph) for _ in range(K)]
+        if group_rows is None:
+            G, nv = 1, 1
+            lead = [[float(v) for v in anchor_rows[b]]]
+        else:
+            G, nv = len(group_rows[b]), int(group_valid[b])
+            lead = [[float(v) for v in group_rows[b][j]] if j >= G - nv else [0.0] * len(ph)
+                    for j in range(G)]
+        x = lead + [list(ph) for _ in range(K)]
         for li, lw in enumerate(layers):
-            x = _layer(ctx, x, lw, dims)
+            x = _layer(ctx, x, lw, dims, G, nv)
             out["x_layers"][li].append([list(row) for row in x])
-        hs = [_rmsnorm_row(x[1 + k], fin, eps) for k in range(K)]
+        hs = [_rmsnorm_row(x[G + k], fin, eps) for k in range(K)]
         out["h"].append(hs)
         state = [0.0] * r
         states, logits, cands = [], [], []
