@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG, "libdlite.so")
 DLITE_F32, DLITE_BF16 = 0, 1
 ERRORS = {-1: "DLITE_ERR_NULL", -2: "DLITE_ERR_SHAPE", -3: "DLITE_ERR_DTYPE",
           -4: "DLITE_ERR_WORKSPACE", -5: "DLITE_ERR_UNSUPPORTED", -6: "DLITE_ERR_HIP"}
-EXPORTS = ["dlite_workspace_bytes", "dlite_draft_block", "dlite_draft_block_at",
+EXPORTS = ["dlite_workspace_bytes", "dlite_draft_block", "dlite_draft_block_noalloc",
+           "dlite_draft_block_at",
            "dlite_draft_block_gated", "dlite_sampling_workspace_bytes", "dlite_sample_tokens",
            "dlite_accept_sampled", "dlite_accept_window",
            "dlite_accept_prefix", "dlite_draft_status", "dlite_set_stage_events",
@@ -75,6 +76,10 @@ def load_library(path: str = LIB_PATH):
                                       c_void_p, c_void_p, c_void_p, POINTER(DliteTaps),
                                       c_void_p, c_size_t, c_void_p]
     lib.dlite_draft_block.restype = c_int
+    lib.dlite_draft_block_noalloc.argtypes = [POINTER(DliteDims), POINTER(DliteWeights), c_void_p,
+                                              c_void_p, c_void_p, c_void_p, POINTER(DliteTaps),
+                                              c_void_p, c_void_p]
+    lib.dlite_draft_block_noalloc.restype = c_int
     lib.dlite_draft_block_gated.argtypes = [POINTER(DliteDims), POINTER(DliteWeights),
                                             POINTER(DliteGatedHead), c_void_p, c_void_p,
                                             c_void_p, c_void_p, POINTER(DliteTaps), c_void_p,
@@ -178,6 +183,16 @@ def dlite_draft_block(dims, weights, features, anchor_ids, candidates, max_logit
         ctypes.byref(dims), ctypes.byref(weights), _ptr(features), _ptr(anchor_ids),
         _ptr(candidates), _ptr(max_logit), ctypes.byref(taps) if taps is not None else None,
         _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc)
+
+
+def dlite_draft_block_noalloc(dims, weights, features, anchor_ids, candidates, max_logit=None,
+                              taps=None, status=None, stream=None):
+    """Enqueue one draft step with the library's own scratch (no workspace, no allocation)."""
+    rc = load_library().dlite_draft_block_noalloc(
+        ctypes.byref(dims), ctypes.byref(weights), _ptr(features), _ptr(anchor_ids),
+        _ptr(candidates), _ptr(max_logit), ctypes.byref(taps) if taps is not None else None,
+        _ptr(status), _stream(stream))
     _check(rc)
 
 

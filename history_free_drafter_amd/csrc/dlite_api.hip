@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "dlite.h"
@@ -486,6 +487,34 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   return ok();
 }
 
+// The allocation-free entry point's scratch: one array per GPU, held until the
+// process ends.  Host code never uses its name as an address (that is a host
+// stand-in); each device's address is looked up once with that device current.
+constexpr size_t kStaticScratchBytes = size_t{64} << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (resolved on first use).
+int static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DLITE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DLITE_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DLITE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DLITE_OK;
+}
+
 }  // namespace
 
 namespace dlite {
@@ -527,6 +556,26 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   const FeatureSource fs{features, static_cast<long>(dims->m) * D, D, 0, nullptr, 1};
   return draft_impl(dims, w, fs, nullptr, anchor_ids, candidates, max_logit, taps, workspace,
                     workspace_bytes, st);
+}
+
+int dlite_draft_block_noalloc(const dlite_dims* dims, const dlite_weights* w, const void* features,
+                              const int32_t* anchor_ids, int32_t* candidates, float* max_logit,
+                              const dlite_taps* taps, uint32_t* status, hipStream_t st) {
+  DLITE_TRY(check_dims(dims));
+  DLITE_TRY(check_ptr(features, "features"));
+  const size_t need = make_plan(*dims).total;
+  if (need > kStaticScratchBytes)
+    return fail(DLITE_ERR_WORKSPACE,
+                "these dimensions need %zu bytes of scratch; the allocation-free entry point has %zu "
+                "(use dlite_draft_block with a workspace)", need, kStaticScratchBytes);
+  void* ws = nullptr;
+  DLITE_TRY(static_scratch(&ws));
+  const long D = dims->D;
+  const FeatureSource fs{features, static_cast<long>(dims->m) * D, D, 0, nullptr, 1};
+  DLITE_TRY(draft_impl(dims, w, fs, nullptr, anchor_ids, candidates, max_logit, taps, ws,
+                       kStaticScratchBytes, st));
+  if (status) DLITE_LAUNCH(launch_status_copy(static_cast<const unsigned*>(ws) + CNT_STATUS, status, st));
+  return ok();
 }
 
 int dlite_draft_block_gated(const dlite_dims* dims, const dlite_weights* w, const dlite_gated_head* head,

@@ -180,6 +180,33 @@ int dlite_draft_block(const dlite_dims *dims, const dlite_weights *weights,
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dlite_draft_block_noalloc — dlite_draft_block for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * Same computation, kernels and results as dlite_draft_block; the scratch is
+ * a fixed 64 MiB array inside the library (one per GPU, on the current
+ * device, created with the code object and held until the process ends)
+ * instead of the caller's workspace.  The call allocates nothing.  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, or two host threads) race and give undefined results; order them
+ * on one stream.  The array keeps the last call's contents; the step clears
+ * what must start at zero itself.
+ *
+ * Dimensions whose dlite_workspace_bytes exceeds 64 MiB (at the 8B-shaped
+ * drafter: more than about 20 requests) are rejected with DLITE_ERR_WORKSPACE
+ * before anything is enqueued.
+ * status  [1] uint32 (device, out, may be NULL): the call's status word, as
+ *         dlite_draft_status reports it for a workspace (0 = every bounded
+ *         wait ended normally), written on the stream after the step.
+ * All other arguments and errors are as dlite_draft_block.
+ */
+int dlite_draft_block_noalloc(const dlite_dims *dims, const dlite_weights *weights,
+                              const void *features, const int32_t *anchor_ids,
+                              int32_t *candidates, float *max_logit, const dlite_taps *taps,
+                              uint32_t *status, hipStream_t stream);
+
+/*
  * dlite_draft_block_gated — the draft step with the walkthrough's own gated
  * sequential head in place of the fixed recurrence.
  *
