@@ -136,6 +136,18 @@ def seqhead_is_fused(w, head="fixed"):
             and w.rank in (320, 512))
 
 
+def seqhead_folds_p(w, head="fixed", cus=256):
+    """Whether the fused kernel also computes the scan's input P (the
+    library's rule: k slices = helpers // (r / 16), at most 16, each slice at
+    most 32 k-steps of 32)."""
+    if not seqhead_is_fused(w, head) or w.D % 32:
+        return False
+    team = 16 if w.rank % 256 == 0 and w.B <= 16 else 8
+    helpers = max(cus, team * 8) - team * w.B
+    nps = min(16, helpers // (w.rank // 16))
+    return nps >= 1 and -(-(w.D // 32) // nps) <= 32
+
+
 def gatedhead_is_fused(w, head="fixed"):
     """Whether the gated head runs as one cooperative launch (the library's
     rule on this chip: bf16, rank 512, 1..8 requests)."""
@@ -344,10 +356,15 @@ def main():
 
     costs = stage_costs(w, args.head, layers=[0])   # what one timed launch group covers
     fused = seqhead_is_fused(w, args.head)
-    if fused:   # one kernel: its stage events bracket both
-        costs["scan"] = [costs["scan"][0] + costs["lm_head"][0], costs["scan"][1] + costs["lm_head"][1]]
+    folds_p = seqhead_folds_p(w, args.head)
+    if fused:   # one kernel: its stage events bracket both (and the scan's input)
+        parts = ["scan", "lm_head"] + (["seq_proj"] if folds_p else [])
+        costs["scan"] = [sum(costs[k][0] for k in parts), sum(costs[k][1] for k in parts)]
         costs["lm_head"] = [0.0, 0.0]
-    kernel_names = {"scan": "seqhead_kernel (fused scan + vocabulary + argmax)"} if fused else {}
+        if folds_p:
+            costs["seq_proj"] = [0.0, 0.0]
+    kernel_names = ({"scan": "seqhead_kernel (fused scan input + scan + vocabulary + argmax)" if folds_p
+                     else "seqhead_kernel (fused scan + vocabulary + argmax)"} if fused else {})
     gfused = gatedhead_is_fused(w, args.head)
     if gfused:   # all K positions in one launch; W_o and the head's weights read once
         e_ = 2
@@ -415,6 +432,8 @@ def main():
     # stages that launch nothing here (their events are recorded back to back)
     if fused or gfused:
         stage_us["lm_head"] = None          # inside the fused sequential-head kernel
+    if folds_p:
+        stage_us["seq_proj"] = None         # computed inside the fused kernel too
     stage_us["final_norm"] = None           # folded into the GEMMs (a kernel only for the fp32 tap)
     stage_us = {k: v for k, v in stage_us.items() if v is not None}
 

@@ -141,8 +141,11 @@ Plan make_plan(const dlite_dims& d) {
   p.P = take(B * K * r * 4);
   // scan exchange slots, then (fused head) the helpers' tagged words: both
   // zeroed by the feature kernel
+  // (and the P partials when the fused kernel computes P: at most 16 slices)
   p.U = take(scan_scratch_floats(d.B, d.rank) * 4 +
-             (seqhead_fused(d.B, d.K, d.rank, d.dtype == DLITE_BF16) ? seqhead_fold_bytes(d.B * d.K) : 0));
+             (seqhead_fused(d.B, d.K, d.rank, d.dtype == DLITE_BF16)
+                  ? seqhead_fold_bytes(d.B * d.K) + seqhead_pw_bytes(d.B * d.K, d.rank, 16)
+                  : 0));
   p.Sf = take(B * K * r * 4);
   p.Sb = take(B * K * r * es);
   p.GR = take(B * r * es);        // gated head: r_i of the current step
@@ -312,8 +315,12 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   fa.anchors = anchor_ids; fa.X = X; fa.XB = XB; fa.ssq = SSQ; fa.tap_z = tp.z;
   fa.counters = counters; fa.n_counters = counter_words();
   fa.clear = reinterpret_cast<uint4*>(U);
+  // the fused sequential-head kernel computes P itself when it can (then its
+  // tagged partials follow the helpers' words in the cleared region)
+  const int p_slices = !gh ? seqhead_p_slices(B, K, r, D) : 0;
   const size_t fold_bytes = seqhead_fused(B, K, r, bf16) ? seqhead_fold_bytes(B * K) : 0;
-  fa.n_clear = static_cast<long>((scan_scratch_floats(B, r) * sizeof(float) + fold_bytes) / 16);
+  const size_t pw_bytes = p_slices ? seqhead_pw_bytes(B * K, r, p_slices) : 0;
+  fa.n_clear = static_cast<long>((scan_scratch_floats(B, r) * sizeof(float) + fold_bytes + pw_bytes) / 16);
   fa.B = B; fa.m = m; fa.K = K; fa.D = D; fa.V = d.vocab; fa.n_layers = d.n_layers;
   fa.eps = d.rms_eps;
   DLITE_LAUNCH(mark(DLITE_STAGE_FEATURES, true, st));
@@ -408,7 +415,7 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   ph.np_hi = local_parts; ph.norm_len = D; ph.eps = d.rms_eps;
   ph.out = P; ph.ld_out = r; ph.omap = RowMap{K, K, 0};
   DLITE_LAUNCH(mark(DLITE_STAGE_SEQ_PROJ, true, st));
-  DLITE_LAUNCH(launch_gemm(ph, EPI_STORE_F32, bf16, gs, st));
+  if (!p_slices) DLITE_LAUNCH(launch_gemm(ph, EPI_STORE_F32, bf16, gs, st));
   DLITE_LAUNCH(mark(DLITE_STAGE_SEQ_PROJ, false, st));
 
   // 5. the K-step recurrence, 6. vocabulary projection + argmax (one fused
@@ -469,10 +476,9 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
     }
   } else if (seqhead_fused(B, K, r, bf16)) {
     DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
-    DLITE_LAUNCH(launch_seqhead(sa, la,
-                                reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(U) +
-                                                            scan_scratch_floats(B, r) * sizeof(float)),
-                                st));
+    uint64_t* px = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(U) + scan_scratch_floats(B, r) * sizeof(float));
+    uint64_t* pw = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(px) + fold_bytes);
+    DLITE_LAUNCH(launch_seqhead(sa, la, px, p_slices ? &ph : nullptr, p_slices ? pw : nullptr, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, true, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, false, st));

@@ -198,6 +198,11 @@ struct ScanArgs {
   unsigned tag0;         // steps run by earlier launches of this call (offsets the exchange tags)
   int rpt;               // requests per team (set by the launcher)
   int stage;             // byte offset of the weight staging area in dynamic LDS (0: none)
+  // P from tagged k-slice partials instead of P (fused kernel): the value of
+  // token t, row n is the sum over slices q < Pslices of the word at
+  // Pw[(q * B K + t) * r + n] (value bits low, tag 1 high), in slice order
+  const uint64_t* Pw;
+  int Pslices;
 };
 hipError_t launch_scan(const ScanArgs& a, bool bf16, hipStream_t st);
 
@@ -231,7 +236,15 @@ constexpr int kFuseMaxHelpers = 1024;
 bool seqhead_fused(int B, int K, int r, bool bf16);
 // px: seqhead_fold_bytes(B K) of zeroed scratch (the helpers' tagged words).
 size_t seqhead_fold_bytes(int M);
-hipError_t launch_seqhead(const ScanArgs& s, const LmArgs& l, uint64_t* px, hipStream_t st);
+// The fused kernel can also compute the scan's input P = W_down[:, :D] h
+// itself (ph: the GEMM arguments of the separate launch, EPI_STORE_F32): its
+// first helpers each take a 16-row tile and a k slice and publish tagged
+// partials into pw, which the team sums before its first step.  Returns the
+// number of k slices (0: P must come from the separate launch).
+int seqhead_p_slices(int B, int K, int r, int D);
+size_t seqhead_pw_bytes(int M, int r, int slices);   // zeroed scratch for pw
+hipError_t launch_seqhead(const ScanArgs& s, const LmArgs& l, uint64_t* px, const GemmArgs* ph, uint64_t* pw,
+                          hipStream_t st);
 
 // ------------------------------------------------- gated sequential head ----
 constexpr int kGatedMaxRank = 512;

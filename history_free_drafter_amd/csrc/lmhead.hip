@@ -351,7 +351,67 @@ struct FuseArgs {
   int nteam;        // scan teams (one request each): blocks xq * 8 + t, t < nteam, xq < team size
   unsigned* done;   // published-state counter of the team members
   uint64_t* px;     // [M, G] tagged (max, index) words of the helpers (zero at launch)
+  GemmArgs ph;      // P = W_down[:, :D] h, when the helpers compute it (nps > 0)
+  int nps;          // its k slices: helper q * nps + p takes row tile q, slice p
 };
+
+constexpr int kPSteps = 4;   // k-steps of 32 per wave and P slice (at most)
+
+// One helper's share of P: the 16 rows pt * 16 .. of W_down[:, :D] times the
+// M pre-gained token rows over k slice ps, scaled by each token's 1/rms (the
+// slices add up to P), published as tagged words (tag 1) for the team.  The
+// eight waves split the slice's k-steps and are added in wave order.
+__device__ void seqhead_p_partial(const FuseArgs& f, int hp, unsigned char* smem) {
+  const GemmArgs& g = f.ph;
+  const int r = f.la.r, M = g.M;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, grp = lane >> 4;
+  const int pt = hp / f.nps, ps = hp % f.nps;
+  const int nst = g.K / 32;
+  const int k0 = static_cast<int>(static_cast<long>(ps) * nst / f.nps);
+  const int k1 = static_cast<int>(static_cast<long>(ps + 1) * nst / f.nps);
+  const int s0 = k0 + wave * (k1 - k0) / kWaves, s1 = k0 + (wave + 1) * (k1 - k0) / kWaves;
+  const uint16_t* W = static_cast<const uint16_t*>(g.W);
+  const uint16_t* X = static_cast<const uint16_t*>(g.src);
+  const bool tok_ok = c16 < M;
+  const long xrow = g.smap.row(tok_ok ? c16 : 0);
+  const long wrow = static_cast<long>(pt) * 16 + c16;
+  uint4 av[kPSteps], bv[kPSteps];
+#pragma unroll
+  for (int i = 0; i < kPSteps; ++i) {
+    const int s = s0 + i < s1 ? s0 + i : k0;   // in-range clamp
+    av[i] = ld_stream(W + wrow * g.ldw + s * 32 + grp * 8);
+    bv[i] = *reinterpret_cast<const uint4*>(X + xrow * g.ld_src + s * 32 + grp * 8);
+  }
+  float* red = reinterpret_cast<float*>(smem);          // [8 waves][64 lanes][4]
+  float* inv = red + kWaves * 64 * 4;                   // [16]
+  // each token's 1/rms from the producer's partial sums of squares
+  for (int t = wave; t < M; t += kWaves) {
+    const float* sp = g.ssq + g.qmap.row(t) * kSsqParts;
+    float v = 0.f;
+    for (int j = lane; j < g.np_hi; j += 64) v += sp[j];
+    v = wave_sum(v);
+    if (lane == 0) inv[t] = 1.0f / sqrtf(v / static_cast<float>(g.norm_len) + g.eps);
+  }
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kPSteps; ++i)
+    if (s0 + i < s1) acc = mma_step(av[i], tok_ok ? bv[i] : make_uint4(0, 0, 0, 0), acc, uint16_t());
+  *reinterpret_cast<floatx4*>(red + (wave * 64 + lane) * 4) = acc;
+  __syncthreads();
+  // lane (row group q, token c) holds rows 4 q .. 4 q + 3 of token c
+  for (int e = threadIdx.x; e < 16 * M; e += blockDim.x) {
+    const int t = e >> 4, rr = e & 15;
+    const int src = ((rr >> 2) * 16 + t) * 4 + (rr & 3);
+    float v = 0.f;
+    for (int w = 0; w < kWaves; ++w) v += red[w * 256 + src];
+    v *= inv[t];
+    const long o = (static_cast<long>(ps) * M + t) * r + pt * 16 + rr;
+    __hip_atomic_store(const_cast<uint64_t*>(f.sa.Pw) + o, (uint64_t{1} << 32) | __float_as_uint(v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();   // the LDS is reused for the resident tiles
+}
 
 // A helper's (max, index) for one token as one word: the value's bits in the
 // high half, the index in the low 24 bits, a tag (1) in the top 8 bits of
@@ -435,6 +495,8 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
   const LmArgs& a = f.la;
   const int h = bx < 8 * kTeam ? xq * (8 - nteam) + (x - nteam) : bx - kTeam * nteam;
   const int G = static_cast<int>(gridDim.x) - kTeam * nteam;
+  // the scan's input first: the team waits for it before its first step
+  if (f.nps > 0 && h < (a.r / 16) * f.nps) seqhead_p_partial(f, h, smem);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, grp = lane >> 4;
   const int r = a.r, V = a.V, M = a.M;
@@ -1010,14 +1072,36 @@ bool seqhead_fused(int B, int K, int r, bool bf16) {
 
 size_t seqhead_fold_bytes(int M) { return static_cast<size_t>(M) * kFuseMaxHelpers * sizeof(uint64_t); }
 
-hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, uint64_t* px, hipStream_t st) {
+namespace {
+// Grid of the fused kernel (one workgroup per CU, at least 8 per team member).
+int seqhead_grid(int B, int r) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const int team = scan_detail::team_size(r, B);
+  return cus > team * 8 ? cus : team * 8;
+}
+}  // namespace
+
+int seqhead_p_slices(int B, int K, int r, int D) {
+  if (!seqhead_fused(B, K, r, true) || D % 32) return 0;
+  const int G = seqhead_grid(B, r) - scan_detail::team_size(r, B) * B;
+  const int tiles = r / 16, nst = D / 32;
+  int nps = G / tiles;
+  nps = nps < 16 ? nps : 16;
+  // every wave's share of a slice fits its kPSteps registers
+  if (nps < 1 || (nst + nps - 1) / nps > kWaves * kPSteps) return 0;
+  return nps;
+}
+
+size_t seqhead_pw_bytes(int M, int r, int slices) {
+  return static_cast<size_t>(slices) * M * r * sizeof(uint64_t);
+}
+
+hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, uint64_t* px, const GemmArgs* ph, uint64_t* pw,
+                          hipStream_t st) {
   using namespace scan_detail;
   if (!seqhead_fused(s0.B, s0.K, s0.r, true) || l0.M != s0.B * s0.K || l0.tok0 != 0) return hipErrorInvalidValue;
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
   FuseArgs f{};
   f.sa = s0;
   f.sa.rpt = 1;
@@ -1025,18 +1109,29 @@ hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, uint64_t* px, hi
   f.nteam = s0.B;
   f.done = s0.counters + counter_seq_done();
   f.px = px;
+  if (ph) {
+    f.nps = seqhead_p_slices(s0.B, s0.K, s0.r, ph->K);
+    if (f.nps == 0 || !pw || ph->M != l0.M || ph->N != s0.r) return hipErrorInvalidValue;
+    f.ph = *ph;
+    f.sa.Pw = pw;
+    f.sa.Pslices = f.nps;
+  }
   const int team = team_size(s0.r, s0.B);
-  const int grid = cus > team * 8 ? cus : team * 8;
+  const int grid = seqhead_grid(s0.B, s0.r);
+  if (grid == 0) return hipErrorInvalidDevice;
   f.la = l0;
   f.la.G = grid - team * f.nteam;
   if (f.la.G > kFuseMaxHelpers) return hipErrorInvalidValue;
+  if (f.nps * (s0.r / 16) > f.la.G) return hipErrorInvalidValue;
   const int RK = s0.r / 32;
   const size_t sm_scan = team_lds(s0.r, team, 1, s0.K, true, &f.sa.stage);
   const void* fn = RK == 16 ? reinterpret_cast<const void*>(&seqhead_kernel<16>)
                             : reinterpret_cast<const void*>(&seqhead_kernel<10>);
   size_t sm = RK == 16 ? seqhead_lds<16>(l0.M, s0.r) : seqhead_lds<10>(l0.M, s0.r);
   sm = sm > sm_scan ? sm : sm_scan;
-  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
+  const size_t sm_p = (kWaves * 64 * 4 + 16) * sizeof(float);   // the P partial's reduction
+  sm = sm > sm_p ? sm : sm_p;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
   if (e != hipSuccess) return e;
   if (RK == 16) launch_k(seqhead_kernel<16>, dim3(grid), dim3(kWaves * 64), sm, st, f);
   else launch_k(seqhead_kernel<10>, dim3(grid), dim3(kWaves * 64), sm, st, f);

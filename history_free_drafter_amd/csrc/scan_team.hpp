@@ -216,6 +216,31 @@ __device__ __forceinline__ void scan_team(const ScanArgs& a, float* sm, int team
     const int bb = idx / (a.K * nr), k = (idx / nr) % a.K, i = idx % nr;
     return (bb * a.K + k) * 64 + i;
   };
+  // one P value: from P, or summed from the helpers' tagged k-slice partials
+  // (polled until every slice's word carries tag 1; bounded)
+  unsigned* pstatus = a.counters + CNT_STATUS;
+  auto load_p = [&](int idx) -> float {
+    const long o = p_index(idx);
+    if (!a.Pw) return a.P[o];
+    const long t = o / r, n = o % r;
+    const long stride = static_cast<long>(a.B) * a.K * r;
+    float v = 0.f;
+    for (int q = 0; q < a.Pslices; ++q) {
+      const uint64_t* w = a.Pw + q * stride + t * r + n;
+      uint64_t x = ld_tagged(w);
+      unsigned spins = 0;
+      while ((x >> 32) != 1u) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          atomicOr(pstatus, static_cast<unsigned>(STATUS_BARRIER_TIMEOUT));
+          break;
+        }
+        x = ld_tagged(w);
+      }
+      v += __uint_as_float(static_cast<uint32_t>(x));
+    }
+    return v;
+  };
   const int n_own = static_cast<int>(threadIdx.x) < r ? static_cast<int>(threadIdx.x) : 0;
   const int row_c = row < nr ? row : 0;
   bool staged = false;
@@ -229,12 +254,6 @@ __device__ __forceinline__ void scan_team(const ScanArgs& a, float* sm, int team
       // that the read-back of one chunk by 8 consecutive rows hits 8 different
       // bank groups.
       staged = true;
-      float pv[kPMax];
-#pragma unroll
-      for (int q = 0; q < kPMax; ++q) {
-        const int idx = static_cast<int>(threadIdx.x) + q * kThreads;
-        pv[q] = a.P[p_index(idx < np ? idx : np - 1)];
-      }
       const int cpr = nr / 8, cps = r / 8;    // 16-byte chunks of a W_up row slice / of a W_s row
       uint4* su = reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(sm) + a.stage);   // [r][8]
       uint4* sw = su + r * 8;                                                                   // [nr][cps]
@@ -245,6 +264,14 @@ __device__ __forceinline__ void scan_team(const ScanArgs& a, float* sm, int team
       for (int i = wave * 64; i < nr * cps; i += kThreads) {
         const int p = i + lane, rw = p / cps, c = (p % cps) ^ (rw & 7);
         if (rw < nr) load_lds16(Wd + static_cast<long>(r0 + rw) * ldd + a.D + c * 8, sw + i);
+      }
+      // the P values behind the weight slices (in the fused kernel they are
+      // still being computed by the helpers while the slices arrive)
+      float pv[kPMax];
+#pragma unroll
+      for (int q = 0; q < kPMax; ++q) {
+        const int idx = static_cast<int>(threadIdx.x) + q * kThreads;
+        pv[q] = (a.Pw && idx >= np) ? 0.f : load_p(idx < np ? idx : np - 1);
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       __syncthreads();
@@ -274,7 +301,7 @@ __device__ __forceinline__ void scan_team(const ScanArgs& a, float* sm, int team
 #pragma unroll
       for (int q = 0; q < kPMax; ++q) {
         const int idx = base + q * kThreads;
-        pv[q] = a.P[p_index(idx < np ? idx : np - 1)];   // clamped: unconditional loads
+        pv[q] = (a.Pw && idx >= np) ? 0.f : load_p(idx < np ? idx : np - 1);   // clamped: unconditional loads
       }
 #pragma unroll
       for (int q = 0; q < kPMax; ++q) {
