@@ -18,7 +18,7 @@ DLITE_F32, DLITE_BF16 = 0, 1
 ERRORS = {-1: "DLITE_ERR_NULL", -2: "DLITE_ERR_SHAPE", -3: "DLITE_ERR_DTYPE",
           -4: "DLITE_ERR_WORKSPACE", -5: "DLITE_ERR_UNSUPPORTED", -6: "DLITE_ERR_HIP"}
 EXPORTS = ["dlite_workspace_bytes", "dlite_draft_block", "dlite_draft_block_noalloc",
-           "dlite_draft_block_at",
+           "dlite_draft_block_at", "dlite_workspace_bytes_ex", "dlite_draft_block_ex",
            "dlite_draft_block_gated", "dlite_sampling_workspace_bytes", "dlite_sample_tokens",
            "dlite_accept_sampled", "dlite_accept_window",
            "dlite_accept_prefix", "dlite_draft_status", "dlite_set_stage_events",
@@ -47,6 +47,10 @@ class DliteWeights(Structure):
 
 class DliteGatedHead(Structure):
     _fields_ = [(n, c_void_p) for n in ("emb", "w_s", "b_s", "w_h", "b_h", "w_o")]
+
+
+class DliteBlockOptions(Structure):
+    _fields_ = [("group", c_int32), ("group_ids", c_void_p), ("warmup_ids", c_void_p)]
 
 
 class DliteTaps(Structure):
@@ -89,6 +93,13 @@ def load_library(path: str = LIB_PATH):
                                          c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                          POINTER(DliteTaps), c_void_p, c_size_t, c_void_p]
     lib.dlite_draft_block_at.restype = c_int
+    lib.dlite_workspace_bytes_ex.argtypes = [POINTER(DliteDims), POINTER(DliteBlockOptions)]
+    lib.dlite_workspace_bytes_ex.restype = c_size_t
+    lib.dlite_draft_block_ex.argtypes = [POINTER(DliteDims), POINTER(DliteWeights),
+                                         POINTER(DliteGatedHead), POINTER(DliteBlockOptions),
+                                         c_void_p, c_void_p, c_void_p, c_void_p,
+                                         POINTER(DliteTaps), c_void_p, c_size_t, c_void_p]
+    lib.dlite_draft_block_ex.restype = c_int
     lib.dlite_accept_window.argtypes = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p,
                                         c_void_p, c_void_p]
     lib.dlite_accept_window.restype = c_int
@@ -228,6 +239,35 @@ def dlite_draft_block_at(dims, weights, verify_hidden, T, accept_len, anchor_ids
         _ptr(anchor_ids), _ptr(candidates), _ptr(max_logit),
         ctypes.byref(taps) if taps is not None else None, _ptr(workspace), ws_bytes,
         _stream(stream))
+    _check(rc)
+
+
+def make_block_options(group=1, group_ids=None, warmup_ids=None) -> DliteBlockOptions:
+    """dlite_block_options: group length, [B, G-1] group ids, [B] warm-up ids (device)."""
+    return DliteBlockOptions(group, _ptr(group_ids), _ptr(warmup_ids))
+
+
+def dlite_workspace_bytes_ex(dims: DliteDims, opts=None) -> int:
+    n = load_library().dlite_workspace_bytes_ex(ctypes.byref(dims),
+                                                ctypes.byref(opts) if opts is not None else None)
+    if n == 0:
+        raise DliteError(-2, load_library().dlite_last_error().decode())
+    return n
+
+
+def dlite_draft_block_ex(dims, weights, head, opts, features, anchor_ids, candidates,
+                         max_logit=None, taps=None, workspace=None, workspace_bytes=None,
+                         stream=None):
+    """Enqueue a draft step with a local token group and/or the gated head's
+    warm-up token (head None: the fixed head); see include/dlite.h."""
+    ws_bytes = workspace_bytes
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load_library().dlite_draft_block_ex(
+        ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(head) if head is not None else None,
+        ctypes.byref(opts) if opts is not None else None, _ptr(features), _ptr(anchor_ids),
+        _ptr(candidates), _ptr(max_logit), ctypes.byref(taps) if taps is not None else None,
+        _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc)
 
 

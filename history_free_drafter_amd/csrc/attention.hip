@@ -1,17 +1,19 @@
-// Non-causal block attention over the m + 1 + K slots of one request.
+// Non-causal block attention over the m + G + K slots of one request.
 //
 // One workgroup per (request, group of HPW query heads of one key/value head):
-// the block is tiny (at most 81 keys and 17 query rows), so with few requests
+// the block is tiny (at most 96 keys and 32 query rows), so with few requests
 // the work is latency-bound and HPW = 1 spreads it over n_q * B workgroups;
 // with many requests HPW grows so that the heads sharing a key/value head
 // load and rotate it once.  A workgroup loads its key/value head and its query
 // rows once (all global loads issued up front), builds the rotation table for
-// local positions 0..K meanwhile, rotates keys and queries into LDS, then each
-// wave takes whole (head, query row) pairs: scores with one lane per key, the
-// softmax in registers (wave max and sum), and the weighted sum with one lane
-// per output element.  Local RoPE positions: context slots and the
-// anchor sit at 0, placeholder k at k (DLite walkthrough, Figure 3 layout);
-// nothing is kept after the call.
+// local positions 0..G+K-1 meanwhile, rotates keys and queries into LDS, then
+// each wave takes whole (head, query row) pairs: scores with one lane per key,
+// the softmax in registers (wave max and sum), and the weighted sum with one
+// lane per output element.  Local RoPE positions (DLite walkthrough, Figure 3
+// layout and "局部位置编码切断草稿端的全局位置增长"): the first real token of
+// the local group at 0, the anchor at n - 1 with every context slot, and
+// placeholder k at n - 1 + k (G = 1: all at 0 but placeholder k at k); group
+// padding slots are no keys.  Nothing is kept after the call.
 #include "kernels.hpp"
 
 namespace dlite {
@@ -21,20 +23,21 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kMaxD = 128;
 constexpr int kLd = kMaxD + 4;   // padded LDS row: 16-byte aligned, banks spread
-constexpr int kMaxS = 81;        // m <= 64, K <= 16
+constexpr int kMaxS = 96;        // m <= 64, G <= 16, K <= 16
 constexpr int kLoads = 4;        // 16-byte global loads per thread and pass
-
-__device__ __forceinline__ float rope_pos(int slot, int m) { return slot <= m ? 0.f : static_cast<float>(slot - m); }
 
 template <typename T, int DH>   // DH: head width (64 or 128), fixed so the dot products unroll
 __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   extern __shared__ __align__(16) float sm[];
   const int hpw = a.n_q / gridDim.x;          // query heads of this workgroup
   const int h0 = blockIdx.x * hpw, b = blockIdx.y;
-  const int G = a.n_q / a.n_kv, kvh = h0 / G;
+  const int qpk = a.n_q / a.n_kv, kvh = h0 / qpk;   // query heads per key/value head
   constexpr int d = DH, half = d / 2, hq = half / 4;   // float4 groups per half row
-  const int S = a.m + 1 + a.K, L = 1 + a.K;
+  const int S = a.m + a.G + a.K, L = a.G + a.K;
   const int Hq = a.n_q * d, Hkv = a.n_kv * d;
+  // group padding: slots m .. m + pad - 1 are no keys
+  const int pad = a.G > 1 ? group_pad(a.gids + static_cast<long>(b) * (a.G - 1), a.G) : 0;
+  const int nokey0 = a.m, nokey1 = a.m + pad;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int nw = kThreads / 64;
 
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
       hi[q] = *reinterpret_cast<const float4*>(p + off2);
     }
     if (ps == 0) {
-      // rotation table for local positions 0..K while the loads are in flight:
+      // rotation table for local positions 0..L-1 while the loads are in flight:
       // frequency i is theta^(-2 i / d)
       const float l2t = log2f(a.theta);
       for (int idx = threadIdx.x; idx < L * half; idx += kThreads) {
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
         // rotate pairs (i, i + half), i = 4 g .. 4 g + 3
         const bool key = it < nk;
         const int row = key ? it / hq : (it - nk) / hq, g = key ? it % hq : (it - nk) % hq;
-        const int pos = key ? static_cast<int>(rope_pos(row, a.m)) : row % L;
+        const int pos = group_position(key ? row : a.m + row % L, a.m, a.G, pad);
         const float* c = rc + pos * half + 4 * g;
         const float* sn = rs + pos * half + 4 * g;
         float* dst = (key ? Ks : Qs) + row * kLd + 4 * g;
@@ -113,8 +116,10 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
         *reinterpret_cast<float4*>(dst) = make_float4(y1[0], y1[1], y1[2], y1[3]);
         *reinterpret_cast<float4*>(dst + half) = make_float4(y2[0], y2[1], y2[2], y2[3]);
       } else {
-        const int t = it - nk - nq;
-        *reinterpret_cast<float4*>(Vs + (t / (d / 4)) * kLd + (t % (d / 4)) * 4) = lo[q];
+        const int t = it - nk - nq, row = t / (d / 4);
+        const bool key = row < nokey0 || row >= nokey1;   // padding values read as 0
+        *reinterpret_cast<float4*>(Vs + row * kLd + (t % (d / 4)) * 4) =
+            key ? lo[q] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
   }
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps) {
       const int s = lane + 64 * ps;
-      const bool ok = s < S;
+      const bool ok = s < S && (s < nokey0 || s >= nokey1);
       const float* kr = Ks + (ok ? s : 0) * kLd;
       float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -193,17 +198,17 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
 }
 
 size_t smem_hpw(const AttnArgs& a, int hpw) {
-  const int S = a.m + 1 + a.K, L = 1 + a.K;
+  const int S = a.m + a.G + a.K, L = a.G + a.K;
   return (static_cast<size_t>(2 * S * kLd) + hpw * L * kLd + hpw * L * (S + 1) + L * a.d_h) * 4;
 }
 
 // Query heads per workgroup: 1 while requests x key/value heads leave CUs
 // idle, else the largest divisor of the group size whose LDS fits.
 int pick_hpw(const AttnArgs& a) {
-  const int G = a.n_q / a.n_kv;
+  const int qpk = a.n_q / a.n_kv;
   if (static_cast<long>(a.B) * a.n_kv < 256) return 1;
-  for (int h = G; h > 1; --h)
-    if (G % h == 0 && smem_hpw(a, h) <= 160 * 1024) return h;
+  for (int h = qpk; h > 1; --h)
+    if (qpk % h == 0 && smem_hpw(a, h) <= 160 * 1024) return h;
   return 1;
 }
 
@@ -212,7 +217,8 @@ int pick_hpw(const AttnArgs& a) {
 size_t attention_smem(const AttnArgs& a) { return smem_hpw(a, pick_hpw(a)); }
 
 hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t st) {
-  if (a.m + 1 + a.K > kMaxS || a.d_h > kMaxD) return hipErrorInvalidValue;
+  if (a.G < 1 || a.m + a.G + a.K > kMaxS || a.d_h > kMaxD || (a.G > 1 && !a.gids))
+    return hipErrorInvalidValue;
   const dim3 grid(a.n_q / pick_hpw(a), a.B), block(kThreads);
   const size_t sm = attention_smem(a);
   if (a.d_h != 64 && a.d_h != 128) return hipErrorInvalidValue;

@@ -126,4 +126,28 @@ struct RowMap {
   }
 };
 
+// Local token group of one request (DLite walkthrough, section "局部位置编码
+// 切断草稿端的全局位置增长": the position builder may take a fixed-length group
+// of local tokens and puts the origin at the start of its valid part).  The
+// group is the G - 1 tokens before the anchor (oldest first, ids[0 .. G-2])
+// and the anchor; leading negative ids are padding (fewer tokens exist).
+// Returns the number of padding slots, 0 .. G - 1 (the anchor always counts).
+__device__ __forceinline__ int group_pad(const int32_t* ids, int G) {
+  int pad = 0;
+  while (pad < G - 1 && ids[pad] < 0) ++pad;
+  return pad;
+}
+
+// Local position of slot s of a request with m feature slots, a group of G
+// slots (pad of them padding) and placeholders after it: the first real group
+// token at 0, the anchor at n - 1 (n = G - pad real tokens), the feature slots
+// with the anchor, placeholder k (slot m + G - 1 + k) at n - 1 + k.  Padding
+// slots are no keys; their position is 0.  G = 1 is the Figure 3 layout.
+__device__ __forceinline__ int group_position(int s, int m, int G, int pad) {
+  const int n = G - pad;
+  if (s < m) return n - 1;
+  if (s < m + G) return s - m >= pad ? s - m - pad : 0;
+  return n - 1 + (s - m - G + 1);
+}
+
 }  // namespace dlite

@@ -57,9 +57,25 @@ int ok() {
 
 size_t esize(const dlite_dims& d) { return d.dtype == DLITE_BF16 ? 2 : 4; }
 
+// Options of one draft step (dlite_block_options, checked).
+struct Opts {
+  int G = 1;                         // local token group length
+  const int32_t* gids = nullptr;     // [B, G - 1] the tokens before the anchor
+  const int32_t* warm = nullptr;     // [B] gated head: warm-up tokens, or null
+};
+
+// NULL options: the defaults; a group of 0 means 1.
+void read_opts(const dlite_block_options* o, Opts* out) {
+  *out = Opts{};
+  if (!o) return;
+  out->G = o->group == 0 ? 1 : o->group;
+  out->gids = out->G > 1 ? o->group_ids : nullptr;
+  out->warm = o->warmup_ids;
+}
+
 // Workspace regions, each 256-byte aligned.
 struct Plan {
-  size_t counters, X, XB, XF, SSQ, Q, KV, AO, ACT, P, U, Sf, Sb, GR, GT, pmax, pidx, TP, SP, total;
+  size_t counters, X, XB, XF, SSQ, Q, KV, AO, ACT, P, U, Sf, Sb, GR, GT, WS, pmax, pidx, TP, SP, total;
   int G;
 };
 
@@ -67,9 +83,9 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 // Partial-tile scratch of the tiled GEMMs: the largest need of any launch of
 // the step (the same tile plan the launches use).
-size_t tile_scratch_bytes(const dlite_dims& d) {
+size_t tile_scratch_bytes(const dlite_dims& d, int G) {
   if (d.dtype != DLITE_BF16) return 0;
-  const int B = d.B, S = d.m + 1 + d.K, L = 1 + d.K, K = d.K, D = d.D, F = d.ffn, r = d.rank;
+  const int B = d.B, S = d.m + G + d.K, L = G + d.K, K = d.K, D = d.D, F = d.ffn, r = d.rank;
   const int Hq = d.n_q * d.d_h, Hkv2 = 2 * d.n_kv * d.d_h;
   auto one = [&](int M0, int M1, int N0, int N1, int Kd, int epi) -> size_t {
     const int mx = M0 > M1 ? M0 : M1;
@@ -94,9 +110,9 @@ size_t tile_scratch_bytes(const dlite_dims& d) {
 // k-slice partials of the weight-streaming GEMMs: the largest need of any
 // launch of the step (launches of at most 32 tokens, the same decisions the
 // launchers take).
-size_t stream_scratch_bytes(const dlite_dims& d) {
+size_t stream_scratch_bytes(const dlite_dims& d, int G) {
   const bool bf16 = d.dtype == DLITE_BF16;
-  const int B = d.B, S = d.m + 1 + d.K, L = 1 + d.K, K = d.K, D = d.D, F = d.ffn, r = d.rank;
+  const int B = d.B, S = d.m + G + d.K, L = G + d.K, K = d.K, D = d.D, F = d.ffn, r = d.rank;
   const int Hq = d.n_q * d.d_h, Hkv2 = 2 * d.n_kv * d.d_h;
   auto tiled = [&](int M, int Kd) { GemmArgs g{}; g.M = M; g.K = Kd; return gemm_tiled(g, bf16); };
   auto c32 = [](int M) { return M < 32 ? M : 32; };
@@ -118,8 +134,8 @@ size_t stream_scratch_bytes(const dlite_dims& d) {
   return need;
 }
 
-Plan make_plan(const dlite_dims& d) {
-  const size_t B = d.B, S = d.m + 1 + d.K, L = 1 + d.K, D = d.D;
+Plan make_plan(const dlite_dims& d, int G = 1) {
+  const size_t B = d.B, S = d.m + G + d.K, L = G + d.K, D = d.D;
   const size_t Hq = static_cast<size_t>(d.n_q) * d.d_h, Hkv = static_cast<size_t>(d.n_kv) * d.d_h;
   const size_t F = d.ffn, K = d.K, r = d.rank, es = esize(d);
   Plan p{};
@@ -150,16 +166,18 @@ Plan make_plan(const dlite_dims& d) {
   p.Sb = take(B * K * r * es);
   p.GR = take(B * r * es);        // gated head: r_i of the current step
   p.GT = take(B * 4);             // gated head: d_i of the current step
+  p.WS = take(B * r * 4);         // gated head: warm-up state
   p.pmax = take(B * K * Gmax * 4);
   p.pidx = take(B * K * Gmax * 4);
-  p.TP = take(tile_scratch_bytes(d));
-  p.SP = take(stream_scratch_bytes(d));
+  p.TP = take(tile_scratch_bytes(d, G));
+  p.SP = take(stream_scratch_bytes(d, G));
   p.total = off;
   return p;
 }
 
-int check_dims(const dlite_dims* dp) {
+int check_dims(const dlite_dims* dp, int G = 1) {
   if (!dp) return fail(DLITE_ERR_NULL, "dims is NULL");
+  if (G < 1 || G > 16) return fail(DLITE_ERR_SHAPE, "group=%d not in [1, 16]", G);
   const dlite_dims& d = *dp;
   if (d.dtype != DLITE_F32 && d.dtype != DLITE_BF16)
     return fail(DLITE_ERR_DTYPE, "dtype %d is neither DLITE_F32 nor DLITE_BF16", d.dtype);
@@ -186,10 +204,10 @@ int check_dims(const dlite_dims* dp) {
     return fail(DLITE_ERR_UNSUPPORTED, "D=%d too large for the feature kernel", d.D);
   {
     AttnArgs aa{};
-    aa.n_q = d.n_q; aa.n_kv = d.n_kv; aa.m = d.m; aa.K = d.K; aa.d_h = d.d_h;
+    aa.n_q = d.n_q; aa.n_kv = d.n_kv; aa.m = d.m; aa.K = d.K; aa.d_h = d.d_h; aa.G = G;
     if (attention_smem(aa) > 160 * 1024)
-      return fail(DLITE_ERR_UNSUPPORTED, "attention block too large for LDS (m=%d, K=%d, n_q/n_kv=%d)",
-                  d.m, d.K, d.n_q / d.n_kv);
+      return fail(DLITE_ERR_UNSUPPORTED, "attention block too large for LDS (m=%d, G=%d, K=%d, n_q/n_kv=%d)",
+                  d.m, G, d.K, d.n_q / d.n_kv);
   }
   if (!(d.rms_eps >= 0.f) || !std::isfinite(d.rms_eps))
     return fail(DLITE_ERR_SHAPE, "rms_eps must be finite and >= 0");
@@ -231,7 +249,7 @@ struct FeatureSource {
 // The draft step with the boundary features read through `fs` (both entry
 // points; dims and the feature pointer are checked by the caller).
 int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSource& fs,
-               const dlite_gated_head* gh, const int32_t* anchor_ids, int32_t* candidates,
+               const dlite_gated_head* gh, const Opts& op, const int32_t* anchor_ids, int32_t* candidates,
                float* max_logit, const dlite_taps* taps, void* workspace, size_t workspace_bytes,
                hipStream_t st) {
   const dlite_dims& d = *dims;
@@ -271,13 +289,16 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   if (!workspace) return fail(DLITE_ERR_NULL, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(DLITE_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
-  const Plan p = make_plan(d);
+  if (op.G > 1 && !op.gids) return fail(DLITE_ERR_NULL, "options.group_ids is NULL with group=%d", op.G);
+  if (op.warm && !gh) return fail(DLITE_ERR_UNSUPPORTED, "a warm-up token needs the gated head");
+  const Plan p = make_plan(d, op.G);
   if (workspace_bytes < p.total)
     return fail(DLITE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, p.total);
 
   const bool bf16 = d.dtype == DLITE_BF16;
   const size_t es = esize(d);
-  const int B = d.B, m = d.m, K = d.K, D = d.D, S = m + 1 + K, L = 1 + K;
+  const int G = op.G;
+  const int B = d.B, m = d.m, K = d.K, D = d.D, S = m + G + K, L = G + K;
   const int Hq = d.n_q * d.d_h, Hkv = d.n_kv * d.d_h, F = d.ffn, r = d.rank;
   char* ws = static_cast<char*>(workspace);
   unsigned* counters = reinterpret_cast<unsigned*>(ws + p.counters);
@@ -305,7 +326,7 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   // (the feature kernel writes one)
   int local_parts = 1;
 
-  // 1. feature slots, anchor and placeholder rows, first GEMM inputs
+  // 1. feature slots, group (anchor) and placeholder rows, first GEMM inputs
   //    (also clears the counters)
   FeatureArgs fa{};
   fa.H = fs.H; fa.h_sb = fs.sb; fa.h_sl = fs.sl; fa.h_st = fs.st; fa.h_pos = fs.pos; fa.h_T = fs.T;
@@ -322,7 +343,7 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   const size_t pw_bytes = p_slices ? seqhead_pw_bytes(B * K, r, p_slices) : 0;
   fa.n_clear = static_cast<long>((scan_scratch_floats(B, r) * sizeof(float) + fold_bytes + pw_bytes) / 16);
   fa.B = B; fa.m = m; fa.K = K; fa.D = D; fa.V = d.vocab; fa.n_layers = d.n_layers;
-  fa.eps = d.rms_eps;
+  fa.eps = d.rms_eps; fa.G = G; fa.gids = op.gids;
   DLITE_LAUNCH(mark(DLITE_STAGE_FEATURES, true, st));
   DLITE_LAUNCH(launch_feature(fa, bf16, st));
   DLITE_LAUNCH(mark(DLITE_STAGE_FEATURES, false, st));
@@ -330,8 +351,8 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   // 2. backbone layers
   for (int l = 0; l < d.n_layers; ++l) {
     const dlite_layer_weights& lw = w->layers[l];
-    // the anchor row of the last layer feeds nothing downstream
-    const int q0 = (l == d.n_layers - 1) ? 1 : 0;
+    // the group rows of the last layer feed nothing downstream
+    const int q0 = (l == d.n_layers - 1) ? G : 0;
     const int Lr = L - q0;
     const RowMap slot_rows{Lr, S, m + q0}, local_rows{Lr, L, q0}, all_slots{S, S, 0};
     const void* xb = XB + l * xb_layer;
@@ -351,6 +372,7 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
     DLITE_LAUNCH(mark(DLITE_STAGE_QKV, false, st, l));
 
     AttnArgs aa{Qb, KVb, AO, B, m, K, d.n_q, d.n_kv, d.d_h, q0, d.rope_theta};
+    aa.G = G; aa.gids = op.gids;
     DLITE_LAUNCH(mark(DLITE_STAGE_ATTENTION, true, st, l));
     DLITE_LAUNCH(launch_attention(aa, bf16, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_ATTENTION, false, st, l));
@@ -395,12 +417,13 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   DLITE_LAUNCH(mark(DLITE_STAGE_FINAL_NORM, true, st));
   if (tp.hidden) {
     NormArgs na{X, w->final_norm, tp.hidden, B, m, K, D, d.rms_eps};
+    na.G = G;
     DLITE_LAUNCH(launch_hidden_tap(na, bf16, st));
   }
   DLITE_LAUNCH(mark(DLITE_STAGE_FINAL_NORM, false, st));
 
   // 4. hidden part of the sequential head's input projection, all B*K rows at once
-  const RowMap ph_rows{K, S, m + 1};
+  const RowMap ph_rows{K, S, m + G};
   GemmArgs ph{};
   // fixed head: W_down[:, :D] h (hidden columns first); gated head:
   // W_h[:, R:] u (state columns first)
@@ -433,6 +456,13 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
     // tokens feed the next step (stage events: the first step)
     float* Sst = tp.state ? tp.state : Sf;
     int32_t* GT = reinterpret_cast<int32_t*>(ws + p.GT);
+    float* Sw = op.warm ? reinterpret_cast<float*>(ws + p.WS) : nullptr;
+    // warm-up: one state update from s = 0 with the token before the anchor
+    // (no output), so that position 1 starts from that state
+    GatedArgs gw{};
+    gw.emb = gh->emb; gw.w_s = gh->w_s; gw.b_s = gh->b_s; gw.w_h = gh->w_h; gw.b_h = gh->b_h;
+    gw.tok = op.warm; gw.s_prev = nullptr; gw.s_out = Sw; gw.ld_s = r; gw.ld_sp = r; gw.warm = 1;
+    gw.B = B; gw.R = r; gw.V = d.vocab; gw.D = D;
     const bool fused = gatedhead_fused(B, K, r, d.vocab, bf16) &&
                        gatedhead_exchange_bytes(B, r) <= scan_scratch_floats(B, r) * sizeof(float);
     if (fused) {
@@ -446,7 +476,9 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
       gf.la = la;
       gf.la.W = gh->w_o; gf.la.M = B; gf.la.tok0 = 0;
       gf.B = B; gf.K = K; gf.D = D;
+      gf.s_init = Sw;
       DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
+      if (Sw) DLITE_LAUNCH(launch_gated_step(gw, bf16, st));
       DLITE_LAUNCH(launch_gatedhead(gf, st));
       DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st));
       DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, true, st));
@@ -456,14 +488,16 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
       GatedArgs ga{};
       ga.emb = gh->emb; ga.w_s = gh->w_s; ga.b_s = gh->b_s; ga.w_h = gh->w_h; ga.b_h = gh->b_h;
       ga.tok = i == 0 ? anchor_ids : GT;
-      ga.s_prev = i == 0 ? nullptr : Sst + static_cast<size_t>(i - 1) * r;
+      ga.s_prev = i == 0 ? Sw : Sst + static_cast<size_t>(i - 1) * r;
       ga.s_out = Sst + static_cast<size_t>(i) * r;
       ga.ld_s = static_cast<long>(K) * r;
+      ga.ld_sp = i == 0 ? r : ga.ld_s;
       ga.qh = P + static_cast<size_t>(i) * r;
       ga.ld_q = static_cast<long>(K) * r;
       ga.r_out = ws + p.GR;
       ga.B = B; ga.R = r; ga.V = d.vocab; ga.D = D;
       DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st, i));
+      if (i == 0 && Sw) DLITE_LAUNCH(launch_gated_step(gw, bf16, st));
       DLITE_LAUNCH(launch_gated_step(ga, bf16, st));
       DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st, i));
       LmArgs lg = la;
@@ -560,7 +594,7 @@ int dlite_draft_block(const dlite_dims* dims, const dlite_weights* w, const void
   DLITE_TRY(check_ptr(features, "features"));
   const long D = dims->D;
   const FeatureSource fs{features, static_cast<long>(dims->m) * D, D, 0, nullptr, 1};
-  return draft_impl(dims, w, fs, nullptr, anchor_ids, candidates, max_logit, taps, workspace,
+  return draft_impl(dims, w, fs, nullptr, Opts{}, anchor_ids, candidates, max_logit, taps, workspace,
                     workspace_bytes, st);
 }
 
@@ -578,7 +612,7 @@ int dlite_draft_block_noalloc(const dlite_dims* dims, const dlite_weights* w, co
   DLITE_TRY(static_scratch(&ws));
   const long D = dims->D;
   const FeatureSource fs{features, static_cast<long>(dims->m) * D, D, 0, nullptr, 1};
-  DLITE_TRY(draft_impl(dims, w, fs, nullptr, anchor_ids, candidates, max_logit, taps, ws,
+  DLITE_TRY(draft_impl(dims, w, fs, nullptr, Opts{}, anchor_ids, candidates, max_logit, taps, ws,
                        kStaticScratchBytes, st));
   if (status) DLITE_LAUNCH(launch_status_copy(static_cast<const unsigned*>(ws) + CNT_STATUS, status, st));
   return ok();
@@ -593,7 +627,29 @@ int dlite_draft_block_gated(const dlite_dims* dims, const dlite_weights* w, cons
   DLITE_TRY(check_ptr(features, "features"));
   const long D = dims->D;
   const FeatureSource fs{features, static_cast<long>(dims->m) * D, D, 0, nullptr, 1};
-  return draft_impl(dims, w, fs, head, anchor_ids, candidates, max_logit, taps, workspace,
+  return draft_impl(dims, w, fs, head, Opts{}, anchor_ids, candidates, max_logit, taps, workspace,
+                    workspace_bytes, st);
+}
+
+size_t dlite_workspace_bytes_ex(const dlite_dims* dims, const dlite_block_options* opts) {
+  Opts op;
+  read_opts(opts, &op);
+  if (check_dims(dims, op.G) != DLITE_OK) return 0;
+  ok();
+  return make_plan(*dims, op.G).total;
+}
+
+int dlite_draft_block_ex(const dlite_dims* dims, const dlite_weights* w, const dlite_gated_head* head,
+                         const dlite_block_options* opts, const void* features, const int32_t* anchor_ids,
+                         int32_t* candidates, float* max_logit, const dlite_taps* taps, void* workspace,
+                         size_t workspace_bytes, hipStream_t st) {
+  Opts op;
+  read_opts(opts, &op);
+  DLITE_TRY(check_dims(dims, op.G));
+  DLITE_TRY(check_ptr(features, "features"));
+  const long D = dims->D;
+  const FeatureSource fs{features, static_cast<long>(dims->m) * D, D, 0, nullptr, 1};
+  return draft_impl(dims, w, fs, head, op, anchor_ids, candidates, max_logit, taps, workspace,
                     workspace_bytes, st);
 }
 
@@ -609,7 +665,7 @@ int dlite_draft_block_at(const dlite_dims* dims, const dlite_weights* w, const v
   // [m, B, T, D]: layer l of request b at verify index A_b
   const FeatureSource fs{verify_hidden, static_cast<long>(T) * D, static_cast<long>(dims->B) * T * D, D,
                          accept_len, T};
-  return draft_impl(dims, w, fs, nullptr, anchor_ids, candidates, max_logit, taps, workspace,
+  return draft_impl(dims, w, fs, nullptr, Opts{}, anchor_ids, candidates, max_logit, taps, workspace,
                     workspace_bytes, st);
 }
 

@@ -11,6 +11,8 @@
 //           s_i = sigmoid(g) * s_{i-1} + (1 - sigmoid(g)) * tanh(c)   (fp32)
 //   output: r_i = W_h[:, :R] s_i + qh_i + b_h   (storage type, the
 //           vocabulary pass's input)
+// A warm-up update (the token before the anchor, same section) runs the state
+// launch alone from s = 0, before position 1.
 // One wave per output element (rows j and R + j of W_s; row j of W_h) holds
 // its weight rows in registers and serves a chunk of requests whose inputs
 // are staged in LDS; weights are read once per request chunk.
@@ -38,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void gated_state_kernel(GatedArgs a) {
     const int bb = e / R2, k = e % R2, b = b0 + bb;
     float v = 0.f;
     if (k < R) {
-      if (a.s_prev) v = a.s_prev[b * a.ld_s + k];
+      if (a.s_prev) v = a.s_prev[b * a.ld_sp + k];
     } else {
       const int d = a.tok[b];
       if (d >= 0 && d < a.V) v = Elem<T>::to_f32(emb[static_cast<long>(d) * R + (k - R)]);
@@ -82,8 +84,9 @@ __global__ __launch_bounds__(kThreads) void gated_state_kernel(GatedArgs a) {
     if (lane == 0) {
       const int b = b0 + bb;
       const float f = 1.0f / (1.0f + expf(-(dg + bg)));
-      const float sp = a.s_prev ? a.s_prev[b * a.ld_s + j] : 0.f;
-      a.s_out[b * a.ld_s + j] = f * sp + (1.0f - f) * tanhf(dc + bc);
+      const float sp = a.s_prev ? a.s_prev[b * a.ld_sp + j] : 0.f;
+      const bool skip = a.warm && !(a.tok[b] >= 0 && a.tok[b] < a.V);   // no token to warm up with
+      a.s_out[b * a.ld_s + j] = skip ? 0.f : f * sp + (1.0f - f) * tanhf(dc + bc);
     }
   }
 }
@@ -144,10 +147,10 @@ hipError_t launch_gated_step(const GatedArgs& a, bool bf16, hipStream_t st) {
   const size_t sm_out = static_cast<size_t>(kChunk) * a.R * sizeof(float);
   if (bf16) {
     launch_k(gated_state_kernel<uint16_t>, grid, block, sm_state, st, a);
-    launch_k(gated_out_kernel<uint16_t>, grid, block, sm_out, st, a);
+    if (!a.warm) launch_k(gated_out_kernel<uint16_t>, grid, block, sm_out, st, a);
   } else {
     launch_k(gated_state_kernel<float>, grid, block, sm_state, st, a);
-    launch_k(gated_out_kernel<float>, grid, block, sm_out, st, a);
+    if (!a.warm) launch_k(gated_out_kernel<float>, grid, block, sm_out, st, a);
   }
   return hipGetLastError();
 }

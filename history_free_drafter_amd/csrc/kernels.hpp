@@ -93,6 +93,8 @@ struct FeatureArgs {
   long n_clear;
   int B, m, K, D, V, n_layers;
   float eps;
+  int G = 1;                        // local token group length (slots m .. m + G - 1)
+  const int32_t* gids = nullptr;    // [B, G - 1] the tokens before the anchor (G > 1)
 };
 hipError_t launch_feature(const FeatureArgs& a, bool bf16, hipStream_t st);
 
@@ -168,8 +170,10 @@ struct AttnArgs {
   const float* Q;   // [B, L, n_q d_h]
   const float* KV;  // [B, S, 2 n_kv d_h] (k heads, then v heads)
   void* out;        // [B, L, n_q d_h] storage type
-  int B, m, K, n_q, n_kv, d_h, q0;  // rows j = q0..K of each request are computed
+  int B, m, K, n_q, n_kv, d_h, q0;  // local rows j = q0 .. G + K - 1 are computed
   float theta;
+  int G = 1;                        // local token group length
+  const int32_t* gids = nullptr;    // [B, G - 1] the tokens before the anchor (G > 1)
 };
 hipError_t launch_attention(const AttnArgs& a, bool bf16, hipStream_t st);
 size_t attention_smem(const AttnArgs& a);   // dynamic LDS bytes of one workgroup
@@ -181,6 +185,7 @@ struct NormArgs {
   const void* gain;   // [D]
   float* tap;         // [B, K, D]
   int B, m, K, D; float eps;
+  int G = 1;          // local token group length (placeholders from slot m + G)
 };
 hipError_t launch_hidden_tap(const NormArgs& a, bool bf16, hipStream_t st);
 
@@ -255,9 +260,10 @@ struct GatedArgs {
   const void* w_h;        // [R, R + D]: columns state then backbone row
   const void* b_h;        // [R]
   const int32_t* tok;     // [B] d_{i-1}; ids outside [0, V) read a zero row
-  const float* s_prev;    // row b at s_prev + b ld_s; null: s_0 = 0
+  const float* s_prev;    // row b at s_prev + b ld_sp; null: s_0 = 0
   float* s_out;           // row b at s_out + b ld_s
-  long ld_s;
+  long ld_s, ld_sp;
+  int warm;               // warm-up update: a token outside [0, V) leaves s = 0
   const float* qh;        // W_h[:, R:] u_i: row b at qh + b ld_q
   long ld_q;
   void* r_out;            // [B, R] storage type
@@ -271,6 +277,7 @@ hipError_t launch_gated_step(const GatedArgs& a, bool bf16, hipStream_t st);
 struct GatedFuseArgs {
   const void* emb; const void* w_s; const void* b_s; const void* w_h; const void* b_h;
   const int32_t* anchors;   // [B] d_0
+  const float* s_init;      // [B, R] state before position 1 (warm-up) or null: 0
   const float* qh;          // [B K, R] W_h[:, R:] u
   float* s_out;             // [B K, R] states
   uint64_t* sx;             // [B, R]   tagged state words (team exchange)

@@ -478,7 +478,6 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float sv[kWaves][16];
   __shared__ int si[kWaves][16];
-  __shared__ int last;
 
   const int bx = blockIdx.x, xq = bx >> 3, x = bx & 7;
   const int nteam = f.nteam;
@@ -669,7 +668,8 @@ size_t seqhead_lds(int M, int r) {
 // TR of them per wave in registers and TL per workgroup in LDS for the whole
 // launch; only the remainder (touched into L2 before the first position) is
 // re-read at each position.  Sixteen team workgroups run the state updates.
-// Per position i (tag i + 1):
+// Per position i (tag i + 1; s_0 = 0, or the warm-up state computed before
+// the launch):
 //   team     d_{i-1} (the anchor at i = 0) -> v_i = E_R(d_{i-1});
 //            [g; c] = W_s [s_{i-1}; v_i] + b_s and the gate for its 32 state
 //            elements, published as tagged words; all R read back;
@@ -832,7 +832,7 @@ __device__ __forceinline__ void gated_team(const GatedFuseArgs& f, unsigned char
     for (int e = threadIdx.x; e < B * R; e += blockDim.x) {
       const int b = e / R, k = e % R;
       const int d = dsh[b];
-      xs[b * R2 + k] = i == 0 ? 0.f : ss[e];
+      xs[b * R2 + k] = i == 0 ? (f.s_init ? f.s_init[e] : 0.f) : ss[e];
       xs[b * R2 + R + k] = (d >= 0 && d < V) ? bf16_to_f32(E[static_cast<long>(d) * R + k]) : 0.f;
     }
     __syncthreads();

@@ -1,11 +1,14 @@
 // Row-wise kernels of the draft step: building the slot buffer (depth-embedded,
-// RMS-normalised context features, anchor embedding, placeholders) with the
-// first GEMM inputs, and the optional fp32 copy of the final-normed hidden rows.
+// RMS-normalised context features, anchor or local token group embeddings,
+// placeholders) with the first GEMM inputs, and the optional fp32 copy of the
+// final-normed hidden rows.
 //
 // Feature slots follow the DLite walkthrough, section "历史并没有消失，而是由目标
 // 模型编码" (z = Norm(h^(l) + e_depth^(l))), kept as m separate sequence slots
-// ("沿序列维拼接，保留各层的独立身份").  The anchor enters through its token
-// embedding and the K placeholders through one shared input vector.
+// ("沿序列维拼接，保留各层的独立身份").  The anchor (or a local group of G
+// tokens ending at it, section "锚点是已经确定、尚待目标前向处理的输入") enters
+// through its token embeddings and the K placeholders through one shared input
+// vector.  Slot order per request: m features, G group tokens, K placeholders.
 #include "kernels.hpp"
 
 namespace dlite {
@@ -31,10 +34,10 @@ __device__ __forceinline__ float ld(const void* p, long i) {
 }
 
 // One workgroup per slot (b, s).  Writes the row's sum of squares (slot 0 of
-// the row's partials), the fp32 residual row of anchor and placeholder slots
+// the row's partials), the fp32 residual row of group and placeholder slots
 // (context slots are key/value inputs only and never updated), and the
 // pre-gained GEMM input rows:
-// context slots for every layer (they do not change between layers), anchor
+// context slots for every layer (they do not change between layers), group
 // and placeholder rows for the first layer.  Each thread holds its share of
 // the row in registers (16-byte loads, all issued before the reduction).
 constexpr int kMaxVec = 8;   // 16-byte vectors per thread: D <= 8 * 256 * 8
@@ -48,7 +51,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
   constexpr int PER = Elem<T>::kPerLane;
   __shared__ float sh[kThreads / 64];
-  const int S = a.m + 1 + a.K;
+  const int S = a.m + a.G + a.K;
   const int b = blockIdx.x / S, s = blockIdx.x % S;
   const long row = blockIdx.x;
   float* x = a.X + row * a.D;
@@ -70,10 +73,13 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
     src = static_cast<const T*>(a.H) + static_cast<long>(b) * a.h_sb + static_cast<long>(s) * a.h_sl +
           static_cast<long>(pos) * a.h_st;
     add = static_cast<const T*>(a.depth_emb) + static_cast<long>(s) * a.D;
-  } else if (s == a.m) {
-    const int tok = a.anchors[b];
+  } else if (s < a.m + a.G) {
+    // group token j (j = G - 1: the anchor); padding and out-of-range ids: zero row
+    const int j = s - a.m;
+    const int32_t* ids = a.gids + static_cast<long>(b) * (a.G - 1);
+    const int tok = j == a.G - 1 ? a.anchors[b] : (j >= group_pad(ids, a.G) ? ids[j] : -1);
     src = (tok >= 0 && tok < a.V) ? static_cast<const T*>(a.tok_emb) + static_cast<long>(tok) * a.D
-                                  : nullptr;   // out of range: zero input row
+                                  : nullptr;
   } else {
     src = static_cast<const T*>(a.ph_emb);
   }
@@ -118,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
         v[t] = add ? gz[t] * ((h[t] + e[t]) * inv) : h[t];
         ss += v[t] * v[t];
       }
-      if (!add) {   // residual stream: anchor and placeholder rows only
+      if (!add) {   // residual stream: group and placeholder rows only
         float* xo = x + idx * PER;
 #pragma unroll
         for (int t = 0; t < PER; t += 4)
@@ -156,9 +162,9 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
 template <typename T>
 __global__ __launch_bounds__(kThreads) void hidden_tap_kernel(NormArgs a) {
   __shared__ float sh[kThreads / 64];
-  const int S = a.m + 1 + a.K;
+  const int S = a.m + a.G + a.K;
   const int b = blockIdx.x / a.K, k = blockIdx.x % a.K;
-  const float* x = a.X + (static_cast<long>(b) * S + a.m + 1 + k) * a.D;
+  const float* x = a.X + (static_cast<long>(b) * S + a.m + a.G + k) * a.D;
   float ss = 0.f;
   for (int e = threadIdx.x; e < a.D; e += blockDim.x) ss += x[e] * x[e];
   const float inv = 1.0f / sqrtf(block_sum(ss, sh) / static_cast<float>(a.D) + a.eps);
@@ -169,7 +175,8 @@ __global__ __launch_bounds__(kThreads) void hidden_tap_kernel(NormArgs a) {
 }  // namespace
 
 hipError_t launch_feature(const FeatureArgs& a, bool bf16, hipStream_t st) {
-  const dim3 grid(a.B * (a.m + 1 + a.K)), block(kThreads);
+  if (a.G < 1 || (a.G > 1 && !a.gids)) return hipErrorInvalidValue;
+  const dim3 grid(a.B * (a.m + a.G + a.K)), block(kThreads);
   if (bf16)
     launch_k(feature_kernel<uint16_t>, grid, block, 0, st, a);
   else

@@ -82,6 +82,22 @@ class DraftModel:
                                 self.workspace, self.ws_bytes, stream)
         return self.candidates
 
+    def draft_ex(self, features: torch.Tensor, anchors: torch.Tensor, group_ids=None,
+                 warmup_ids=None, gated=False, taps=None, stream=None):
+        """Draft with a local token group (group_ids [B, G-1] int32: the tokens
+        before each anchor, leading negatives = padding) and/or the gated head's
+        warm-up token (warmup_ids [B] int32).  The workspace grows on demand."""
+        G = 1 if group_ids is None else int(group_ids.shape[1]) + 1
+        opts = _b.make_block_options(G, group_ids, warmup_ids)
+        need = _b.dlite_workspace_bytes_ex(self.dims, opts)
+        if need > self.ws_bytes:
+            self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self.ws_bytes = need
+        _b.dlite_draft_block_ex(self.dims, self.wstruct, self.ghstruct if gated else None, opts,
+                                features, anchors, self.candidates, self.max_logit, taps,
+                                self.workspace, self.ws_bytes, stream)
+        return self.candidates
+
     def accept(self, target_tokens: torch.Tensor, stream=None):
         B, K = self.shape["B"], self.shape["K"]
         _b.dlite_accept_prefix(self.candidates, target_tokens, B, K, self.accept_len,

@@ -129,9 +129,11 @@ typedef struct dlite_gated_head {
  * run either way; hidden (which the fast path never forms in fp32: the final
  * RMSNorm is folded into the GEMMs around it) adds one small kernel.
  *   z       [B, m, D]               normalised, depth-embedded feature slots
- *   x       [n_layers, B, 1 + K, D] anchor + placeholder residual stream after
- *                                   each layer (the anchor row of the last
- *                                   layer is not computed and is left as is)
+ *   x       [n_layers, B, G + K, D] group (G = 1: the anchor) + placeholder
+ *                                   residual stream after each layer (the
+ *                                   group rows of the last layer are not
+ *                                   computed and are left as is; padding rows
+ *                                   of a token group hold no defined value)
  *   hidden  [B, K, D]               h_k after the final RMSNorm
  *   state   [B, K, r]               sequential-head states s_1..s_K
  *   logits  [B, K, V]               vocabulary logits
@@ -233,6 +235,62 @@ int dlite_draft_block_gated(const dlite_dims *dims, const dlite_weights *weights
                             const int32_t *anchor_ids, int32_t *candidates, float *max_logit,
                             const dlite_taps *taps, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/*
+ * Options of dlite_draft_block_ex.  A zeroed struct (or NULL) is the plain
+ * step of dlite_draft_block / dlite_draft_block_gated.
+ *
+ * group       G in [0, 16] (0 and 1: the anchor alone).  The local input is a
+ *             token group: the G - 1 tokens before the anchor and the anchor
+ *             ([W] "锚点是已经确定、尚待目标前向处理的输入": the draft input
+ *             holds the anchor or a fixed-length local token group;
+ *             "局部位置编码切断草稿端的全局位置增长": the origin of the local
+ *             positions is the start of the group's valid part).
+ * group_ids   [B, G - 1] int32, device (read when G > 1): the tokens before
+ *             each anchor, oldest first.  Leading ids < 0 are padding (the
+ *             sequence holds fewer tokens): padding slots are neither keys nor
+ *             read.  Any other id outside [0, V) gives a zero input row.
+ *             With n = G - padding real tokens: group token j sits at local
+ *             position j - padding (the anchor at n - 1), every feature slot at
+ *             n - 1, placeholder k at n - 1 + k.  All G group rows query and
+ *             are updated in every layer like the anchor row (rows of the
+ *             group are local rows); only placeholders are drafted.
+ * warmup_ids  [B] int32, device, or NULL; gated head only (else
+ *             DLITE_ERR_UNSUPPORTED).  [W] "官方顺序头具体算了什么": one token
+ *             before the anchor may warm the state up.  An id w in [0, V)
+ *             runs one state update from s = 0 with v = E_R(w) and no output
+ *             before position 1; an id outside [0, V) leaves s_0 = 0.
+ */
+typedef struct dlite_block_options {
+  int32_t group;
+  const int32_t *group_ids;
+  const int32_t *warmup_ids;
+} dlite_block_options;
+
+/* Workspace bytes of dlite_draft_block_ex for these dimensions and options
+ * (the group length changes the slot count); 0 if invalid. */
+size_t dlite_workspace_bytes_ex(const dlite_dims *dims, const dlite_block_options *opts);
+
+/*
+ * dlite_draft_block_ex — the draft step with a local token group and/or the
+ * gated head's warm-up token (dlite_block_options).
+ *
+ * head     NULL: the fixed recurrence of dlite_draft_block; else the gated
+ *          head of dlite_draft_block_gated (same weights and rules)
+ * opts     may be NULL (the plain step)
+ * taps     x is [n_layers, B, G + K, D]; the others as dlite_draft_block
+ * workspace  at least dlite_workspace_bytes_ex(dims, opts) bytes
+ * A request whose anchor id is outside [0, V) gets candidates -1, as in
+ * dlite_draft_block.  All other arguments and errors are as
+ * dlite_draft_block; G > 1 with group_ids NULL is DLITE_ERR_NULL, G outside
+ * [0, 16] or an attention block too large for LDS (m + G + K slots) is
+ * DLITE_ERR_SHAPE / DLITE_ERR_UNSUPPORTED.
+ */
+int dlite_draft_block_ex(const dlite_dims *dims, const dlite_weights *weights,
+                         const dlite_gated_head *head, const dlite_block_options *opts,
+                         const void *features, const int32_t *anchor_ids, int32_t *candidates,
+                         float *max_logit, const dlite_taps *taps, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * dlite_draft_block_at — the draft step of the next round, fed straight from

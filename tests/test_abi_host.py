@@ -190,3 +190,35 @@ def test_draft_status_validation_codes():
     assert lib.dlite_draft_status(f, n, None, None) == -1
     assert lib.dlite_draft_status(f + 16, n, f, None) == -5
     assert lib.dlite_draft_status(f, 64, f, None) == -4
+
+
+def test_block_options_workspace_and_validation_codes():
+    lib = B.load_library()
+    wl = WORKLOADS["tiny_f32"]
+    d = _dims(wl)
+    plain = B.dlite_workspace_bytes(d)
+    assert B.dlite_workspace_bytes_ex(d, None) == plain
+    assert B.dlite_workspace_bytes_ex(d, B.make_block_options(0)) == plain
+    assert B.dlite_workspace_bytes_ex(d, B.make_block_options(1)) == plain
+    need4 = B.dlite_workspace_bytes_ex(d, B.make_block_options(4, 0x500000))
+    assert need4 > plain and need4 % 256 == 0
+    for G in (-1, 17):
+        with pytest.raises(B.DliteError) as e:
+            B.dlite_workspace_bytes_ex(d, B.make_block_options(G, 0x500000))
+        assert e.value.code == -2 and b"group" in lib.dlite_last_error()
+    w, keep = _fake_weights(wl.n_layers)
+    fake = 0x200000
+    head = B.DliteGatedHead(*[fake] * 6)
+    call = lambda hd, opts, nbytes: lib.dlite_draft_block_ex(
+        ctypes.byref(d), ctypes.byref(w), hd, opts, fake, fake, fake, None, None, fake, nbytes, None)
+    # a group without its ids, a warm-up token without the gated head
+    assert call(None, ctypes.byref(B.make_block_options(4)), need4) == -1
+    assert call(None, ctypes.byref(B.make_block_options(1, None, fake)), plain) == -5
+    assert b"gated" in lib.dlite_last_error()
+    # a group needs the larger workspace
+    assert call(None, ctypes.byref(B.make_block_options(4, fake)), plain) == -4
+    assert call(ctypes.byref(head), ctypes.byref(B.make_block_options(4, fake, fake)), need4 - 1) == -4
+    assert call(None, ctypes.byref(B.make_block_options(17, fake)), need4) == -2
+    # the largest block: m = 64 features, a group of 16 and 16 placeholders
+    big = _dims(WORKLOADS["tiny_f32"], m=64, K=16)
+    assert B.dlite_workspace_bytes_ex(big, B.make_block_options(16, fake)) > 0
