@@ -311,19 +311,28 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
         bi_s[wn * BM + tloc] = bi;
       }
     }
-    if (a.tap) {   // logits copy (checking only)
+    if (a.tap) {   // logits copy (the sampled path reads it)
+      // four consecutive rows per (i, q): one 16-byte store when the rows
+      // exist and the row stride keeps them aligned
+      const bool vec = full && (a.ld_tap & 3) == 0 && (reinterpret_cast<uintptr_t>(a.tap) & 15) == 0;
 #pragma unroll
       for (int u = 0; u < WTM; ++u) {
-        float* trow = a.tap + a.tmap.row(a.tok0 + (tok_ok[u] ? tk[u] : 0)) * a.ld_tap;
+        if (!tok_ok[u]) continue;
+        float* trow = a.tap + a.tmap.row(a.tok0 + tk[u]) * a.ld_tap;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < 4; ++q) {
+            const int n = nbase + i * 32 + 8 * q;
+            if (vec) {
+              *reinterpret_cast<float4*>(trow + n) =
+                  make_float4(acc[i][u][4 * q], acc[i][u][4 * q + 1], acc[i][u][4 * q + 2], acc[i][u][4 * q + 3]);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int n = nbase + i * 32 + 8 * q + e;
-              if (tok_ok[u] && n < a.N) trow[n] = acc[i][u][4 * q + e];
+              for (int e = 0; e < 4; ++e)
+                if (n + e < a.N) trow[n + e] = acc[i][u][4 * q + e];
             }
+          }
       }
     }
     __syncthreads();

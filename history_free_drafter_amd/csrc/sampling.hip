@@ -2,10 +2,11 @@
 // (DLite walkthrough, section "贪心模式与随机模式要分别说明").
 //
 // Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
-// numbers: as easy as 1, 2, 3", SC 2011), a counter-based generator: the
-// value for counter (a, b, stream, 0) under key (seed low, seed high) is
-// computed where it is needed, so no generator state exists.  A uniform in
-// (0, 1) is (x0 + 1/2) / 2^32 in fp64.
+// numbers: as easy as 1, 2, 3", SC 2011), a counter-based generator computed
+// where it is needed, so no generator state exists.  The uniform with index
+// a of row b in a stream is word a mod 4 of the generator at counter
+// (a div 4, b, stream, 0) under key (seed low, seed high), as
+// (word + 1/2) / 2^32 in fp64: one call serves four consecutive indices.
 //
 // Draws from softmax(l / T) use the Gumbel-max rule, argmax_v (l_v / T -
 // log(-log u_v)), with the (value, index) reduction of the vocabulary pass.
@@ -13,10 +14,13 @@
 // at the first rejection the token is drawn from the positive residual
 // [p - q]_+ (inverse CDF), after K acceptances from the target's last row.
 // Three passes over the vocabulary, each spread over 64 chunks: log-sum-exp
-// partials of every row, the deciding row's chunk sums, and the draw (chunk,
-// then index inside it).
+// partials of every row (one pass each), the deciding row's chunk sums, and
+// the draw (chunk, then index inside it).  A draw's perturbed scores are
+// formed in fp32 and only the near-maximal ones again in fp64, which finds
+// the same token as an fp64 evaluation of every score.
 // Probabilities, exponentials and logarithms are fp64: the decisions are the
 // ones an exact evaluation would make except within rounding of a threshold.
+#include "gumbel_bounds.hpp"
 #include "kernels.hpp"
 
 namespace dlite {
@@ -38,10 +42,16 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint2 k) {
   return c;
 }
 
+__device__ __forceinline__ uint4 philox_group(unsigned long long seed, unsigned stream, unsigned g, unsigned b) {
+  return philox4x32_10(make_uint4(g, b, stream, 0u),
+                       make_uint2(static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32)));
+}
+__device__ __forceinline__ uint32_t pick_word(const uint4& x, unsigned w) {
+  return w == 0 ? x.x : w == 1 ? x.y : w == 2 ? x.z : x.w;
+}
+__device__ __forceinline__ double to_uniform(uint32_t x) { return (static_cast<double>(x) + 0.5) * (1.0 / 4294967296.0); }
 __device__ __forceinline__ double uniform01(unsigned long long seed, unsigned stream, unsigned a, unsigned b) {
-  const uint4 x = philox4x32_10(make_uint4(a, b, stream, 0u),
-                                make_uint2(static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32)));
-  return (static_cast<double>(x.x) + 0.5) * (1.0 / 4294967296.0);
+  return to_uniform(pick_word(philox_group(seed, stream, a >> 2, b), a & 3u));
 }
 
 struct Best {
@@ -71,24 +81,113 @@ __device__ Best block_best(double v, int i, Best* sh) {
   return b;
 }
 
-// Pass 1 of a draw: the best perturbed score of chunk c of row n.
-__global__ __launch_bounds__(kThreads) void sample_partial_kernel(const float* logits, int V, double invT,
+
+// Pass 1 of a draw: the best perturbed score of chunk c of row n, exactly
+// as an fp64 evaluation of every score would find it; one wave per chunk
+// (CPB chunks per workgroup).  The chunk is walked in groups of four
+// consecutive indices (one generator call and, for rows of a multiple of
+// four, one 16-byte load each).  The Gumbel term of a word lies between the
+// bounds of its bucket (kGumbelBounds, staged in LDS), so every score has an
+// fp32 interval [lo, hi] that holds its fp64 value (rounding covered by a
+// relative margin of 4e-7).  No index whose hi is below the largest lo of the
+// chunk can win, so only the others (a few per chunk) are formed in fp64 (the
+// costly logarithms) and compared as (value, index) with ties to the lower
+// index.  A lane keeps the largest hi of each of its first kKeep groups;
+// later groups are formed again to find their candidates.
+constexpr int kKeep = 16;
+constexpr int kChunksPerBlock = 4;      // waves (chunks) per workgroup of the large passes
+constexpr float kBoundMargin = 4e-7f;
+template <int CPB>
+__global__ __launch_bounds__(64 * CPB) void sample_partial_kernel(const float* logits, int V, double invT,
                                                                   unsigned long long seed, unsigned stream,
                                                                   Best* part) {
-  __shared__ Best sh[kThreads / 64];
-  const int c = blockIdx.x, n = blockIdx.y;
+  __shared__ float2 gb[kGumbelBuckets];
+  for (int i = threadIdx.x; i < kGumbelBuckets; i += 64 * CPB)
+    gb[i] = make_float2(kGumbelBounds[2 * i], kGumbelBounds[2 * i + 1]);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * CPB + wave, n = blockIdx.y;
   const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
   const int v1 = static_cast<int>(static_cast<long>(c + 1) * V / kSampleChunks);
   const float* row = logits + static_cast<long>(n) * V;
+  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+  const float invTf = static_cast<float>(invT);
+  const int g0 = v0 >> 2, g1 = v1 > v0 ? ((v1 - 1) >> 2) + 1 : g0;   // groups touching the chunk
+  // group g: its logits, words, and score intervals (empty outside the chunk)
+  auto group = [&](int g, float (&lv)[4], uint32_t (&wd)[4], float (&lo)[4], float (&hi)[4]) {
+    const uint4 x = philox_group(seed, stream, static_cast<unsigned>(g), static_cast<unsigned>(n));
+    wd[0] = x.x; wd[1] = x.y; wd[2] = x.z; wd[3] = x.w;
+    const int vb = 4 * g;
+    if (vec && vb >= v0 && vb + 3 < v1) {
+      const float4 q = *reinterpret_cast<const float4*>(row + vb);
+      lv[0] = q.x; lv[1] = q.y; lv[2] = q.z; lv[3] = q.w;
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) lv[w] = (vb + w >= v0 && vb + w < v1) ? row[vb + w] : 0.f;
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bool in = vb + w >= v0 && vb + w < v1;
+      const float lt = lv[w] * invTf;
+      const float2 bd = gb[wd[w] >> kGumbelShift];
+      const float l0 = lt + bd.x, h0 = lt + bd.y;
+      lo[w] = in ? l0 - (fabsf(lt) + fabsf(bd.x)) * kBoundMargin : -INFINITY;
+      hi[w] = in ? h0 + (fabsf(lt) + fabsf(bd.y)) * kBoundMargin : -INFINITY;
+    }
+  };
+  float ghi[kKeep];
+  float mlo = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) {
+    const int g = g0 + lane + k * 64;
+    ghi[k] = -INFINITY;
+    if (g < g1) {
+      float lv[4], lo[4], hi[4];
+      uint32_t wd[4];
+      group(g, lv, wd, lo, hi);
+      ghi[k] = fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3]));
+      mlo = fmaxf(mlo, fmaxf(fmaxf(lo[0], lo[1]), fmaxf(lo[2], lo[3])));
+    }
+  }
+  for (int g = g0 + lane + kKeep * 64; g < g1; g += 64) {
+    float lv[4], lo[4], hi[4];
+    uint32_t wd[4];
+    group(g, lv, wd, lo, hi);
+    mlo = fmaxf(mlo, fmaxf(fmaxf(lo[0], lo[1]), fmaxf(lo[2], lo[3])));
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mlo = fmaxf(mlo, __shfl_xor(mlo, o, kWave));
+  // the candidates, in fp64 (each lane visits its indices in ascending
+  // order, so strictly greater keeps the lower index on ties)
   double bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kThreads) {
-    const double u = uniform01(seed, stream, static_cast<unsigned>(v), static_cast<unsigned>(n));
-    const double s = static_cast<double>(row[v]) * invT - log(-log(u));
-    if (s > bv) { bv = s; bi = v; }   // v ascends within a thread: ties keep the lower
+  auto candidates = [&](int g) {
+    float lv[4], lo[4], hi[4];
+    uint32_t wd[4];
+    group(g, lv, wd, lo, hi);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (hi[w] >= mlo && hi[w] != -INFINITY) {
+        const double sv = static_cast<double>(lv[w]) * invT - log(-log(to_uniform(wd[w])));
+        if (sv > bv) { bv = sv; bi = 4 * g + w; }
+      }
+    }
+  };
+  if (mlo != -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k) {
+      const int g = g0 + lane + k * 64;
+      if (g < g1 && ghi[k] >= mlo) candidates(g);
+    }
+    for (int g = g0 + lane + kKeep * 64; g < g1; g += 64) candidates(g);
   }
-  const Best b = block_best(bv, bi, sh);
-  if (threadIdx.x == 0) part[static_cast<long>(n) * kSampleChunks + c] = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double ov = __shfl_xor(bv, o, kWave);
+    const int oi = __shfl_xor(bi, o, kWave);
+    if (better_d(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if (lane == 0) part[static_cast<long>(n) * kSampleChunks + c] = Best{bv, bi};
 }
 
 // Pass 2: the chunks of a row (one wave per row, a lane per chunk; the
@@ -115,33 +214,67 @@ struct Lse {
   double m, s;
 };
 
-__global__ __launch_bounds__(kThreads) void lse_partial_kernel(const float* draft, const float* target, int BK,
-                                                               int V, double invT, Lse* part) {
-  __shared__ double sh[kThreads / 64];
-  const int c = blockIdx.x, row = blockIdx.y;
+// One wave per chunk (four chunks per workgroup): a single pass over the
+// chunk in batches of eight values per lane (two 16-byte loads), with a
+// running maximum m and sum s of exp(y - m) rescaled once per batch when the
+// maximum grows; the eight exponentials of a batch are independent.  The
+// lanes' (m, s) pairs are merged in a fixed order.
+__global__ __launch_bounds__(64 * kChunksPerBlock) void lse_partial_kernel(const float* draft, const float* target,
+                                                                           int BK, int V, double invT, Lse* part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * kChunksPerBlock + wave, row = blockIdx.y;
   const float* x = row < BK ? draft + static_cast<long>(row) * V : target + static_cast<long>(row - BK) * V;
   const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
   const int v1 = static_cast<int>(static_cast<long>(c + 1) * V / kSampleChunks);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  double m = -INFINITY;
-  for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kThreads) m = fmax(m, static_cast<double>(x[v]) * invT);
+  // groups of four consecutive values (one 16-byte load for rows of a
+  // multiple of four), two groups per lane and batch
+  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  const int g0 = v0 >> 2, g1 = v1 > v0 ? ((v1 - 1) >> 2) + 1 : g0;
+  constexpr int kGB = 2;
+  double m = -INFINITY, s = 0.0;
+  for (int gb = g0 + lane; gb < g1; gb += kGB * 64) {
+    double y[kGB * 4];
+    double bm = -INFINITY;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) m = fmax(m, __shfl_xor(m, o, kWave));
-  if (lane == 0) sh[wave] = m;
-  __syncthreads();
-  for (int w = 0; w < kThreads / 64; ++w) m = fmax(m, sh[w]);
-  __syncthreads();
-  double s = 0.0;
-  for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kThreads) s += exp(static_cast<double>(x[v]) * invT - m);
+    for (int q = 0; q < kGB; ++q) {
+      const int vb = 4 * (gb + q * 64);
+      float f[4];
+      if (vec && vb >= v0 && vb + 3 < v1) {
+        const float4 t4 = *reinterpret_cast<const float4*>(x + vb);
+        f[0] = t4.x; f[1] = t4.y; f[2] = t4.z; f[3] = t4.w;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, kWave);
-  if (lane == 0) sh[wave] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int w = 0; w < kThreads / 64; ++w) t += sh[w];
-    part[static_cast<long>(row) * kSampleChunks + c] = Lse{m, t};
+        for (int w = 0; w < 4; ++w) y[q * 4 + w] = static_cast<double>(f[w]) * invT;
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int v = vb + w;
+          y[q * 4 + w] = (v >= v0 && v < v1) ? static_cast<double>(x[v]) * invT : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) bm = fmax(bm, y[q * 4 + w]);
+    }
+    if (bm > m) {
+      s = m == -INFINITY ? 0.0 : s * exp(m - bm);
+      m = bm;
+    }
+    if (m != -INFINITY) {
+      double t = 0.0;
+#pragma unroll
+      for (int j = 0; j < kGB * 4; ++j) t += exp(y[j] - m);   // exp(-inf) = 0
+      s += t;
+    }
   }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double om = __shfl_xor(m, o, kWave), os = __shfl_xor(s, o, kWave);
+    const double M = fmax(m, om);
+    const double a = m == -INFINITY ? 0.0 : s * exp(m - M);
+    const double b = om == -INFINITY ? 0.0 : os * exp(om - M);
+    m = M;
+    s = a + b;
+  }
+  if (lane == 0) part[static_cast<long>(row) * kSampleChunks + c] = Lse{m, s};
 }
 
 constexpr int kMaxRows = 2 * 64 + 1;   // rows of one request: K draft + K + 1 target (K <= 64)
@@ -352,8 +485,13 @@ size_t sampling_scratch_bytes(long rows) {
 hipError_t launch_sample_tokens(const float* logits, int N, int V, float T, unsigned long long seed,
                                 unsigned stream, int32_t* tokens, void* scratch, hipStream_t st) {
   Best* part = static_cast<Best*>(scratch);
-  launch_k(sample_partial_kernel, dim3(kSampleChunks, N), dim3(kThreads), 0, st, logits, V,
-                     1.0 / static_cast<double>(T), seed, stream, part);
+  // few rows: one wave per workgroup, so that the chunks spread over more CUs
+  if (N * kSampleChunks < 4096)
+    launch_k(sample_partial_kernel<1>, dim3(kSampleChunks, N), dim3(64), 0, st, logits, V,
+             1.0 / static_cast<double>(T), seed, stream, part);
+  else
+    launch_k(sample_partial_kernel<kChunksPerBlock>, dim3(kSampleChunks / kChunksPerBlock, N),
+             dim3(64 * kChunksPerBlock), 0, st, logits, V, 1.0 / static_cast<double>(T), seed, stream, part);
   launch_k(sample_final_kernel, dim3((N + 3) / 4), dim3(256), 0, st, part, N, tokens);
   return hipGetLastError();
 }
@@ -365,7 +503,7 @@ hipError_t launch_accept_sampled(const int32_t* cand, const float* draft, const 
   Lse* part = static_cast<Lse*>(scratch);
   double* csum = reinterpret_cast<double*>(part + static_cast<long>(B) * (2 * K + 1) * kSampleChunks);
   const double invT = 1.0 / static_cast<double>(T);
-  launch_k(lse_partial_kernel, dim3(kSampleChunks, B * (2 * K + 1)), dim3(kThreads), 0, st, draft,
+  launch_k(lse_partial_kernel, dim3(kSampleChunks / kChunksPerBlock, B * (2 * K + 1)), dim3(64 * kChunksPerBlock), 0, st, draft,
                      target, B * K, V, invT, part);
   launch_k(chunk_sum_kernel, dim3(kSampleChunks, B), dim3(kThreads), 0, st, cand, draft, target, part, B,
                      K, V, invT, seed, csum);

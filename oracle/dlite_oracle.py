@@ -444,12 +444,18 @@ def philox4x32_10(ctr, key):
 
 
 def uniform01(seed: int, stream: int, a, b) -> np.ndarray:
-    """Uniform in (0, 1) for counter (a, b, stream, 0) under key (seed low, seed high)."""
+    """Uniform in (0, 1) with index a of row b in the given stream.
+
+    READING (the pages name no generator): word a mod 4 of Philox4x32-10 at
+    counter (a div 4, b, stream, 0) under key (seed low, seed high), as
+    u = (word + 1/2) / 2^32; one generator call yields four uniforms.
+    """
     a = np.asarray(a)
     b = np.broadcast_to(np.asarray(b), a.shape)
-    x = philox4x32_10((a, b, np.full(a.shape, stream), np.zeros(a.shape)),
+    x = philox4x32_10((a >> 2, b, np.full(a.shape, stream), np.zeros(a.shape)),
                       (np.full(a.shape, seed & 0xFFFFFFFF), np.full(a.shape, (seed >> 32) & 0xFFFFFFFF)))
-    return (x[0].astype(np.float64) + 0.5) / 4294967296.0
+    word = np.choose(a & 3, x)
+    return (word.astype(np.float64) + 0.5) / 4294967296.0
 
 
 def softmax_t(logits: np.ndarray, T: float) -> np.ndarray:

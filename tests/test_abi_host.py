@@ -222,3 +222,26 @@ def test_block_options_workspace_and_validation_codes():
     # the largest block: m = 64 features, a group of 16 and 16 placeholders
     big = _dims(WORKLOADS["tiny_f32"], m=64, K=16)
     assert B.dlite_workspace_bytes_ex(big, B.make_block_options(16, fake)) > 0
+
+
+def test_gumbel_bucket_bounds_hold():
+    """The draw kernel's per-bucket bounds of -log(-log u) (generated header)
+    enclose the fp64 value at every bucket's first and last word and at
+    random words, and are tight enough to prune (hi - lo small except near
+    u = 1)."""
+    import numpy as np
+    txt = open(os.path.join(ROOT, "history_free_drafter_amd", "csrc", "gumbel_bounds.hpp")).read()
+    body = txt[txt.index("{", txt.index("kGumbelBounds[2 *")) + 1:txt.index("};")]
+    vals = np.array([float.fromhex(t.strip().rstrip("f")) for t in body.split(",") if t.strip()])
+    lo, hi = vals[0::2], vals[1::2]
+    nb = len(lo)
+    shift = 32 - int(np.log2(nb))
+    g = lambda x: -np.log(-np.log((x.astype(np.float64) + 0.5) / 2.0 ** 32))
+    b = np.arange(nb, dtype=np.uint64)
+    first, last = b << np.uint64(shift), ((b + np.uint64(1)) << np.uint64(shift)) - np.uint64(1)
+    assert (lo <= g(first)).all() and (g(last) <= hi).all()
+    x = np.random.default_rng(0).integers(0, 2 ** 32, 200000, dtype=np.uint64)
+    k = (x >> np.uint64(shift)).astype(int)
+    gx = g(x)
+    assert (lo[k] <= gx).all() and (gx <= hi[k]).all()
+    assert np.median(hi - lo) < 0.01

@@ -33,6 +33,29 @@ def test_uniforms_are_open_interval_and_uniform():
     assert stats.chisquare(counts).pvalue > 1e-4
 
 
+def test_uniforms_of_one_generator_call_are_distinct_and_uncorrelated():
+    """Four consecutive indices share a counter and take its four words: they
+    must differ and show no correlation at lags 1..4 (a word reused for
+    several indices, or a counter reused across groups, would); rows and
+    streams give unrelated values."""
+    u = oracle.uniform01(11, 0, np.arange(400000), 3)
+    g = u.reshape(-1, 4)
+    assert all(len(set(row)) == 4 for row in g[:20000])          # a call's words differ
+    dup = len(u) - len(np.unique(u))                             # 32-bit birthday collisions only
+    assert dup <= 3 * len(u) ** 2 / 2.0 ** 33 + 10, dup
+    z = u - 0.5
+    for lag in (1, 2, 3, 4):
+        r = float(np.mean(z[:-lag] * z[lag:]) / np.mean(z * z))
+        assert abs(r) < 0.01, (lag, r)
+    w = oracle.uniform01(11, 0, np.arange(400000), 4)
+    y = oracle.uniform01(11, 1, np.arange(400000), 3)
+    for other in (w, y):
+        assert abs(float(np.corrcoef(u, other)[0, 1])) < 0.01
+    # the four words of one call are the generator's own outputs
+    x = oracle.philox4x32_10((np.uint32(5), np.uint32(3), np.uint32(0), np.uint32(0)), (np.uint32(11), np.uint32(0)))
+    np.testing.assert_array_equal(u[20:24], (np.array([int(v) for v in x], dtype=np.float64) + 0.5) / 2.0 ** 32)
+
+
 @pytest.mark.parametrize("T", [0.5, 1.0, 2.0])
 def test_gumbel_draws_follow_softmax(T):
     V, N = 6, 60000
