@@ -227,32 +227,40 @@ __global__ __launch_bounds__(64 * kChunksPerBlock) void lse_partial_kernel(const
   const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
   const int v1 = static_cast<int>(static_cast<long>(c + 1) * V / kSampleChunks);
   // groups of four consecutive values (one 16-byte load for rows of a
-  // multiple of four), two groups per lane and batch
+  // multiple of four), two groups per lane and batch; the next batch is
+  // loaded while the current one is summed
   const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   const int g0 = v0 >> 2, g1 = v1 > v0 ? ((v1 - 1) >> 2) + 1 : g0;
   constexpr int kGB = 2;
-  double m = -INFINITY, s = 0.0;
-  for (int gb = g0 + lane; gb < g1; gb += kGB * 64) {
-    double y[kGB * 4];
-    double bm = -INFINITY;
+  auto load = [&](int gb, float (&f)[kGB * 4]) {
 #pragma unroll
     for (int q = 0; q < kGB; ++q) {
       const int vb = 4 * (gb + q * 64);
-      float f[4];
       if (vec && vb >= v0 && vb + 3 < v1) {
         const float4 t4 = *reinterpret_cast<const float4*>(x + vb);
-        f[0] = t4.x; f[1] = t4.y; f[2] = t4.z; f[3] = t4.w;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) y[q * 4 + w] = static_cast<double>(f[w]) * invT;
+        f[q * 4] = t4.x; f[q * 4 + 1] = t4.y; f[q * 4 + 2] = t4.z; f[q * 4 + 3] = t4.w;
       } else {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int v = vb + w;
-          y[q * 4 + w] = (v >= v0 && v < v1) ? static_cast<double>(x[v]) * invT : -INFINITY;
+          f[q * 4 + w] = (v >= v0 && v < v1) ? x[v] : -INFINITY;
         }
       }
+    }
+  };
+  double m = -INFINITY, s = 0.0;
+  float cur[kGB * 4];
+  int gb = g0 + lane;
+  if (gb < g1) load(gb, cur);
+  for (; gb < g1; gb += kGB * 64) {
+    float nxt[kGB * 4];
+    if (gb + kGB * 64 < g1) load(gb + kGB * 64, nxt);
+    double y[kGB * 4];
+    double bm = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) bm = fmax(bm, y[q * 4 + w]);
+    for (int j = 0; j < kGB * 4; ++j) {
+      y[j] = static_cast<double>(cur[j]) * invT;
+      bm = fmax(bm, y[j]);
     }
     if (bm > m) {
       s = m == -INFINITY ? 0.0 : s * exp(m - bm);
@@ -264,6 +272,8 @@ __global__ __launch_bounds__(64 * kChunksPerBlock) void lse_partial_kernel(const
       for (int j = 0; j < kGB * 4; ++j) t += exp(y[j] - m);   // exp(-inf) = 0
       s += t;
     }
+#pragma unroll
+    for (int j = 0; j < kGB * 4; ++j) cur[j] = nxt[j];
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -329,27 +339,40 @@ __device__ void decide(const int32_t* cand, const float* draft, const float* tar
   }
 }
 
-// Pass 2: per (chunk, request), the deciding row's chunk sums of the
-// residual weights and of the target probabilities (the fallback when the
-// residual vanishes).
-__global__ __launch_bounds__(kThreads) void chunk_sum_kernel(const int32_t* cand, const float* draft,
-                                                             const float* target, const Lse* part, int B, int K,
-                                                             int V, double invT, unsigned long long seed,
-                                                             double* csum) {
+// The decision of request b, made once: the deciding position, whether its
+// draw is from the residual, and the log-sum-exps its weights need.
+struct Decision {
+  double lp, lq;   // lse of the target row at the position (and of the draft row, residual)
+  int i, res;
+};
+__global__ __launch_bounds__(kThreads) void decide_kernel(const int32_t* cand, const float* draft,
+                                                          const float* target, const Lse* part, int B, int K,
+                                                          int V, double invT, unsigned long long seed,
+                                                          Decision* dec) {
   __shared__ double lse[kMaxRows];
-  __shared__ double shr[kThreads / 64], shp[kThreads / 64];
-  __shared__ int di;
-  __shared__ int dres;
-  const int c = blockIdx.x, b = blockIdx.y;
+  __shared__ int di, dres;
+  const int b = blockIdx.x;
   request_lse(part, b, B, K, lse);
   __syncthreads();
   decide(cand, draft, target, lse, b, K, V, invT, seed, &di, &dres);
   __syncthreads();
-  const int i = di;
-  const bool res = dres != 0;
+  if (threadIdx.x == 0) dec[b] = Decision{lse[K + di], dres ? lse[di] : 0.0, di, dres};
+}
+
+// Pass 2: per (chunk, request), the deciding row's chunk sums of the
+// residual weights and of the target probabilities (the fallback when the
+// residual vanishes).
+__global__ __launch_bounds__(kThreads) void chunk_sum_kernel(const float* draft, const float* target,
+                                                             const Decision* dec, int K, int V, double invT,
+                                                             double* csum) {
+  __shared__ double shr[kThreads / 64], shp[kThreads / 64];
+  const int c = blockIdx.x, b = blockIdx.y;
+  const Decision d = dec[b];
+  const int i = d.i;
+  const bool res = d.res != 0;
   const float* tp = target + (static_cast<long>(b) * (K + 1) + i) * V;
   const float* dp = draft + (static_cast<long>(b) * K + (res ? i : 0)) * V;
-  const double lp = lse[K + i], lq = res ? lse[i] : 0.0;
+  const double lp = d.lp, lq = d.lq;
   const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
   const int v1 = static_cast<int>(static_cast<long>(c + 1) * V / kSampleChunks);
   double sr = 0.0, sp = 0.0;
@@ -380,19 +403,16 @@ __global__ __launch_bounds__(kThreads) void chunk_sum_kernel(const int32_t* cand
 // Pass 3: per request, the chunk whose running range holds the draw, then
 // the index inside it: each thread a contiguous piece of the chunk, the
 // pieces' sums scanned in thread order, the piece holding the draw rescanned.
-__global__ __launch_bounds__(kThreads) void pick_kernel(const int32_t* cand, const float* draft,
-                                                        const float* target, const Lse* part,
-                                                        const double* csum, int B, int K, int V, double invT,
-                                                        unsigned long long seed, int32_t* A_out,
+__global__ __launch_bounds__(kThreads) void pick_kernel(const float* draft, const float* target,
+                                                        const Decision* dec, const double* csum, int K, int V,
+                                                        double invT, unsigned long long seed, int32_t* A_out,
                                                         int32_t* next_out) {
-  __shared__ double lse[kMaxRows];
   __shared__ double pre[kThreads + 1];
   __shared__ int di, dres, chunk;
   __shared__ double tloc;
   const int b = blockIdx.x;
-  request_lse(part, b, B, K, lse);
-  __syncthreads();
-  decide(cand, draft, target, lse, b, K, V, invT, seed, &di, &dres);
+  const Decision d = dec[b];
+  if (threadIdx.x == 0) { di = d.i; dres = d.res; }
   __syncthreads();
   if (threadIdx.x < 64) {
     // wave 0, lane = chunk: the chunk sums scanned in chunk order, the chunk
@@ -432,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(const int32_t* cand, con
   const bool res = dres != 0;
   const float* tp = target + (static_cast<long>(b) * (K + 1) + i) * V;
   const float* dp = draft + (static_cast<long>(b) * K + (res ? i : 0)) * V;
-  const double lp = lse[K + i], lq = res ? lse[i] : 0.0;
+  const double lp = d.lp, lq = res ? d.lq : 0.0;
   auto weight = [&](int v) {
     const double p = exp(static_cast<double>(tp[v]) * invT - lp);
     if (!res) return p;
@@ -505,10 +525,11 @@ hipError_t launch_accept_sampled(const int32_t* cand, const float* draft, const 
   const double invT = 1.0 / static_cast<double>(T);
   launch_k(lse_partial_kernel, dim3(kSampleChunks / kChunksPerBlock, B * (2 * K + 1)), dim3(64 * kChunksPerBlock), 0, st, draft,
                      target, B * K, V, invT, part);
-  launch_k(chunk_sum_kernel, dim3(kSampleChunks, B), dim3(kThreads), 0, st, cand, draft, target, part, B,
-                     K, V, invT, seed, csum);
-  launch_k(pick_kernel, dim3(B), dim3(kThreads), 0, st, cand, draft, target, part, csum, B, K, V, invT,
-                     seed, A, next);
+  Decision* dec = reinterpret_cast<Decision*>(csum + static_cast<long>(B) * kSampleChunks * 2);
+  launch_k(decide_kernel, dim3(B), dim3(kThreads), 0, st, cand, draft, target, part, B, K, V, invT, seed, dec);
+  launch_k(chunk_sum_kernel, dim3(kSampleChunks, B), dim3(kThreads), 0, st, draft, target, dec, K, V, invT,
+           csum);
+  launch_k(pick_kernel, dim3(B), dim3(kThreads), 0, st, draft, target, dec, csum, K, V, invT, seed, A, next);
   return hipGetLastError();
 }
 
