@@ -138,7 +138,9 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
       const bool ok = s < S && (s < nokey0 || s >= nokey1);
       const float* kr = Ks + (ok ? s : 0) * kLd;
       float a0 = 0.f, a1 = 0.f;
-#pragma unroll
+      // a partial unroll: unrolled fully, the 128-wide product's LDS reads
+      // are all hoisted and the registers spill
+#pragma unroll 4
       for (int e = 0; e < d; e += 8) {
         const float4 k0 = *reinterpret_cast<const float4*>(kr + e);
         const float4 k1 = *reinterpret_cast<const float4*>(kr + e + 4);
