@@ -9,6 +9,8 @@
 // tokens ending at it, section "锚点是已经确定、尚待目标前向处理的输入") enters
 // through its token embeddings and the K placeholders through one shared input
 // vector.  Slot order per request: m features, G group tokens, K placeholders.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace dlite {
@@ -40,14 +42,14 @@ __device__ __forceinline__ float ld(const void* p, long i) {
 // context slots for every layer (they do not change between layers), group
 // and placeholder rows for the first layer.  Each thread holds its share of
 // the row in registers (16-byte loads, all issued before the reduction).
-constexpr int kMaxVec = 8;   // 16-byte vectors per thread: D <= 8 * 256 * 8
+constexpr int kMaxVec = 8;   // 16-byte vectors per thread: D <= 8 * 256 * 8 (NV: as many as D needs)
 
 template <typename T>
 __device__ __forceinline__ void unpack16(const uint4& v, float* out) {
   load16_f32(reinterpret_cast<const T*>(&v), out);
 }
 
-template <typename T>
+template <typename T, int NV>
 __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
   constexpr int PER = Elem<T>::kPerLane;
   __shared__ float sh[kThreads / 64];
@@ -85,12 +87,13 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
   }
   const T* g0 = static_cast<const T*>(a.attn_norm[0]);
   const T* gf = static_cast<const T*>(a.feat_norm);
-  uint4 hv[kMaxVec], dv[kMaxVec], gv[kMaxVec];
+  uint4 hv[NV], dv[NV], gv[NV], av[NV];
 #pragma unroll
-  for (int q = 0; q < kMaxVec; ++q) {
+  for (int q = 0; q < NV; ++q) {
     const int idx = threadIdx.x + q * kThreads;
-    hv[q] = dv[q] = gv[q] = make_uint4(0, 0, 0, 0);
+    hv[q] = dv[q] = gv[q] = av[q] = make_uint4(0, 0, 0, 0);
     if (idx < nvec) {
+      av[q] = *reinterpret_cast<const uint4*>(g0 + idx * PER);   // first layer's gain, with the rest
       if (src) hv[q] = *reinterpret_cast<const uint4*>(src + idx * PER);
       if (add) {
         dv[q] = *reinterpret_cast<const uint4*>(add + idx * PER);
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
   }
   float ss = 0.f;
 #pragma unroll
-  for (int q = 0; q < kMaxVec; ++q) {
+  for (int q = 0; q < NV; ++q) {
     float h[PER], e[PER];
     unpack16<T>(hv[q], h);
     unpack16<T>(dv[q], e);
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
   ss = 0.f;
   // final slot values (fp32), their sum of squares, the first layer's inputs
 #pragma unroll
-  for (int q = 0; q < kMaxVec; ++q) {
+  for (int q = 0; q < NV; ++q) {
     const int idx = threadIdx.x + q * kThreads;
     if (idx < nvec) {
       float h[PER], e[PER], gz[PER], v[PER], g[PER];
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(FeatureArgs a) {
         for (int t = 0; t < PER; t += 4)
           *reinterpret_cast<float4*>(tz + t) = make_float4(v[t], v[t + 1], v[t + 2], v[t + 3]);
       }
-      load16_f32(g0 + idx * PER, g);
+      unpack16<T>(av[q], g);
       float o[PER];
 #pragma unroll
       for (int t = 0; t < PER; ++t) o[t] = g[t] * v[t];
@@ -177,10 +180,22 @@ __global__ __launch_bounds__(kThreads) void hidden_tap_kernel(NormArgs a) {
 hipError_t launch_feature(const FeatureArgs& a, bool bf16, hipStream_t st) {
   if (a.G < 1 || (a.G > 1 && !a.gids)) return hipErrorInvalidValue;
   const dim3 grid(a.B * (a.m + a.G + a.K)), block(kThreads);
-  if (bf16)
-    launch_k(feature_kernel<uint16_t>, grid, block, 0, st, a);
-  else
-    launch_k(feature_kernel<float>, grid, block, 0, st, a);
+  // 16-byte vectors per thread for this width (registers sized to it)
+  const int nvec = a.D / (bf16 ? 8 : 4);
+  const int need = (nvec + kThreads - 1) / kThreads;
+  if (need > kMaxVec) return hipErrorInvalidValue;
+  auto go = [&](auto t, auto nv) {
+    using TT = decltype(t);
+    launch_k(feature_kernel<TT, decltype(nv)::value>, grid, block, 0, st, a);
+  };
+  auto pick = [&](auto t) {
+    if (need <= 1) go(t, std::integral_constant<int, 1>{});
+    else if (need <= 2) go(t, std::integral_constant<int, 2>{});
+    else if (need <= 4) go(t, std::integral_constant<int, 4>{});
+    else go(t, std::integral_constant<int, 8>{});
+  };
+  if (bf16) pick(uint16_t{});
+  else pick(float{});
   return hipGetLastError();
 }
 
