@@ -1087,10 +1087,13 @@ int seqhead_p_slices(int B, int K, int r, int D) {
   if (!seqhead_fused(B, K, r, true) || D % 32) return 0;
   const int G = seqhead_grid(B, r) - scan_detail::team_size(r, B) * B;
   const int tiles = r / 16, nst = D / 32;
-  int nps = G / tiles;
-  nps = nps < 16 ? nps : 16;
-  // every wave's share of a slice fits its kPSteps registers
-  if (nps < 1 || (nst + nps - 1) / nps > kWaves * kPSteps) return 0;
+  // few slices: fewer words for the team to sum, and the helpers without a
+  // share start their vocabulary loads at once (4 measured best at the 8B
+  // shape); at least as many as keep every wave's share within its kPSteps
+  // registers, at most one helper per (row tile, slice)
+  const int need = (nst + kWaves * kPSteps - 1) / (kWaves * kPSteps);
+  int nps = need > 4 ? need : 4;
+  if (nps > G / tiles || nps > 16) return 0;
   return nps;
 }
 
