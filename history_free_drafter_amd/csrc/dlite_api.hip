@@ -77,6 +77,7 @@ void read_opts(const dlite_block_options* o, Opts* out) {
 struct Plan {
   size_t counters, X, XB, XF, SSQ, Q, KV, AO, ACT, P, U, Sf, Sb, GR, GT, WS, pmax, pidx, TP, SP, total;
   int G;
+  int Gcap;   // partials per token in pmax / pidx
 };
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -143,6 +144,12 @@ Plan make_plan(const dlite_dims& d, int G = 1) {
   const int Gt = gemm_tile_groups(d.vocab);
   size_t Gmax = p.G > Gt ? p.G : Gt;
   if (seqhead_fused(d.B, d.K, d.rank, d.dtype == DLITE_BF16) && Gmax < kFuseMaxHelpers) Gmax = kFuseMaxHelpers;
+  // the persistent vocabulary pass (all B K tokens, or B per position of the
+  // gated head) leaves vocab_slots partials per token
+  for (const int M : {static_cast<int>(B * K), static_cast<int>(B)})
+    if (vocab_tiled(M, d.vocab, d.rank, d.dtype == DLITE_BF16) && static_cast<size_t>(vocab_slots(M)) > Gmax)
+      Gmax = vocab_slots(M);
+  p.Gcap = static_cast<int>(Gmax);
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
   p.counters = take(counter_words() * sizeof(unsigned));
@@ -446,7 +453,7 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   ScanArgs sa{P, w->seq_w_down, w->seq_w_up, U, Sf, Sb, tp.state, counters, B, K, D, r, 0u, 0};
   LmArgs la{};
   la.W = w->lm_head; la.src = Sb; la.V = d.vocab; la.r = r; la.M = B * K; la.tok0 = 0;
-  la.part_max = pmax; la.part_idx = pidx; la.G = p.G;
+  la.part_max = pmax; la.part_idx = pidx; la.G = p.G; la.G_cap = p.Gcap;
   la.cand = candidates; la.max_logit = max_logit; la.tap = tp.logits;
   la.anchors = anchor_ids; la.pos = fs.pos; la.pos_n = fs.T; la.K = K; la.counters = counters; la.part = TPs;
   la.xcd_counters = counters + counter_lm_xcd();

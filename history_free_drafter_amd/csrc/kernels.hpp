@@ -164,6 +164,13 @@ int gemm_tile_groups(int N);   // output tiles of an EPI_ARGMAX problem of N row
 size_t gemm_tile_scratch(int M0, int M1, int N0, int N1, int K, int epi);
 // `part` is the scratch area (at least gemm_tile_scratch bytes).
 hipError_t launch_gemm_tiled(const GemmArgs* segs, int nseg, int epi, float* part, hipStream_t st);
+// Vocabulary projection + argmax for a few hundred token rows (bf16, K a
+// multiple of 32, contiguous token rows): one persistent launch leaves
+// vocab_slots(M) (max, index) partials per token at part_*[(tok0 + t) *
+// vocab_slots(M) + slot], and the logits in tap when given.
+bool vocab_tiled(int M, int N, int K, bool bf16);
+int vocab_slots(int M);
+hipError_t launch_vocab(const GemmArgs& g, hipStream_t st);
 
 // ------------------------------------------------------------- attention --
 struct AttnArgs {
@@ -231,6 +238,7 @@ struct LmArgs {
   unsigned* counters;
   unsigned* xcd_counters; // counter_lm_xcd() words: arrivals per XCD (64-byte apart)
   float* part;           // partial-tile scratch of the tiled path (gemm_tile_scratch)
+  int G_cap;             // partials per token that part_max / part_idx hold
 };
 hipError_t launch_lmhead(const LmArgs& a, bool bf16, hipStream_t st);
 int lmhead_groups(int V);

@@ -1192,6 +1192,14 @@ hipError_t launch_lmhead(const LmArgs& a0, bool bf16, hipStream_t st) {
   g.src = a0.src; g.ld_src = a0.r; g.smap = RowMap{1, 1, 0}; g.M = a0.M; g.tok0 = a0.tok0;
   g.tap = a0.tap; g.ld_tap = a0.V; g.tmap = a0.omap;
   g.part_max = a0.part_max; g.part_idx = a0.part_idx; g.G_part = gemm_tile_groups(a0.V);
+  if (vocab_tiled(a0.M, a0.V, a0.r, bf16) && vocab_slots(a0.M) <= a0.G_cap) {
+    hipError_t e = launch_vocab(g, st);
+    if (e != hipSuccess) return e;
+    LmArgs a = a0;
+    a.G = vocab_slots(a0.M);
+    launch_k(lmhead_reduce_kernel, dim3((a.M + 3) / 4), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (gemm_tiled(g, bf16)) {
     hipError_t e = launch_gemm_tiled(&g, 1, EPI_ARGMAX, a0.part, st);
     if (e != hipSuccess) return e;

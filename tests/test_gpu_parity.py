@@ -155,6 +155,15 @@ SMALL = [
     # scan with teams of 16 and the streaming vocabulary pass
     _small("scan_team16_bf16", B=2, m=3, D=64, n_q=1, n_kv=1, ffn=32, K=7, rank=512,
            vocab=3001, n_layers=1, weight_std=0.04),
+    # the persistent vocabulary kernel (rank a multiple of 256): two token
+    # tiles of 112 (224 rows) with eight k steps per item and a ragged last
+    # vocabulary tile (5000 rows); four token tiles, the last ragged (384
+    # rows), and fewer vocabulary tiles (4) than XCDs, so some workgroups have
+    # no items (weights scaled so the fixed recurrence keeps the logits O(1))
+    _small("vocab_persistent_bf16", B=32, m=1, D=64, n_q=1, n_kv=1, ffn=32, K=7, rank=256,
+           vocab=5000, n_layers=1, weight_std=0.04),
+    _small("vocab_persistent_ragged_bf16", B=64, m=1, D=64, n_q=1, n_kv=1, ffn=32, K=6,
+           rank=256, vocab=1000, n_layers=1, weight_std=0.04),
 ]
 
 
@@ -195,6 +204,27 @@ def test_workloads_match_oracle_and_accept(key):
     for b in np.nonzero(~same)[0]:       # differing near-tie tokens: rule still holds
         row = list(gpu["cand"][b] == t[b, :w.K]) + [False]
         assert A_gpu[b] == row.index(False) and next_gpu[b] == t[b, A_gpu[b]]
+
+
+@pytest.mark.parametrize("key", ["vocab_persistent_bf16", "vocab_persistent_ragged_bf16",
+                                 "qwen3_8b_b32_l2", "qwen3_8b_b64_m36"])
+def test_candidates_without_taps_match_taps_and_oracle(key):
+    """The vocabulary pass without the logits copy (the timed configuration)
+    gives the same candidates and maxima as with it, bit for bit, and the
+    oracle's tokens wherever its top-2 margin is clear."""
+    _announce(f"no taps {key}")
+    if key in WORKLOADS:   # full size: the oracle's tokens are checked with taps elsewhere
+        w = WORKLOADS[key]
+        weights, H, a, ref = make_weights(w), make_features(w), make_anchors(w), None
+    else:
+        w, weights, H, a, ref = _prepared(key)
+    with_taps, model = _run_gpu(w, weights, H, a)
+    plain, _ = _run_gpu(w, weights, H, a, taps=False, model=model)
+    np.testing.assert_array_equal(plain["cand"], with_taps["cand"])
+    np.testing.assert_array_equal(plain["max_logit"], with_taps["max_logit"])
+    if ref is not None:
+        clear = ref["margin"] >= MARGIN[w.dtype]
+        assert not ((plain["cand"] != ref["cand"]) & clear).any()
 
 
 def test_repeat_calls_are_bitwise_identical_and_ignore_workspace_contents():
