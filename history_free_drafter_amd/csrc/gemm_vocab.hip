@@ -32,7 +32,9 @@ constexpr int kVN = 256;                      // vocabulary rows per item (64 pe
 constexpr int kVT = 7;                        // token blocks of 16 per item
 constexpr int kVM = 16 * kVT;                 // tokens per item (and per workgroup)
 constexpr int kVKs = 32;                      // k per step
-constexpr int kVD = 8;                        // weight steps in flight per wave
+// weight steps in flight per wave (fewer with the logits copy, whose stores
+// need registers of their own)
+template <bool TAP> constexpr int kVD = TAP ? 4 : 8;
 constexpr int kVWg = 256;                     // workgroups
 
 struct VocabArgs {
@@ -73,12 +75,13 @@ __global__ __launch_bounds__(256, 1) void vocab_kernel(VocabArgs a) {
   const int NT = (a.N + kVN - 1) / kVN;
   const int nx0 = xcd * NT / 8, nx1 = (xcd + 1) * NT / 8;
   const int items = nx1 - nx0 > p ? (nx1 - nx0 - p + np - 1) / np : 0;
-  static_assert(KS % kVD == 0, "whole prefetch rounds per item");   // KS = K / kVKs steps per item
+  constexpr int D = kVD<TAP>;
+  static_assert(KS % D == 0, "whole prefetch rounds per item");   // KS = K / kVKs steps per item
   const int cpr = a.K / 8;                      // 16-byte chunks per token row
 
   // ---- weight fragments of step g: lane holds row c16 of each 16-row block
   //      i and the 8 k elements at grp * 8 of the step
-  uint4 wv[kVD][4];
+  uint4 wv[D][4];
   auto issue = [&](int g, uint4 (&w)[4]) {
     const int it = g / KS, kk = g - it * KS;
     const int n = nx0 + p + it * np;
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(256, 1) void vocab_kernel(VocabArgs a) {
   // (issued unconditionally, past the last step too: rows are clamped to the
   // matrix, and without branches the compiler's waits stay exact)
 #pragma unroll
-  for (int h = 0; h < kVD; ++h) issue(h, wv[h]);
+  for (int h = 0; h < D; ++h) issue(h, wv[h]);
 
   // ---- the token tile into LDS (direct loads, all in flight at once), chunk
   //      c of row R at position c ^ (R & 15)
@@ -171,31 +174,45 @@ __global__ __launch_bounds__(256, 1) void vocab_kernel(VocabArgs a) {
     if (full) argmax_rows(acc, nb, std::true_type());
     else argmax_rows(acc, nb, std::false_type());
     if (TAP) {
-      // four consecutive rows per (i, u): one 16-byte store when they exist
-      // and stay aligned
+      // through LDS, one 16-token block at a time, so that each token's 256
+      // logits of the item go out as one contiguous kilobyte: the waves put
+      // their rows in place (rows padded by 4 floats: the 16 tokens of a
+      // 16-byte write hit distinct banks), then wave w writes tokens
+      // 4 w .. 4 w + 3
       const bool vec = full && (a.ld_tap & 3) == 0 && (reinterpret_cast<uintptr_t>(a.tap) & 15) == 0;
+      float* st = reinterpret_cast<float*>(smem + static_cast<size_t>(kVM) * kCpr * 16);   // [16][kVN + 4]
+      const int row0 = n * kVN;
 #pragma unroll
       for (int u = 0; u < kVT; ++u) {
-        const int tk = m * kVM + u * 16 + c16;
-        if (tk >= a.M) continue;
-        float* trow = a.tap + a.tmap.row(a.tok0 + tk) * a.ld_tap + nb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (vec) {
-            *reinterpret_cast<float4*>(trow + i * 16) =
-                make_float4(acc[i][u][0], acc[i][u][1], acc[i][u][2], acc[i][u][3]);
-          } else {
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4*>(st + c16 * (kVN + 4) + wave * 64 + i * 16 + 4 * grp) =
+              make_float4(acc[i][u][0], acc[i][u][1], acc[i][u][2], acc[i][u][3]);
+        __syncthreads();
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (nb + i * 16 + e < a.N) trow[i * 16 + e] = acc[i][u][e];
+        for (int q = 0; q < 4; ++q) {
+          const int t = wave * 4 + q;
+          const int tk = m * kVM + u * 16 + t;
+          if (tk < a.M) {
+            const float4 v = *reinterpret_cast<const float4*>(st + t * (kVN + 4) + lane * 4);
+            float* trow = a.tap + a.tmap.row(a.tok0 + tk) * a.ld_tap + row0 + lane * 4;
+            if (vec) {
+              *reinterpret_cast<float4*>(trow) = v;
+            } else {
+              const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (row0 + lane * 4 + e < a.N) trow[e] = f[e];
+            }
           }
         }
+        __syncthreads();
       }
     }
   };
 
   // ---- items one after another; the weight slot of step kk is refilled
-  //      with the step kVD later (the next item's for the last steps) once
+  //      with the step D later (the next item's for the last steps) once
   //      its MFMAs are issued
   uint4 bf[2][kVT];
 #pragma unroll
@@ -204,8 +221,8 @@ __global__ __launch_bounds__(256, 1) void vocab_kernel(VocabArgs a) {
     floatx4 acc[4][kVT];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      compute(kk, wv[kk % kVD], acc, bf[kk & 1], bf[(kk + 1) & 1]);   // KS even
-      issue(it * KS + kk + kVD, wv[kk % kVD]);
+      compute(kk, wv[kk % D], acc, bf[kk & 1], bf[(kk + 1) & 1]);   // KS even
+      issue(it * KS + kk + D, wv[kk % D]);
       __builtin_amdgcn_sched_barrier(0);   // one step at a time (register pressure)
     }
     finish_item(acc, nx0 + p + it * np);
@@ -275,7 +292,8 @@ hipError_t launch_vocab(const GemmArgs& g, hipStream_t st) {
   a.tap = g.tap; a.ld_tap = g.ld_tap; a.tmap = g.tmap;
   a.part_max = g.part_max; a.part_idx = g.part_idx;
   a.slots = vocab_slots(g.M);
-  const size_t sm = static_cast<size_t>(kVM) * g.K * 2;
+  // the resident token tile, and with the logits copy its staging block
+  const size_t sm = static_cast<size_t>(kVM) * g.K * 2 + (g.tap ? 16 * (kVN + 4) * sizeof(float) : 0);
   auto go = [&](auto kern) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
