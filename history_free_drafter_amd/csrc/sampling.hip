@@ -33,9 +33,11 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint2 k) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-    c = make_uint4(hi1 ^ c.y ^ k.x, lo1, hi0 ^ c.w ^ k.y, lo0);
+    // full 64-bit products: one multiply instruction each for both halves
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c.x;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
+    c = make_uint4(static_cast<uint32_t>(p1 >> 32) ^ c.y ^ k.x, static_cast<uint32_t>(p1),
+                   static_cast<uint32_t>(p0 >> 32) ^ c.w ^ k.y, static_cast<uint32_t>(p0));
     k.x += 0x9E3779B9u;
     k.y += 0xBB67AE85u;
   }
@@ -92,12 +94,18 @@ __device__ Best block_best(double v, int i, Best* sh) {
 // relative margin of 4e-7).  No index whose hi is below the largest lo of the
 // chunk can win, so only the others (a few per chunk) are formed in fp64 (the
 // costly logarithms) and compared as (value, index) with ties to the lower
-// index.  A lane keeps the largest hi of each of its first kKeep groups;
-// later groups are formed again to find their candidates.
-constexpr int kKeep = 16;
+// index.  The first phase takes a lane's groups kSB at a time, the next
+// batch's loads issued (at addresses clamped into the chunk) before the
+// current batch's generator words and intervals are formed; a lane keeps the
+// largest hi of each of its first kKeep groups, later groups are formed again
+// to find their candidates.
+constexpr int kSB = 5;                  // groups per lane and batch
+constexpr int kKeepB = 4;               // batches whose groups' bounds are kept
+constexpr int kKeep = kSB * kKeepB;
+static_assert(kKeep <= 32, "candidate groups of a lane as a 32-bit mask");
 constexpr int kChunksPerBlock = 4;      // waves (chunks) per workgroup of the large passes
 constexpr float kBoundMargin = 4e-7f;
-template <int CPB>
+template <int CPB, bool VEC>   // VEC: rows of a multiple of four values at a 16-byte aligned address
 __global__ __launch_bounds__(64 * CPB) void sample_partial_kernel(const float* logits, int V, double invT,
                                                                   unsigned long long seed, unsigned stream,
                                                                   Best* part) {
@@ -110,7 +118,6 @@ __global__ __launch_bounds__(64 * CPB) void sample_partial_kernel(const float* l
   const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
   const int v1 = static_cast<int>(static_cast<long>(c + 1) * V / kSampleChunks);
   const float* row = logits + static_cast<long>(n) * V;
-  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
   const float invTf = static_cast<float>(invT);
   const int g0 = v0 >> 2, g1 = v1 > v0 ? ((v1 - 1) >> 2) + 1 : g0;   // groups touching the chunk
   // group g: its logits, words, and score intervals (empty outside the chunk)
@@ -118,7 +125,7 @@ __global__ __launch_bounds__(64 * CPB) void sample_partial_kernel(const float* l
     const uint4 x = philox_group(seed, stream, static_cast<unsigned>(g), static_cast<unsigned>(n));
     wd[0] = x.x; wd[1] = x.y; wd[2] = x.z; wd[3] = x.w;
     const int vb = 4 * g;
-    if (vec && vb >= v0 && vb + 3 < v1) {
+    if (VEC && vb >= v0 && vb + 3 < v1) {
       const float4 q = *reinterpret_cast<const float4*>(row + vb);
       lv[0] = q.x; lv[1] = q.y; lv[2] = q.z; lv[3] = q.w;
     } else {
@@ -135,25 +142,67 @@ __global__ __launch_bounds__(64 * CPB) void sample_partial_kernel(const float* l
       hi[w] = in ? h0 + (fabsf(lt) + fabsf(bd.y)) * kBoundMargin : -INFINITY;
     }
   };
-  float ghi[kKeep];
-  float mlo = -INFINITY;
+  // batch loads: group b0 + lane + 64 q, clamped to the chunk's last group
+  auto load = [&](int b0, float (&f)[kSB][4]) {
 #pragma unroll
-  for (int k = 0; k < kKeep; ++k) {
-    const int g = g0 + lane + k * 64;
-    ghi[k] = -INFINITY;
-    if (g < g1) {
-      float lv[4], lo[4], hi[4];
-      uint32_t wd[4];
-      group(g, lv, wd, lo, hi);
-      ghi[k] = fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3]));
-      mlo = fmaxf(mlo, fmaxf(fmaxf(lo[0], lo[1]), fmaxf(lo[2], lo[3])));
+    for (int q = 0; q < kSB; ++q) {
+      const int g = min(b0 + lane + q * 64, g1 - 1);
+      if constexpr (VEC) {
+        const float4 t4 = *reinterpret_cast<const float4*>(row + 4 * g);
+        f[q][0] = t4.x; f[q][1] = t4.y; f[q][2] = t4.z; f[q][3] = t4.w;
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) f[q][w] = row[min(max(4 * g + w, v0), v1 - 1)];
+      }
+    }
+  };
+  // the batch's intervals: the largest lo into mlo, each group's largest hi
+  float mlo = -INFINITY;
+  auto bounds = [&](int b0, const float (&f)[kSB][4], float* gh) {
+#pragma unroll
+    for (int q = 0; q < kSB; ++q) {
+      const int g = b0 + lane + q * 64;
+      const uint4 x = philox_group(seed, stream, static_cast<unsigned>(g), static_cast<unsigned>(n));
+      const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+      float h = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int v = 4 * g + w;
+        const float lt = f[q][w] * invTf;
+        const float2 bd = gb[wd[w] >> kGumbelShift];
+        const float lo = lt + bd.x - (fabsf(lt) + fabsf(bd.x)) * kBoundMargin;
+        const float hi = lt + bd.y + (fabsf(lt) + fabsf(bd.y)) * kBoundMargin;
+        const bool in = v >= v0 && v < v1;
+        mlo = fmaxf(mlo, in ? lo : -INFINITY);
+        h = fmaxf(h, in ? hi : -INFINITY);
+      }
+      if (gh) gh[q] = h;
+    }
+  };
+  float ghi[kKeep];
+  float cur[kSB][4], nxt[kSB][4];
+  if (g1 > g0) load(g0, cur);
+#pragma unroll
+  for (int kb = 0; kb < kKeepB; ++kb) {
+    const int b0 = g0 + kb * kSB * 64;
+#pragma unroll
+    for (int q = 0; q < kSB; ++q) ghi[kb * kSB + q] = -INFINITY;
+    if (b0 < g1) {
+      load(b0 + kSB * 64, nxt);
+      bounds(b0, cur, ghi + kb * kSB);
+#pragma unroll
+      for (int q = 0; q < kSB; ++q)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) cur[q][w] = nxt[q][w];
     }
   }
-  for (int g = g0 + lane + kKeep * 64; g < g1; g += 64) {
-    float lv[4], lo[4], hi[4];
-    uint32_t wd[4];
-    group(g, lv, wd, lo, hi);
-    mlo = fmaxf(mlo, fmaxf(fmaxf(lo[0], lo[1]), fmaxf(lo[2], lo[3])));
+  for (int b0 = g0 + kKeep * 64; b0 < g1; b0 += kSB * 64) {
+    load(b0 + kSB * 64, nxt);
+    bounds(b0, cur, nullptr);
+#pragma unroll
+    for (int q = 0; q < kSB; ++q)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) cur[q][w] = nxt[q][w];
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) mlo = fmaxf(mlo, __shfl_xor(mlo, o, kWave));
@@ -165,19 +214,30 @@ __global__ __launch_bounds__(64 * CPB) void sample_partial_kernel(const float* l
     float lv[4], lo[4], hi[4];
     uint32_t wd[4];
     group(g, lv, wd, lo, hi);
+    uint32_t em = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (hi[w] >= mlo && hi[w] != -INFINITY) {
-        const double sv = static_cast<double>(lv[w]) * invT - log(-log(to_uniform(wd[w])));
-        if (sv > bv) { bv = sv; bi = 4 * g + w; }
-      }
+    for (int w = 0; w < 4; ++w)
+      if (hi[w] >= mlo && hi[w] != -INFINITY) em |= 1u << w;
+    while (em) {   // one fp64 evaluation per lane and iteration
+      const int w = __builtin_ctz(em);
+      em &= em - 1;
+      const float l = w == 0 ? lv[0] : w == 1 ? lv[1] : w == 2 ? lv[2] : lv[3];
+      const uint32_t x = w == 0 ? wd[0] : w == 1 ? wd[1] : w == 2 ? wd[2] : wd[3];
+      const double sv = static_cast<double>(l) * invT - log(-log(to_uniform(x)));
+      if (sv > bv) { bv = sv; bi = 4 * g + w; }
     }
   };
   if (mlo != -INFINITY) {
+    // a lane's candidate groups among its first kKeep, visited in ascending
+    // order (typically one per lane: the loads wait once per wave)
+    uint32_t cm = 0;
 #pragma unroll
-    for (int k = 0; k < kKeep; ++k) {
-      const int g = g0 + lane + k * 64;
-      if (g < g1 && ghi[k] >= mlo) candidates(g);
+    for (int k = 0; k < kKeep; ++k)
+      if (g0 + lane + k * 64 < g1 && ghi[k] >= mlo) cm |= 1u << k;
+    while (cm) {
+      const int k = __builtin_ctz(cm);
+      cm &= cm - 1;
+      candidates(g0 + lane + k * 64);
     }
     for (int g = g0 + lane + kKeep * 64; g < g1; g += 64) candidates(g);
   }
@@ -214,54 +274,94 @@ struct Lse {
   double m, s;
 };
 
-// One wave per chunk (four chunks per workgroup): a single pass over the
-// chunk in batches of eight values per lane (two 16-byte loads), with a
-// running maximum m and sum s of exp(y - m) rescaled once per batch when the
-// maximum grows; the eight exponentials of a batch are independent.  The
-// lanes' (m, s) pairs are merged in a fixed order.
+// exp(d) in fp64 for the probabilities of the verification passes (d <= 0
+// there), four at a time: d = (256 k + j) ln2 / 256 + r with |r| <= ln2 / 512,
+// so exp(d) = 2^k 2^(j/256) e^r.  n = 256 k + j is d 256 / ln2 rounded to an
+// integer (added to 1.5 2^52, so the sum's low word holds it), r follows by a
+// Cody-Waite reduction (ln2 / 256 as a head of 29 significant bits, whose
+// products with n are exact, plus the fp64 remainder), e^r by its Taylor
+// polynomial through r^4 (truncation below 4e-17 relative), 2^(j/256) from a
+// 256-entry table in LDS (exp_table).  About 3 ulp in all.  The four table
+// reads are issued before the polynomials, so their latency is covered.
+// Arguments below -1000 (and -inf) give exactly 0 through the final scaling;
+// a NaN stays NaN.  Valid for d up to 700.
+constexpr int kExpTab = 256;
+constexpr double kInvLn2xT = 0x1.71547652b82fep+8;     // 256 / ln 2
+constexpr double kLn2xTHi = 0x1.62e42ffp-9;            // ln 2 / 256, head
+constexpr double kLn2xTLo = -0x1.718432a1b0e26p-43;    // ln 2 / 256 - head
+constexpr double kRound52 = 0x1.8p52;
+__device__ __forceinline__ void exp_table(double* tab) {   // then a barrier
+  for (int i = threadIdx.x; i < kExpTab; i += blockDim.x) tab[i] = exp2(static_cast<double>(i) / kExpTab);
+}
+__device__ __forceinline__ void exp4(const double (&d4)[4], const double* tab, double (&e)[4]) {
+  double r[4], tv[4];
+  int n[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const double d = d4[w] < -1000.0 ? -1000.0 : d4[w];   // (a NaN stays NaN)
+    const double t = fma(d, kInvLn2xT, kRound52);
+    n[w] = __double2loint(t);
+    const double nf = t - kRound52;
+    r[w] = fma(-nf, kLn2xTLo, fma(-nf, kLn2xTHi, d));
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) tv[w] = tab[n[w] & (kExpTab - 1)];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    double p = fma(r[w], 1.0 / 24.0, 1.0 / 6.0);
+    p = fma(p, r[w], 0.5);
+    p = fma(p, r[w], 1.0);
+    p = fma(p, r[w], 1.0);
+    e[w] = ldexp(tv[w] * p, n[w] >> 8);
+  }
+}
+
+// One wave per chunk (four chunks per workgroup).  A lane takes its groups of
+// four consecutive values kLseGroups at a time (16-byte loads for rows of a
+// multiple of four, all issued before any is used; a group straddling the
+// chunk's edge is masked): their maximum (in fp32 on the raw logits: scaling
+// by 1/T > 0 keeps the order), the running maximum m rescaling the sum s
+// once per batch when it grows, then the batch's exp(y - m).  The lanes'
+// (m, s) pairs are merged in a fixed order.
+constexpr int kLseGroups = 10;   // one batch covers chunks of up to 2560 values
+template <bool VEC>   // rows of a multiple of four values at 16-byte aligned addresses
 __global__ __launch_bounds__(64 * kChunksPerBlock) void lse_partial_kernel(const float* draft, const float* target,
                                                                            int BK, int V, double invT, Lse* part) {
+  __shared__ double tab[kExpTab];
+  exp_table(tab);
+  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = blockIdx.x * kChunksPerBlock + wave, row = blockIdx.y;
   const float* x = row < BK ? draft + static_cast<long>(row) * V : target + static_cast<long>(row - BK) * V;
   const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
   const int v1 = static_cast<int>(static_cast<long>(c + 1) * V / kSampleChunks);
-  // groups of four consecutive values (one 16-byte load for rows of a
-  // multiple of four), two groups per lane and batch; the next batch is
-  // loaded while the current one is summed
-  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   const int g0 = v0 >> 2, g1 = v1 > v0 ? ((v1 - 1) >> 2) + 1 : g0;
-  constexpr int kGB = 2;
-  auto load = [&](int gb, float (&f)[kGB * 4]) {
+  double m = -INFINITY, s = 0.0;
+  for (int b0 = g0; b0 < g1; b0 += kLseGroups * 64) {
+    // addresses clamped into the chunk's groups, values outside it masked
+    float f[kLseGroups * 4];
 #pragma unroll
-    for (int q = 0; q < kGB; ++q) {
-      const int vb = 4 * (gb + q * 64);
-      if (vec && vb >= v0 && vb + 3 < v1) {
-        const float4 t4 = *reinterpret_cast<const float4*>(x + vb);
+    for (int q = 0; q < kLseGroups; ++q) {
+      const int g = min(b0 + lane + q * 64, g1 - 1);
+      if constexpr (VEC) {
+        const float4 t4 = *reinterpret_cast<const float4*>(x + 4 * g);
         f[q * 4] = t4.x; f[q * 4 + 1] = t4.y; f[q * 4 + 2] = t4.z; f[q * 4 + 3] = t4.w;
       } else {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int v = vb + w;
-          f[q * 4 + w] = (v >= v0 && v < v1) ? x[v] : -INFINITY;
-        }
+        for (int w = 0; w < 4; ++w) f[q * 4 + w] = x[min(max(4 * g + w, v0), v1 - 1)];
+        __builtin_amdgcn_sched_barrier(0);   // (registers)
       }
     }
-  };
-  double m = -INFINITY, s = 0.0;
-  float cur[kGB * 4];
-  int gb = g0 + lane;
-  if (gb < g1) load(gb, cur);
-  for (; gb < g1; gb += kGB * 64) {
-    float nxt[kGB * 4];
-    if (gb + kGB * 64 < g1) load(gb + kGB * 64, nxt);
-    double y[kGB * 4];
-    double bm = -INFINITY;
+    float xm = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kGB * 4; ++j) {
-      y[j] = static_cast<double>(cur[j]) * invT;
-      bm = fmax(bm, y[j]);
-    }
+    for (int q = 0; q < kLseGroups; ++q)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int v = 4 * (b0 + lane + q * 64) + w;
+        if (v < v0 || v >= v1) f[q * 4 + w] = -INFINITY;
+        xm = fmaxf(xm, f[q * 4 + w]);
+      }
+    const double bm = static_cast<double>(xm) * invT;
     if (bm > m) {
       s = m == -INFINITY ? 0.0 : s * exp(m - bm);
       m = bm;
@@ -269,11 +369,17 @@ __global__ __launch_bounds__(64 * kChunksPerBlock) void lse_partial_kernel(const
     if (m != -INFINITY) {
       double t = 0.0;
 #pragma unroll
-      for (int j = 0; j < kGB * 4; ++j) t += exp(y[j] - m);   // exp(-inf) = 0
+      for (int q = 0; q < kLseGroups; ++q) {
+        double d4[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) d4[w] = static_cast<double>(f[q * 4 + w]) * invT - m;
+        double e[4];
+        exp4(d4, tab, e);
+        t += ((e[0] + e[1]) + e[2]) + e[3];
+        __builtin_amdgcn_sched_barrier(0);   // one group at a time (registers)
+      }
       s += t;
     }
-#pragma unroll
-    for (int j = 0; j < kGB * 4; ++j) cur[j] = nxt[j];
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -361,11 +467,14 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(const int32_t* cand, c
 
 // Pass 2: per (chunk, request), the deciding row's chunk sums of the
 // residual weights and of the target probabilities (the fallback when the
-// residual vanishes).
+// residual vanishes); four consecutive values per thread and step.
 __global__ __launch_bounds__(kThreads) void chunk_sum_kernel(const float* draft, const float* target,
                                                              const Decision* dec, int K, int V, double invT,
                                                              double* csum) {
   __shared__ double shr[kThreads / 64], shp[kThreads / 64];
+  __shared__ double tab[kExpTab];
+  exp_table(tab);
+  __syncthreads();
   const int c = blockIdx.x, b = blockIdx.y;
   const Decision d = dec[b];
   const int i = d.i;
@@ -376,12 +485,22 @@ __global__ __launch_bounds__(kThreads) void chunk_sum_kernel(const float* draft,
   const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
   const int v1 = static_cast<int>(static_cast<long>(c + 1) * V / kSampleChunks);
   double sr = 0.0, sp = 0.0;
-  for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kThreads) {
-    const double p = exp(static_cast<double>(tp[v]) * invT - lp);
-    sp += p;
-    if (res) {
-      const double q = exp(static_cast<double>(dp[v]) * invT - lq);
-      sr += p > q ? p - q : 0.0;
+  for (int v = v0 + 4 * static_cast<int>(threadIdx.x); v < v1; v += 4 * kThreads) {
+    double dpv[4], dqv[4], p[4], q[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int u = min(v + w, v1 - 1);
+      dpv[w] = static_cast<double>(tp[u]) * invT - lp;
+      dqv[w] = res ? static_cast<double>(dp[u]) * invT - lq : 0.0;
+    }
+    exp4(dpv, tab, p);
+    if (res) exp4(dqv, tab, q);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (v + w < v1) {
+        sp += p[w];
+        if (res) sr += p[w] > q[w] ? p[w] - q[w] : 0.0;
+      }
     }
   }
 #pragma unroll
@@ -410,6 +529,8 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(const float* draft, cons
   __shared__ double pre[kThreads + 1];
   __shared__ int di, dres, chunk;
   __shared__ double tloc;
+  __shared__ double tab[kExpTab];
+  exp_table(tab);
   const int b = blockIdx.x;
   const Decision d = dec[b];
   if (threadIdx.x == 0) { di = d.i; dres = d.res; }
@@ -453,11 +574,20 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(const float* draft, cons
   const float* tp = target + (static_cast<long>(b) * (K + 1) + i) * V;
   const float* dp = draft + (static_cast<long>(b) * K + (res ? i : 0)) * V;
   const double lp = d.lp, lq = res ? d.lq : 0.0;
-  auto weight = [&](int v) {
-    const double p = exp(static_cast<double>(tp[v]) * invT - lp);
-    if (!res) return p;
-    const double q = exp(static_cast<double>(dp[v]) * invT - lq);
-    return p > q ? p - q : 0.0;
+  // the weights of v .. v + 3 (0 from a1 on; requires v < a1)
+  auto weights4 = [&](int v, int a1, double (&wt)[4]) {
+    double dpv[4], dqv[4], p[4], q[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int u = min(v + w, a1 - 1);
+      dpv[w] = static_cast<double>(tp[u]) * invT - lp;
+      dqv[w] = res ? static_cast<double>(dp[u]) * invT - lq : 0.0;
+    }
+    exp4(dpv, tab, p);
+    if (res) exp4(dqv, tab, q);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      wt[w] = v + w >= a1 ? 0.0 : !res ? p[w] : p[w] > q[w] ? p[w] - q[w] : 0.0;
   };
   const int c = chunk;
   const int v0 = static_cast<int>(static_cast<long>(c) * V / kSampleChunks);
@@ -466,7 +596,12 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(const float* draft, cons
   const int a0 = v0 + static_cast<int>(threadIdx.x) * per;
   const int a1 = a0 + per < v1 ? a0 + per : v1;
   double mine = 0.0;
-  for (int v = a0; v < a1; ++v) mine += weight(v);
+  for (int v = a0; v < a1; v += 4) {
+    double wt[4];
+    weights4(v, a1, wt);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mine += wt[w];   // (+0 past a1 leaves it unchanged)
+  }
   pre[threadIdx.x + 1] = mine;
   if (threadIdx.x == 0) pre[0] = 0.0;
   __syncthreads();
@@ -484,11 +619,14 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(const float* draft, cons
   if (lo <= t && t < hi) {
     double run = lo;
     int pick = -1, lastpos = a0;
-    for (int v = a0; v < a1; ++v) {
-      const double w = weight(v);
-      if (w > 0.0) lastpos = v;
-      run += w;
-      if (run > t) { pick = v; break; }
+    for (int v = a0; v < a1 && pick < 0; v += 4) {
+      double wt[4];
+      weights4(v, a1, wt);
+      for (int w = 0; w < 4 && v + w < a1; ++w) {
+        if (wt[w] > 0.0) lastpos = v + w;
+        run += wt[w];
+        if (run > t) { pick = v + w; break; }
+      }
     }
     next_out[b] = pick >= 0 ? pick : lastpos;
   }
@@ -506,12 +644,19 @@ hipError_t launch_sample_tokens(const float* logits, int N, int V, float T, unsi
                                 unsigned stream, int32_t* tokens, void* scratch, hipStream_t st) {
   Best* part = static_cast<Best*>(scratch);
   // few rows: one wave per workgroup, so that the chunks spread over more CUs
-  if (N * kSampleChunks < 4096)
-    launch_k(sample_partial_kernel<1>, dim3(kSampleChunks, N), dim3(64), 0, st, logits, V,
-             1.0 / static_cast<double>(T), seed, stream, part);
-  else
-    launch_k(sample_partial_kernel<kChunksPerBlock>, dim3(kSampleChunks / kChunksPerBlock, N),
-             dim3(64 * kChunksPerBlock), 0, st, logits, V, 1.0 / static_cast<double>(T), seed, stream, part);
+  const bool few = N * kSampleChunks < 4096;
+  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+  const dim3 grid = few ? dim3(kSampleChunks, N) : dim3(kSampleChunks / kChunksPerBlock, N);
+  const dim3 block = few ? dim3(64) : dim3(64 * kChunksPerBlock);
+  const double invT = 1.0 / static_cast<double>(T);
+  auto go = [&](auto kern) { launch_k(kern, grid, block, 0, st, logits, V, invT, seed, stream, part); };
+  if (few) {
+    if (vec) go(sample_partial_kernel<1, true>);
+    else go(sample_partial_kernel<1, false>);
+  } else {
+    if (vec) go(sample_partial_kernel<kChunksPerBlock, true>);
+    else go(sample_partial_kernel<kChunksPerBlock, false>);
+  }
   launch_k(sample_final_kernel, dim3((N + 3) / 4), dim3(256), 0, st, part, N, tokens);
   return hipGetLastError();
 }
@@ -523,8 +668,13 @@ hipError_t launch_accept_sampled(const int32_t* cand, const float* draft, const 
   Lse* part = static_cast<Lse*>(scratch);
   double* csum = reinterpret_cast<double*>(part + static_cast<long>(B) * (2 * K + 1) * kSampleChunks);
   const double invT = 1.0 / static_cast<double>(T);
-  launch_k(lse_partial_kernel, dim3(kSampleChunks / kChunksPerBlock, B * (2 * K + 1)), dim3(64 * kChunksPerBlock), 0, st, draft,
-                     target, B * K, V, invT, part);
+  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(draft) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(target) & 15) == 0;
+  const dim3 lgrid(kSampleChunks / kChunksPerBlock, B * (2 * K + 1)), lblock(64 * kChunksPerBlock);
+  if (vec)
+    launch_k(lse_partial_kernel<true>, lgrid, lblock, 0, st, draft, target, B * K, V, invT, part);
+  else
+    launch_k(lse_partial_kernel<false>, lgrid, lblock, 0, st, draft, target, B * K, V, invT, part);
   Decision* dec = reinterpret_cast<Decision*>(csum + static_cast<long>(B) * kSampleChunks * 2);
   launch_k(decide_kernel, dim3(B), dim3(kThreads), 0, st, cand, draft, target, part, B, K, V, invT, seed, dec);
   launch_k(chunk_sum_kernel, dim3(kSampleChunks, B), dim3(kThreads), 0, st, draft, target, dec, K, V, invT,

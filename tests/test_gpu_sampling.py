@@ -59,7 +59,8 @@ def _accept_gpu(cand, draft, target, T, seed):
 
 @pytest.mark.parametrize("Bn,K,V,T,seed", [(64, 7, 3000, 1.0, 11), (64, 7, 3000, 0.75, 12),
                                            (200, 1, 64, 1.0, 13), (2, 7, 151936, 1.0, 14),
-                                           (16, 16, 1000, 1.5, 15), (3, 64, 500, 2.0, 16)])
+                                           (16, 16, 1000, 1.5, 15), (3, 64, 500, 2.0, 16),
+                                           (8, 5, 2999, 1.0, 17)])
 def test_accept_sampled_matches_oracle(Bn, K, V, T, seed):
     print(f"\n[case] accept B={Bn} K={K} V={V} T={T}", flush=True)
     draft, target = make_sampling_case(seed, Bn, K, V)
