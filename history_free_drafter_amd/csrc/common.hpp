@@ -24,6 +24,10 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
 __device__ __forceinline__ void load_lds16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
 }
+// The same with the non-temporal hint (data read once from HBM).
+__device__ __forceinline__ void load_lds16_nt(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(l), 16, 0, 2);
+}
 
 // ------------------------------------------------------------ bf16 <-> f32 --
 

@@ -167,7 +167,8 @@ Plan make_plan(const dlite_dims& d, int G = 1) {
   // (and the P partials when the fused kernel computes P: at most 16 slices)
   p.U = take(scan_scratch_floats(d.B, d.rank) * 4 +
              (seqhead_fused(d.B, d.K, d.rank, d.dtype == DLITE_BF16)
-                  ? seqhead_fold_bytes(d.B * d.K) + seqhead_pw_bytes(d.B * d.K, d.rank, 16)
+                  ? seqhead_fold_bytes(d.B * d.K) + seqhead_sw_bytes(d.B * d.K, d.rank) +
+                        seqhead_pw_bytes(d.B * d.K, d.rank, 16)
                   : 0));
   p.Sf = take(B * K * r * 4);
   p.Sb = take(B * K * r * es);
@@ -347,8 +348,9 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   // tagged partials follow the helpers' words in the cleared region)
   const int p_slices = !gh ? seqhead_p_slices(B, K, r, D) : 0;
   const size_t fold_bytes = seqhead_fused(B, K, r, bf16) ? seqhead_fold_bytes(B * K) : 0;
+  const size_t sw_bytes = seqhead_fused(B, K, r, bf16) ? seqhead_sw_bytes(B * K, r) : 0;
   const size_t pw_bytes = p_slices ? seqhead_pw_bytes(B * K, r, p_slices) : 0;
-  fa.n_clear = static_cast<long>((scan_scratch_floats(B, r) * sizeof(float) + fold_bytes + pw_bytes) / 16);
+  fa.n_clear = static_cast<long>((scan_scratch_floats(B, r) * sizeof(float) + fold_bytes + sw_bytes + pw_bytes) / 16);
   fa.B = B; fa.m = m; fa.K = K; fa.D = D; fa.V = d.vocab; fa.n_layers = d.n_layers;
   fa.eps = d.rms_eps; fa.G = G; fa.gids = op.gids;
   DLITE_LAUNCH(mark(DLITE_STAGE_FEATURES, true, st));
@@ -518,8 +520,9 @@ int draft_impl(const dlite_dims* dims, const dlite_weights* w, const FeatureSour
   } else if (seqhead_fused(B, K, r, bf16)) {
     DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, true, st));
     uint64_t* px = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(U) + scan_scratch_floats(B, r) * sizeof(float));
-    uint64_t* pw = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(px) + fold_bytes);
-    DLITE_LAUNCH(launch_seqhead(sa, la, px, p_slices ? &ph : nullptr, p_slices ? pw : nullptr, st));
+    uint64_t* sw = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(px) + fold_bytes);
+    uint64_t* pw = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(sw) + sw_bytes);
+    DLITE_LAUNCH(launch_seqhead(sa, la, px, sw, p_slices ? &ph : nullptr, p_slices ? pw : nullptr, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_SCAN, false, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, true, st));
     DLITE_LAUNCH(mark(DLITE_STAGE_LM_HEAD, false, st));

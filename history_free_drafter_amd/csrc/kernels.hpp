@@ -247,8 +247,10 @@ int lmhead_groups(int V);
 // kFuseMaxHelpers partials per token in LmArgs::part_max / part_idx.
 constexpr int kFuseMaxHelpers = 1024;
 bool seqhead_fused(int B, int K, int r, bool bf16);
-// px: seqhead_fold_bytes(B K) of zeroed scratch (the helpers' tagged words).
+// px: seqhead_fold_bytes(B K) of zeroed scratch (the helpers' tagged words);
+// sw: seqhead_sw_bytes(B K, r) of zeroed scratch (the teams' tagged states).
 size_t seqhead_fold_bytes(int M);
+size_t seqhead_sw_bytes(int M, int r);
 // The fused kernel can also compute the scan's input P = W_down[:, :D] h
 // itself (ph: the GEMM arguments of the separate launch, EPI_STORE_F32): its
 // first helpers each take a 16-row tile and a k slice and publish tagged
@@ -256,8 +258,8 @@ size_t seqhead_fold_bytes(int M);
 // number of k slices (0: P must come from the separate launch).
 int seqhead_p_slices(int B, int K, int r, int D);
 size_t seqhead_pw_bytes(int M, int r, int slices);   // zeroed scratch for pw
-hipError_t launch_seqhead(const ScanArgs& s, const LmArgs& l, uint64_t* px, const GemmArgs* ph, uint64_t* pw,
-                          hipStream_t st);
+hipError_t launch_seqhead(const ScanArgs& s, const LmArgs& l, uint64_t* px, uint64_t* sw, const GemmArgs* ph,
+                          uint64_t* pw, hipStream_t st);
 
 // ------------------------------------------------- gated sequential head ----
 constexpr int kGatedMaxRank = 512;

@@ -342,14 +342,20 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_pipe_kernel(LmArgs a) {
 // on the team but the team never waits on helpers, and the team's workgroups
 // come first in dispatch order, so the wait always ends; it is also bounded.
 constexpr int kFuseRegs = 192;            // VGPRs per lane for resident fragments
-constexpr int kFuseLdsTiles = 144 * 1024; // LDS bytes for resident tiles
+constexpr int kFuseLdsTiles = 144 * 1024; // LDS bytes for resident tiles (gated head)
+// Sequential head: LDS bytes for resident tiles and rows of staged states.
+// Up to 8 states (one request) the states take 8 rows and the tiles 144 KB,
+// else 16 rows and 128 KB (one tile per wave).
+__host__ __device__ constexpr int seq_state_rows(int M) { return M <= 8 ? 8 : 16; }
+__host__ __device__ constexpr int seq_lds_tiles(int M, int RK) { return (M <= 8 ? 144 : 128) / RK; }
+constexpr int kTouchLds = 256;            // LDS bytes that receive the touch loads (never read)
 constexpr int kStatePad = 32;             // bf16 elements after each staged state row (spreads banks)
 
 struct FuseArgs {
   ScanArgs sa;
   LmArgs la;
   int nteam;        // scan teams (one request each): blocks xq * 8 + t, t < nteam, xq < team size
-  unsigned* done;   // published-state counter of the team members
+  uint64_t* sw;     // [M][r / 2] tagged bf16 state pairs published by the teams (zero at launch)
   uint64_t* px;     // [M, G] tagged (max, index) words of the helpers (zero at launch)
   GemmArgs ph;      // P = W_down[:, :D] h, when the helpers compute it (nps > 0)
   int nps;          // its k slices: helper q * nps + p takes row tile q, slice p
@@ -474,17 +480,15 @@ template <int RK>   // k-steps of 32 (r / 32)
 __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
   using namespace scan_detail;
   constexpr int TR = kFuseRegs / (4 * RK);         // register tiles per wave
-  constexpr int TL = kFuseLdsTiles / (RK * 1024);  // LDS tiles per workgroup
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float sv[kWaves][16];
   __shared__ int si[kWaves][16];
 
   const int bx = blockIdx.x, xq = bx >> 3, x = bx & 7;
   const int nteam = f.nteam;
-  unsigned* done = f.done;
   constexpr int kTeam = (RK * 32) % 256 == 0 ? 16 : 8;   // members per scan team (team_size(r, B), B <= 8)
   if (xq < kTeam && x < nteam) {
-    scan_team<uint16_t, kTeam>(f.sa, reinterpret_cast<float*>(smem), x, xq, done);
+    scan_team<uint16_t, kTeam>(f.sa, reinterpret_cast<float*>(smem), x, xq, f.sw);
     // then the argmax of the tokens from the helpers' words
     __syncthreads();
     fold_tokens(f, x * kTeam + xq, kTeam * nteam, static_cast<int>(gridDim.x) - kTeam * nteam, smem);
@@ -510,75 +514,113 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
     return W + static_cast<long>(row) * r + s * 32 + grp * 8;
   };
 
+  const int TL = seq_lds_tiles(M, RK);            // LDS tiles per workgroup
+  const int SR = seq_state_rows(M);               // staged state rows (zeros past M)
   uint4* lds_w = reinterpret_cast<uint4*>(smem);                                   // [TL][RK][64]
-  uint16_t* lds_s = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(TL) * RK * 1024);  // [M][r + pad]
+  uint16_t* lds_s = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(TL) * RK * 1024);  // [SR][r + pad]
+  unsigned char* lds_touch = smem + static_cast<size_t>(TL) * RK * 1024 + static_cast<size_t>(SR) * (r + kStatePad) * 2;
 
-  // ---- while the scan runs: resident tiles
+  // ---- while the scan runs: resident tiles.  Register tiles are loaded in
+  //      fragment order (16 bytes of each of 16 rows per instruction, the
+  //      two halves of a 128-byte line by consecutive instructions).  LDS
+  //      tiles are loaded row-contiguous (each instruction covers whole
+  //      lines, which streams faster), chunk c of tile row i stored at
+  //      c ^ (i & kSwz) so that the fragment reads spread over the banks.
   const int treg = t0 + wave * TR;             // this wave's register tiles
   uint4 wr[TR][RK];
 #pragma unroll
   for (int i = 0; i < TR; ++i)
 #pragma unroll
     for (int s = 0; s < RK; ++s) wr[i][s] = ld_stream(frag_ptr(treg + i, s));
+  constexpr int CPR = 4 * RK;                  // 16-byte chunks per row
+  constexpr int kSwz = (CPR % 16 == 0) ? 15 : 7;
   const int tlds = t0 + kWaves * TR;           // first LDS tile
   for (int j = wave; j < TL; j += kWaves)
 #pragma unroll
-    for (int s = 0; s < RK; ++s)
-      load_lds16(frag_ptr(tlds + j, s), lds_w + (j * RK + s) * 64);
+    for (int q = 0; q < RK; ++q) {
+      const int g = q * 64 + lane, i = g / CPR, c = g % CPR;
+      int row = (tlds + j) * 16 + i;
+      row = row < V ? row : V - 1;
+      load_lds16_nt(W + static_cast<long>(row) * r + (c ^ (i & kSwz)) * 8, lds_w + (j * RK + q) * 64);
+    }
 
   // ---- the tiles that do not fit: touched once now (one dword per 128-byte
   //      line, temporal loads) so that they sit in L2 when they are streamed
-  //      after the scan
+  //      after the scan.  The touches are direct-to-LDS loads into a scratch
+  //      area that is never read, so no register waits for them and they
+  //      queue behind the resident tiles without stalling the wave.
   const int tstream = tlds + TL;
-  unsigned touch = 0;
   for (int t = tstream + wave; t < t1; t += kWaves) {
     const uint32_t* base = reinterpret_cast<const uint32_t*>(W + static_cast<long>(t) * 16 * r);
     const int lines = (t * 16 + 16 <= V ? 16 : V - t * 16) * r / 64;   // 128-byte lines of the tile
-    for (int l = lane; l < lines; l += 64) touch ^= base[l * 32];
+    for (int l = lane; l < lines; l += 64)
+      __builtin_amdgcn_global_load_lds(base + l * 32, (__attribute__((address_space(3))) void*)(lds_touch), 4, 0, 0);
   }
 
-  // ---- wait for the team's states (relaxed: the states themselves are
-  //      stored and loaded with device scope)
-  if (threadIdx.x == 0) {
-    const unsigned target = static_cast<unsigned>(kTeam * nteam);
-    unsigned spins = 0;
-    while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(8);
-      if (++spins > kSpinLimit) {
-        atomicOr(a.counters + CNT_STATUS, static_cast<unsigned>(STATUS_BARRIER_TIMEOUT));
-        break;
+  // ---- the team's states: tagged words of two bf16 values, the word of
+  //      token t carrying tag (t mod K) + 1 once that step is published;
+  //      every word is requested at once and re-read until its tag is right
+  //      (bounded), then staged in LDS
+  {
+    const int hw = r / 2, nw = M * hw;         // M <= 16, r <= 512: at most 8 words per thread
+    constexpr int kWpt = 4;                    // words per thread and pass (two passes past 8 tokens)
+    for (int base = 0; base < nw; base += kWpt * kWaves * 64) {
+      uint64_t wv[kWpt];
+      auto want = [&](int i) {
+        const int e = base + threadIdx.x + i * kWaves * 64;
+        return static_cast<uint32_t>((e / hw) % a.K + 1);
+      };
+      auto valid = [&](int i) { return base + static_cast<int>(threadIdx.x) + i * kWaves * 64 < nw; };
+#pragma unroll
+      for (int i = 0; i < kWpt; ++i) wv[i] = valid(i) ? ld_tagged(f.sw + base + threadIdx.x + i * kWaves * 64) : 0;
+      unsigned spins = 0;
+      for (;;) {
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < kWpt; ++i) bad = bad || (valid(i) && static_cast<uint32_t>(wv[i] >> 32) != want(i));
+        if (!bad) break;
+        if (++spins > kSpinLimit) {
+          atomicOr(a.counters + CNT_STATUS, static_cast<unsigned>(STATUS_BARRIER_TIMEOUT));
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int i = 0; i < kWpt; ++i)
+          if (valid(i) && static_cast<uint32_t>(wv[i] >> 32) != want(i))
+            wv[i] = ld_tagged(f.sw + base + threadIdx.x + i * kWaves * 64);
+      }
+#pragma unroll
+      for (int i = 0; i < kWpt; ++i) {
+        const int e = base + threadIdx.x + i * kWaves * 64;
+        if (valid(i))
+          *reinterpret_cast<uint32_t*>(lds_s + (e / hw) * (r + kStatePad) + (e % hw) * 2) = static_cast<uint32_t>(wv[i]);
       }
     }
+    // token columns past M read zeros (no select in the fragment reads)
+    for (int e = nw + threadIdx.x; e < SR * hw; e += blockDim.x)
+      *reinterpret_cast<uint32_t*>(lds_s + (e / hw) * (r + kStatePad) + (e % hw) * 2) = 0u;
   }
-  __syncthreads();
-  {
-    const int n16 = M * r / 8;                 // [M][r] bf16 states, 16 bytes at a time
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(a.src), 0, n16 * 16, kRsrcWord3);
-    const int per_row = r / 8;
-    for (int e = threadIdx.x; e < n16; e += blockDim.x)
-      *reinterpret_cast<u32x4*>(lds_s + (e / per_row) * (r + kStatePad) + (e % per_row) * 8) =
-          __builtin_amdgcn_raw_buffer_load_b128(rs, e * 16, 0, kPolicySc1);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): register and LDS tiles have landed too
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): register and LDS tiles have landed
   __syncthreads();
 
   const bool tok_ok = c16 < M;
   auto bfrag = [&](int s) {
-    const uint4 v = *reinterpret_cast<const uint4*>(lds_s + (tok_ok ? c16 : 0) * (r + kStatePad) + s * 32 + grp * 8);
-    return tok_ok ? v : make_uint4(0, 0, 0, 0);
+    return *reinterpret_cast<const uint4*>(lds_s + (c16 & (SR - 1)) * (r + kStatePad) + s * 32 + grp * 8);
   };
   float bv = -INFINITY;
   int bi = 0x7fffffff;
+  float* const tap = a.tap;
   auto take = [&](int t, const floatx4& acc) {
+    const bool ok_t = t < t1 && tok_ok;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int vr = t * 16 + grp * 4 + i;
-      if (t < t1 && vr < V && tok_ok) {
-        const float v = acc[i];
-        if (better(v, vr, bv, bi)) { bv = v; bi = vr; }
-        if (a.tap) a.tap[static_cast<long>(c16) * V + vr] = v;
-      }
+      if (ok_t && vr < V && better(acc[i], vr, bv, bi)) { bv = acc[i]; bi = vr; }
+    }
+    if (tap && ok_t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (t * 16 + grp * 4 + i < V) tap[static_cast<long>(c16) * V + t * 16 + grp * 4 + i] = acc[i];
     }
   };
 
@@ -611,20 +653,31 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
   uint4 bq[RK];
 #pragma unroll
   for (int s = 0; s < RK; ++s) bq[s] = bfrag(s);
+  // one LDS tile per wave: every fragment read is issued before the first
+  // multiply, and the k-steps alternate between two accumulators
   for (int j = wave; j < TL; j += kWaves) {
     uint4 af[RK];
 #pragma unroll
-    for (int s = 0; s < RK; ++s) af[s] = lds_w[(j * RK + s) * 64 + lane];
-    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < RK; ++s) af[s] = lds_w[j * RK * 64 + c16 * CPR + ((4 * s + grp) ^ (c16 & kSwz))];
+    // all reads in flight before the first multiply (one LDS latency per tile)
 #pragma unroll
-    for (int s = 0; s < RK; ++s) acc = mma_step(af[s], bq[s], acc, uint16_t());
-    take(tlds + j, acc);
+    for (int s = 0; s < RK; ++s) asm volatile("" ::"v"(af[s].x), "v"(af[s].y), "v"(af[s].z), "v"(af[s].w));
+    floatx4 acc0 = floatx4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+    for (int s = 0; s < RK; s += 2) {
+      acc0 = mma_step(af[s], bq[s], acc0, uint16_t());
+      if (s + 1 < RK) acc1 = mma_step(af[s + 1], bq[s + 1], acc1, uint16_t());
+    }
+    take(tlds + j, acc0 + acc1);
   }
   for (; t < t1; t += kWaves) {
-    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 acc0 = floatx4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
-    for (int s = 0; s < RK; ++s) acc = mma_step(nx[s], bq[s], acc, uint16_t());
-    take(t, acc);
+    for (int s = 0; s < RK; s += 2) {
+      acc0 = mma_step(nx[s], bq[s], acc0, uint16_t());
+      if (s + 1 < RK) acc1 = mma_step(nx[s + 1], bq[s + 1], acc1, uint16_t());
+    }
+    take(t, acc0 + acc1);
     if (t + kWaves < t1) {
 #pragma unroll
       for (int s = 0; s < RK; ++s) nx[s] = ld_stream(frag_ptr(t + kWaves, s));
@@ -650,13 +703,12 @@ __global__ __launch_bounds__(kWaves * 64) void seqhead_kernel(FuseArgs f) {
     __hip_atomic_store(f.px + static_cast<long>(threadIdx.x) * G + h, pack_best(v, i < V ? i : 0),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (touch == 0x9e3779b9u && M < 0) a.cand[0] = 0;   // keeps the touch loads
 }
 
 template <int RK>
 size_t seqhead_lds(int M, int r) {
-  constexpr int TL = kFuseLdsTiles / (RK * 1024);
-  return static_cast<size_t>(TL) * RK * 1024 + static_cast<size_t>(M) * (r + kStatePad) * 2;
+  return static_cast<size_t>(seq_lds_tiles(M, RK)) * RK * 1024 +
+         static_cast<size_t>(seq_state_rows(M)) * (r + kStatePad) * 2 + kTouchLds;
 }
 
 // --------------------------------------------- fused gated head (few requests) --
@@ -1071,6 +1123,7 @@ bool seqhead_fused(int B, int K, int r, bool bf16) {
 }
 
 size_t seqhead_fold_bytes(int M) { return static_cast<size_t>(M) * kFuseMaxHelpers * sizeof(uint64_t); }
+size_t seqhead_sw_bytes(int M, int r) { return static_cast<size_t>(M) * (r / 2) * sizeof(uint64_t); }
 
 namespace {
 // Grid of the fused kernel (one workgroup per CU, at least 8 per team member).
@@ -1101,7 +1154,8 @@ size_t seqhead_pw_bytes(int M, int r, int slices) {
   return static_cast<size_t>(slices) * M * r * sizeof(uint64_t);
 }
 
-hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, uint64_t* px, const GemmArgs* ph, uint64_t* pw,
+hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, uint64_t* px, uint64_t* sw, const GemmArgs* ph,
+                          uint64_t* pw,
                           hipStream_t st) {
   using namespace scan_detail;
   if (!seqhead_fused(s0.B, s0.K, s0.r, true) || l0.M != s0.B * s0.K || l0.tok0 != 0) return hipErrorInvalidValue;
@@ -1110,7 +1164,7 @@ hipError_t launch_seqhead(const ScanArgs& s0, const LmArgs& l0, uint64_t* px, co
   f.sa.rpt = 1;
   f.sa.tag0 = 0;
   f.nteam = s0.B;
-  f.done = s0.counters + counter_seq_done();
+  f.sw = sw;
   f.px = px;
   if (ph) {
     f.nps = seqhead_p_slices(s0.B, s0.K, s0.r, ph->K);

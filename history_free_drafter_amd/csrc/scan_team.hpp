@@ -170,11 +170,13 @@ __device__ __forceinline__ float dot_f32(const float (&w)[CW], const float4 (&x)
 // chunks: W_up[:, r0:r1] as [r][8] (row slices padded to 8 chunks) and
 // W_s[r0:r1, :] as [nr][r / 8].
 // One team member: workgroup j of team `team` (requests team * rpt ...).
-// done: when given (bf16 states), the bf16 states are stored with
-// device-scope stores and the member counts itself in there once they are
-// complete, for readers in other workgroups (device-scope loads).
+// sw: when given (bf16 states read by other workgroups of the launch), each
+// member publishes its rows of every new state as tagged words [token][r / 2]
+// (two bf16 values in the low half, the step's tag in the high half; one
+// device-scope atomic store each), so readers need no counter: a word with
+// the right tag carries its values.
 template <typename T, int TEAM>
-__device__ __forceinline__ void scan_team(const ScanArgs& a, float* sm, int team, int j, unsigned* done) {
+__device__ __forceinline__ void scan_team(const ScanArgs& a, float* sm, int team, int j, uint64_t* sw) {
   constexpr int H = TEAM / 8;                 // column halves per wave in the first product
   constexpr int CW = 64 / H;                  // register slice width (columns, inputs)
   constexpr bool kBf16 = sizeof(T) == 2;
@@ -415,25 +417,26 @@ __device__ __forceinline__ void scan_team(const ScanArgs& a, float* sm, int team
       for (int w = 0; w < TEAM; ++w) acc += __uint_as_float(static_cast<unsigned>(v[w]));
       s[bb * r + n] = acc;
       if constexpr (kBf16) s16[bb * r + n] = f32_to_bf16(acc);
+      // the neighbouring element (n ^ 1: same wave, same side of every row
+      // boundary since r, r0 and nr are even) for the two-value words
+      const float acc_pair = (kBf16 && sw) ? __shfl_xor(acc, 1, kWave) : 0.f;
       if (n >= r0 && n < r0 + nr) {   // this workgroup's rows
         const long o = (static_cast<long>(b0 + bb) * a.K + k) * r + n;
         a.Sf[o] = acc;
         if (a.tap) a.tap[o] = acc;
-        if (kBf16 && done) {
-          // read by other workgroups in this launch: one device-scope store
-          __hip_atomic_store(static_cast<T*>(a.Sb) + o, Elem<T>::from_f32(acc), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        if (kBf16 && sw) {
+          if ((n & 1) == 0) {
+            const uint32_t lo = f32_to_bf16(acc);
+            const uint32_t hi = f32_to_bf16(acc_pair);
+            __hip_atomic_store(sw + o / 2, (static_cast<uint64_t>(tag) << 32) | (hi << 16) | lo,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         } else {
           static_cast<T*>(a.Sb)[o] = Elem<T>::from_f32(acc);
         }
       }
     }
     __syncthreads();
-  }
-  if (done) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's state stores are done
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
