@@ -156,25 +156,27 @@ def gatedhead_is_fused(w, head="fixed"):
 
 # -------------------------------------------------------------- HBM traffic ---
 
-def kernel_source_hash():
-    """sha256 over the kernel sources (csrc/*.hip, *.hpp in name order)."""
+def kernel_source_hash(files=None):
+    """sha256 over kernel sources in name order: the given csrc files (the
+    kernel's own source and the headers it includes), else every csrc/*.hip,
+    *.hpp."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".hpp")):
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    names = files if files else [f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp"))]
+    for f in sorted(names):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
 def traffic_record(workload, stage):
     """HBM bytes per launch of a stage's kernel(s) from the committed counter
     summaries (profiles/*.md, lines 'traffic-record: {json}'), scaled by the
-    copy calibration.  None when no record matches or the kernel sources
-    changed since the counters were taken."""
+    copy calibration.  None when no record matches or the kernel's sources
+    (the record's "sources", else all of csrc) changed since the counters
+    were taken."""
     if not os.path.isdir(PROFILES):
         return None
-    cur = kernel_source_hash()
     for f in sorted(os.listdir(PROFILES)):
         if not f.endswith(".md"):
             continue
@@ -185,7 +187,7 @@ def traffic_record(workload, stage):
                 rec = json.loads(line.split(":", 1)[1])
                 if rec.get("workload") != workload or rec.get("stage") != stage:
                     continue
-                if rec.get("source_sha256") != cur:
+                if rec.get("source_sha256") != kernel_source_hash(rec.get("sources")):
                     return None
                 return (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]) * 1024.0
     return None
