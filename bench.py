@@ -159,13 +159,20 @@ def gatedhead_is_fused(w, head="fixed"):
 def kernel_source_hash(files=None):
     """sha256 over kernel sources in name order: the given csrc files (the
     kernel's own source and the headers it includes), else every csrc/*.hip,
-    *.hpp."""
+    *.hpp; line comments and blank space are left out, so that a change of
+    comments alone keeps a record valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     names = files if files else [f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp"))]
     for f in sorted(names):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            code = []
+            for line in fh:
+                line = re.sub(r"//.*$", "", line).strip()
+                if line:
+                    code.append(" ".join(line.split()))
+        h.update(f.encode() + b"\0" + "\n".join(code).encode())
     return h.hexdigest()
 
 

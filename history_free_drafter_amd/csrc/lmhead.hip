@@ -335,12 +335,14 @@ __global__ __launch_bounds__(kWaves * 64) void lmhead_pipe_kernel(LmArgs a) {
 // workgroup ("helper") owns a contiguous range of 16-row vocabulary tiles and,
 // while the scan runs, pulls its tiles on chip: TR tiles per wave into
 // registers as ready MFMA fragments, TL tiles per workgroup into LDS
-// (global_load_lds, fragment order).  When the team has published the states
-// (release on a device-scope counter), helpers acquire, stage the states in
-// LDS, multiply the resident tiles, stream the few tiles that did not fit,
-// and reduce (max, index) exactly as the streaming pass does.  Helpers wait
-// on the team but the team never waits on helpers, and the team's workgroups
-// come first in dispatch order, so the wait always ends; it is also bounded.
+// (global_load_lds, row-contiguous).  The team publishes every state as
+// tagged words; helpers read them, stage the states in LDS, multiply the
+// resident tiles, stream the few tiles that did not fit, and publish one
+// tagged (max, index) word per token, which the team folds.  The team waits
+// on the first helpers (the scan's input P) and on all helpers (the fold), the
+// helpers on the team (the states): the launch is one workgroup per CU (at
+// most 256, all resident at once), and every wait is bounded and flags the
+// status word on time-out, so the kernel always drains.
 constexpr int kFuseRegs = 192;            // VGPRs per lane for resident fragments
 constexpr int kFuseLdsTiles = 144 * 1024; // LDS bytes for resident tiles (gated head)
 // Sequential head: LDS bytes for resident tiles and rows of staged states.
