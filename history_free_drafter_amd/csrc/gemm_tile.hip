@@ -47,6 +47,7 @@ constexpr int kSplitTarget = 256;        // work items wanted per launch
 constexpr int kSplitBelow = 128;         // split K only for launches with fewer tiles
 constexpr int kMinSlice = 4;             // stages per k slice, at least
 constexpr int kDirectSum = 2;            // slices the epilogue pass adds itself
+constexpr int kPipeItems = 256;          // work items up to which the main loop is pipelined
 
 // MODE_REDUCE1: the reduce pass with one wave per workgroup (4 workgroups
 // per output tile) for epilogues that need no exchange between waves.
@@ -75,8 +76,8 @@ __device__ __forceinline__ long weight_row(const GemmArgs& a, int nb, int l) {
   return n < a.N ? n : a.N - 1;
 }
 
-template <int EPI, int MODE>
-__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
+template <int EPI, int MODE, int PIPE>
+__global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs ta) {
   constexpr int WTM = 2;                      // 32-token blocks per wave
   constexpr int NT = 256;                     // four waves, 2 x 2 over the tile
   constexpr int BM = kBM;
@@ -86,7 +87,8 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
   constexpr int TPT = NT / BM;                // threads per token for the norm sums
   extern __shared__ __align__(16) unsigned char smem[];
   uint4* lds = reinterpret_cast<uint4*>(smem);                      // [ROWS * 8] chunks
-  float* red = reinterpret_cast<float*>(smem + ROWS * kRowB);       // [TPT][BM]
+  constexpr int NBUF = MODE == MODE_FULL || MODE == MODE_SLICE ? 1 + PIPE : 0;   // LDS stage buffers
+  float* red = reinterpret_cast<float*>(smem + NBUF * ROWS * kRowB);   // [TPT][BM]
   float* bv_s = red + TPT * BM;                                     // [2][BM] argmax values
   int* bi_s = reinterpret_cast<int*>(bv_s + 2 * BM);                // [2][BM] argmax indices
 
@@ -147,44 +149,110 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs ta) {
     }
     const int nk = a.K / kBK;
     const int k0 = (slice * nk) / S, k1 = ((slice + 1) * nk) / S;
-    uint4 pre[NLD];
-    auto load_stage = [&](int kt) {
+    // two register stages and two LDS buffers: while stage kt is multiplied
+    // out of one buffer, stage kt + 1 waits in registers for the other and
+    // stage kt + 2 is on its way from memory
+    uint4 ra[NLD], rb[NLD];
+    auto load_stage = [&](uint4 (&r)[NLD], int kt) {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const uint16_t* q = gp[i] + static_cast<long>(kt) * kBK;
-        pre[i] = i < NLA ? ld_stream(q) : *reinterpret_cast<const uint4*>(q);
+        r[i] = i < NLA ? ld_stream(q) : *reinterpret_cast<const uint4*>(q);
       }
     };
-    auto store_stage = [&]() {
+    auto store_stage = [&](const uint4 (&r)[NLD], int buf) {
+      uint4* l = lds + buf * (ROWS * 8);
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) lds[swz((tid >> 3) + i * (NT / 8), kc)] = pre[i];
+      for (int i = 0; i < NLD; ++i) l[swz((tid >> 3) + i * (NT / 8), kc)] = r[i];
     };
-    auto compute = [&]() {
+    auto compute = [&](int buf) {
+      const uint4* l = lds + buf * (ROWS * 8);
 #pragma unroll
       for (int ks = 0; ks < kBK / 16; ++ks) {
         const int ch = 2 * ks + fk;
         uint4 af[4], bf[WTM];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = lds[swz(wn * 128 + i * 32 + fr, ch)];
+        for (int i = 0; i < 4; ++i) af[i] = l[swz(wn * 128 + i * 32 + fr, ch)];
 #pragma unroll
-        for (int u = 0; u < WTM; ++u) bf[u] = lds[swz(kBN + wm * (BM / 2) + u * 32 + fr, ch)];
+        for (int u = 0; u < WTM; ++u) bf[u] = l[swz(kBN + wm * (BM / 2) + u * 32 + fr, ch)];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int u = 0; u < WTM; ++u) acc[i][u] = mma32(af[i], bf[u], acc[i][u]);
       }
     };
-
-    load_stage(k0);
-    store_stage();
-    __syncthreads();
-    for (int kt = k0; kt < k1; ++kt) {
-      if (kt + 1 < k1) load_stage(kt + 1);
-      compute();
+    // the pipelined step: the fragments of k step ks + 1 are read while the
+    // MFMAs of ks run, and the next stage's registers go into the other
+    // buffer between them (a quarter per k step)
+    auto compute_store = [&](int buf, const uint4 (&r)[NLD]) {
+      const uint4* l = lds + buf * (ROWS * 8);
+      uint4* lw = lds + (buf ^ 1) * (ROWS * 8);
+      uint4 af[2][4], bf[2][WTM];
+      auto rd = [&](int ks, int h) {
+        const int ch = 2 * ks + fk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[h][i] = l[swz(wn * 128 + i * 32 + fr, ch)];
+#pragma unroll
+        for (int u = 0; u < WTM; ++u) bf[h][u] = l[swz(kBN + wm * (BM / 2) + u * 32 + fr, ch)];
+      };
+      rd(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < kBK / 16; ++ks) {
+        if (ks + 1 < kBK / 16) rd(ks + 1, (ks + 1) & 1);
+        constexpr int NQ = NLD / (kBK / 16);
+#pragma unroll
+        for (int i = ks * NQ; i < (ks + 1) * NQ; ++i) lw[swz((tid >> 3) + i * (NT / 8), kc)] = r[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int u = 0; u < WTM; ++u) acc[i][u] = mma32(af[ks & 1][i], bf[ks & 1][u], acc[i][u]);
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads a k step ahead
+      }
+    };
+    int kt = k0;
+    if (PIPE && k1 - k0 >= 4) {
+      load_stage(ra, k0);
+      load_stage(rb, k0 + 1);
+      store_stage(ra, 0);
       __syncthreads();
-      if (kt + 1 < k1) {
-        store_stage();
+      load_stage(ra, k0 + 2);
+      // steady state: buffer 0 holds stage kt, rb stage kt + 1, ra stage
+      // kt + 2.  The loads here are unconditional so that the wait before
+      // each buffer store covers only the older register stage.
+      for (; kt + 4 < k1; kt += 2) {
+        compute_store(0, rb);
         __syncthreads();
+        load_stage(rb, kt + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_store(1, ra);
+        __syncthreads();
+        load_stage(ra, kt + 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the last three or four stages
+      auto step = [&](int k, int b, uint4 (&r)[NLD]) {
+        compute(b);
+        if (k + 1 < k1) store_stage(r, b ^ 1);
+        __syncthreads();
+        if (k + 3 < k1) load_stage(r, k + 3);
+      };
+      for (; kt < k1; kt += 2) {
+        step(kt, 0, rb);
+        if (kt + 1 < k1) step(kt + 1, 1, ra);
+      }
+    } else {
+      // one register stage, one buffer (two workgroups per CU, or short k slices)
+      load_stage(ra, k0);
+      store_stage(ra, 0);
+      __syncthreads();
+      for (; kt < k1; ++kt) {
+        if (kt + 1 < k1) load_stage(ra, kt + 1);
+        compute(0);
+        __syncthreads();
+        if (kt + 1 < k1) {
+          store_stage(ra, 0);
+          __syncthreads();
+        }
       }
     }
     if (MODE == MODE_SLICE) {
@@ -458,17 +526,28 @@ __global__ __launch_bounds__(256) void slice_sum_kernel(float* part, int tiles, 
   base[0] = acc;
 }
 
-template <int EPI, int MODE>
-hipError_t launch_tile_t(const TileArgs& ta, int items, hipStream_t st) {
-  const size_t sm = static_cast<size_t>(kBN + kBM) * kRowB + (256ull + 4ull * kBM) * 4;
-  const void* fn = reinterpret_cast<const void*>(&gemm_tile_kernel<EPI, MODE>);
+template <int EPI, int MODE, int PIPE>
+hipError_t launch_tile_t1(const TileArgs& ta, int items, hipStream_t st) {
+  const size_t nbuf = MODE == MODE_FULL || MODE == MODE_SLICE ? 1 + PIPE : 0;
+  const size_t sm = nbuf * (kBN + kBM) * kRowB + (256ull + 4ull * kBM) * 4;
+  const void* fn = reinterpret_cast<const void*>(&gemm_tile_kernel<EPI, MODE, PIPE>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
   if (e != hipSuccess) return e;
   const int per_xcd = (items + 7) / 8;
   TileArgs t = ta;
   t.per_xcd = per_xcd;
-  launch_k((gemm_tile_kernel<EPI, MODE>), dim3(8 * per_xcd), dim3(MODE == MODE_REDUCE1 ? 64 : 256), sm, st, t);
+  launch_k((gemm_tile_kernel<EPI, MODE, PIPE>), dim3(8 * per_xcd), dim3(MODE == MODE_REDUCE1 ? 64 : 256), sm, st, t);
   return hipGetLastError();
+}
+
+// Main-loop passes with at most one work item per CU take the two-stage
+// pipeline (one workgroup per CU); larger ones keep two workgroups per CU.
+template <int EPI, int MODE>
+hipError_t launch_tile_t(const TileArgs& ta, int items, hipStream_t st) {
+  if constexpr (MODE == MODE_FULL || MODE == MODE_SLICE) {
+    if (items <= kPipeItems) return launch_tile_t1<EPI, MODE, 1>(ta, items, st);
+  }
+  return launch_tile_t1<EPI, MODE, 0>(ta, items, st);
 }
 
 template <int EPI>
