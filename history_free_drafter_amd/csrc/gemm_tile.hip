@@ -64,8 +64,16 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk
 
 // Weight row behind LDS row l of output tile nb (SwiGLU: 64-row blocks
 // alternate gate and up rows of the same 64 outputs).
-template <int EPI>
+template <int EPI, int WTN>
 __device__ __forceinline__ long weight_row(const GemmArgs& a, int nb, int l) {
+  if (EPI == EPI_SWIGLU && WTN == 3) {
+    // 96 rows per wave: each 32-row block holds the gate rows (first 16) and
+    // the up rows (last 16) of the same 16 outputs
+    const int w = l / 96, r = l % 96, i = r >> 5, h = r & 31;
+    int n = nb * 96 + w * 48 + i * 16 + (h & 15);
+    n = n < a.N ? n : a.N - 1;
+    return n + ((h & 16) ? a.pair_off : 0);
+  }
   if (EPI == EPI_SWIGLU) {
     const int q = l >> 6;
     int n = nb * (kBN / 2) + (q >> 1) * 64 + (l & 63);
@@ -76,9 +84,12 @@ __device__ __forceinline__ long weight_row(const GemmArgs& a, int nb, int l) {
   return n < a.N ? n : a.N - 1;
 }
 
-template <int EPI, int MODE, int PIPE>
+template <int EPI, int MODE, int PIPE, int WTN>
 __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs ta) {
+  static_assert(WTN == 4 || EPI == EPI_SWIGLU, "three-block waves only for SwiGLU");
   constexpr int WTM = 2;                      // 32-token blocks per wave
+  constexpr int kBN = 64 * WTN;               // weight rows per tile (WTN 32-row blocks per wave)
+  constexpr int WR = 32 * WTN;                // weight rows per wave
   constexpr int NT = 256;                     // four waves, 2 x 2 over the tile
   constexpr int BM = kBM;
   constexpr int ROWS = kBN + BM;              // LDS rows per stage
@@ -119,9 +130,9 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
   const int wn = wave & 1, wm = wave >> 1;
   const int fr = lane & 31, fk = lane >> 5;
 
-  floatx16 acc[4][WTM];
+  floatx16 acc[WTN][WTM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WTN; ++i)
 #pragma unroll
     for (int u = 0; u < WTM; ++u)
 #pragma unroll
@@ -140,7 +151,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
     for (int i = 0; i < NLD; ++i) {
       const int row = (tid >> 3) + i * (NT / 8);
       if (i < NLA) {
-        gp[i] = W + weight_row<EPI>(a, nb, row) * a.ldw + kc * 8;
+        gp[i] = W + weight_row<EPI, WTN>(a, nb, row) * a.ldw + kc * 8;
       } else {
         int tk = m0 + row - kBN;
         tk = tk < a.M ? tk : a.M - 1;
@@ -170,13 +181,13 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
 #pragma unroll
       for (int ks = 0; ks < kBK / 16; ++ks) {
         const int ch = 2 * ks + fk;
-        uint4 af[4], bf[WTM];
+        uint4 af[WTN], bf[WTM];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = l[swz(wn * 128 + i * 32 + fr, ch)];
+        for (int i = 0; i < WTN; ++i) af[i] = l[swz(wn * WR + i * 32 + fr, ch)];
 #pragma unroll
         for (int u = 0; u < WTM; ++u) bf[u] = l[swz(kBN + wm * (BM / 2) + u * 32 + fr, ch)];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WTN; ++i)
 #pragma unroll
           for (int u = 0; u < WTM; ++u) acc[i][u] = mma32(af[i], bf[u], acc[i][u]);
       }
@@ -187,11 +198,11 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
     auto compute_store = [&](int buf, const uint4 (&r)[NLD]) {
       const uint4* l = lds + buf * (ROWS * 8);
       uint4* lw = lds + (buf ^ 1) * (ROWS * 8);
-      uint4 af[2][4], bf[2][WTM];
+      uint4 af[2][WTN], bf[2][WTM];
       auto rd = [&](int ks, int h) {
         const int ch = 2 * ks + fk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[h][i] = l[swz(wn * 128 + i * 32 + fr, ch)];
+        for (int i = 0; i < WTN; ++i) af[h][i] = l[swz(wn * WR + i * 32 + fr, ch)];
 #pragma unroll
         for (int u = 0; u < WTM; ++u) bf[h][u] = l[swz(kBN + wm * (BM / 2) + u * 32 + fr, ch)];
       };
@@ -199,11 +210,11 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
 #pragma unroll
       for (int ks = 0; ks < kBK / 16; ++ks) {
         if (ks + 1 < kBK / 16) rd(ks + 1, (ks + 1) & 1);
-        constexpr int NQ = NLD / (kBK / 16);
 #pragma unroll
-        for (int i = ks * NQ; i < (ks + 1) * NQ; ++i) lw[swz((tid >> 3) + i * (NT / 8), kc)] = r[i];
+        for (int i = ks * NLD / (kBK / 16); i < (ks + 1) * NLD / (kBK / 16); ++i)
+          lw[swz((tid >> 3) + i * (NT / 8), kc)] = r[i];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WTN; ++i)
 #pragma unroll
           for (int u = 0; u < WTM; ++u) acc[i][u] = mma32(af[ks & 1][i], bf[ks & 1][u], acc[i][u]);
         __builtin_amdgcn_sched_barrier(0);   // keep the reads a k step ahead
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
     if (MODE == MODE_SLICE) {
       float4* pp = reinterpret_cast<float4*>(part_at(slice));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WTN; ++i)
 #pragma unroll
         for (int u = 0; u < WTM; ++u)
 #pragma unroll
@@ -273,7 +284,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
     for (int sl = 0; sl < ta.nsum; ++sl) {
       const float4* pp = reinterpret_cast<const float4*>(part_at(sl));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WTN; ++i)
 #pragma unroll
         for (int u = 0; u < WTM; ++u)
 #pragma unroll
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
     // a lane's values come in increasing row order, so "strictly greater"
     // keeps the lowest index among equal maxima; rows past N only exist in
     // the last weight tile
-    const int nbase = nb * kBN + wn * 128 + 4 * fk;
+    const int nbase = nb * kBN + wn * WR + 4 * fk;
     const bool full = nb * kBN + kBN <= a.N;
 #pragma unroll
     for (int u = 0; u < WTM; ++u) {
@@ -346,7 +357,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
       int bi = 0x7fffffff;
       if (full) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WTN; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -358,7 +369,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
             }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WTN; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -388,7 +399,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
         if (!tok_ok[u]) continue;
         float* trow = a.tap + a.tmap.row(a.tok0 + tk[u]) * a.ld_tap;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WTN; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int n = nbase + i * 32 + 8 * q;
@@ -419,7 +430,31 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
   auto store_u = [&](int u, auto chk) {
     constexpr bool CHK = decltype(chk)::value;
     const long orow = a.omap.row(a.tok0 + tk[u]);
-    if (EPI == EPI_SWIGLU) {
+    if (EPI == EPI_SWIGLU && WTN == 3) {
+      // gate rows 8 q + 4 fk + e (q < 2) and up rows 16 + the same of each block
+      uint16_t* out = static_cast<uint16_t*>(a.out) + orow * a.ld_out;
+#pragma unroll
+      for (int i = 0; i < WTN; ++i)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int n = nb * 96 + wn * 48 + i * 16 + 8 * q + 4 * fk;
+          if (CHK && n >= a.N) continue;
+          uint32_t h[2];
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            float r2[2];
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+              const float gt = acc[i][u][4 * q + e + f] * inv[u];
+              const float up = acc[i][u][4 * (q + 2) + e + f] * inv[u];
+              r2[f] = gt / (1.0f + expf(-gt)) * up;
+            }
+            h[e / 2] = static_cast<uint32_t>(f32_to_bf16(r2[0])) |
+                       (static_cast<uint32_t>(f32_to_bf16(r2[1])) << 16);
+          }
+          *reinterpret_cast<uint2*>(out + n) = make_uint2(h[0], h[1]);
+        }
+    } else if (EPI == EPI_SWIGLU) {
       uint16_t* out = static_cast<uint16_t*>(a.out) + orow * a.ld_out;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -434,7 +469,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
               const float gt = acc[i][u][4 * q + e + f] * inv[u];
-              const float up = acc[i + 2][u][4 * q + e + f] * inv[u];
+              const float up = acc[i + 2 < WTN ? i + 2 : 0][u][4 * q + e + f] * inv[u];
               r2[f] = gt / (1.0f + expf(-gt)) * up;
             }
             h[e / 2] = static_cast<uint32_t>(f32_to_bf16(r2[0])) |
@@ -454,18 +489,18 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
       auto fetch = [&](int i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          int n = nb * kBN + wn * 128 + i * 32 + 8 * q + 4 * fk;
+          int n = nb * kBN + wn * WR + i * 32 + 8 * q + 4 * fk;
           n = (CHK && n >= a.N) ? nb * kBN : n;   // in range; unused
           xr[q] = *reinterpret_cast<const float4*>(static_cast<const float*>(a.out) + orow * a.ld_out + n);
           gr[q] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.next_gain) + n);
         }
       };
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WTN; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           if (kBatch && q == 0) fetch(i);
-          const int n = nb * kBN + wn * 128 + i * 32 + 8 * q + 4 * fk;
+          const int n = nb * kBN + wn * WR + i * 32 + 8 * q + 4 * fk;
           if (CHK && n >= a.N) continue;
           const float4 y = make_float4(acc[i][u][4 * q] * inv[u], acc[i][u][4 * q + 1] * inv[u],
                                        acc[i][u][4 * q + 2] * inv[u], acc[i][u][4 * q + 3] * inv[u]);
@@ -495,7 +530,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
       if (EPI == EPI_RESID && a.ssq_out) {
         // the two row halves of this token's 128 rows sit in lanes fr, fr + 32
         ssq += __shfl_xor(ssq, 32, kWave);
-        if (fk == 0) a.ssq_out[orow * kSsqParts + (nb * kBN + wn * 128) / 128] = ssq;
+        if (fk == 0) a.ssq_out[orow * kSsqParts + (nb * kBN + wn * WR) / 128] = ssq;
       }
     }
   };
@@ -526,34 +561,34 @@ __global__ __launch_bounds__(256) void slice_sum_kernel(float* part, int tiles, 
   base[0] = acc;
 }
 
-template <int EPI, int MODE, int PIPE>
+template <int EPI, int MODE, int PIPE, int WTN>
 hipError_t launch_tile_t1(const TileArgs& ta, int items, hipStream_t st) {
   const size_t nbuf = MODE == MODE_FULL || MODE == MODE_SLICE ? 1 + PIPE : 0;
-  const size_t sm = nbuf * (kBN + kBM) * kRowB + (256ull + 4ull * kBM) * 4;
-  const void* fn = reinterpret_cast<const void*>(&gemm_tile_kernel<EPI, MODE, PIPE>);
+  const size_t sm = nbuf * (64 * WTN + kBM) * kRowB + (256ull + 4ull * kBM) * 4;
+  const void* fn = reinterpret_cast<const void*>(&gemm_tile_kernel<EPI, MODE, PIPE, WTN>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sm));
   if (e != hipSuccess) return e;
   const int per_xcd = (items + 7) / 8;
   TileArgs t = ta;
   t.per_xcd = per_xcd;
-  launch_k((gemm_tile_kernel<EPI, MODE, PIPE>), dim3(8 * per_xcd), dim3(MODE == MODE_REDUCE1 ? 64 : 256), sm, st, t);
+  launch_k((gemm_tile_kernel<EPI, MODE, PIPE, WTN>), dim3(8 * per_xcd), dim3(MODE == MODE_REDUCE1 ? 64 : 256), sm, st, t);
   return hipGetLastError();
 }
 
 // Main-loop passes with at most one work item per CU take the two-stage
 // pipeline (one workgroup per CU); larger ones keep two workgroups per CU.
-template <int EPI, int MODE>
+template <int EPI, int MODE, int WTN>
 hipError_t launch_tile_t(const TileArgs& ta, int items, hipStream_t st) {
   if constexpr (MODE == MODE_FULL || MODE == MODE_SLICE) {
-    if (items <= kPipeItems) return launch_tile_t1<EPI, MODE, 1>(ta, items, st);
+    if (items <= kPipeItems) return launch_tile_t1<EPI, MODE, 1, WTN>(ta, items, st);
   }
-  return launch_tile_t1<EPI, MODE, 0>(ta, items, st);
+  return launch_tile_t1<EPI, MODE, 0, WTN>(ta, items, st);
 }
 
-template <int EPI>
+template <int EPI, int WTN = 4>
 hipError_t launch_tile_e(const TileArgs& ta, hipStream_t st) {
-  if (ta.ksplit == 1) return launch_tile_t<EPI, MODE_FULL>(ta, ta.total, st);
-  hipError_t e = launch_tile_t<EPI, MODE_SLICE>(ta, ta.total * ta.ksplit, st);
+  if (ta.ksplit == 1) return launch_tile_t<EPI, MODE_FULL, WTN>(ta, ta.total, st);
+  hipError_t e = launch_tile_t<EPI, MODE_SLICE, WTN>(ta, ta.total * ta.ksplit, st);
   if (e != hipSuccess) return e;
   TileArgs tr = ta;
   tr.nsum = ta.ksplit;
@@ -566,28 +601,40 @@ hipError_t launch_tile_e(const TileArgs& ta, hipStream_t st) {
     if (e != hipSuccess) return e;
     tr.nsum = 1;
   }
-  if constexpr (EPI == EPI_ARGMAX) return launch_tile_t<EPI, MODE_REDUCE>(tr, ta.total, st);
-  else return launch_tile_t<EPI, MODE_REDUCE1>(tr, ta.total * 4, st);
+  if constexpr (EPI == EPI_ARGMAX) return launch_tile_t<EPI, MODE_REDUCE, WTN>(tr, ta.total, st);
+  else return launch_tile_t<EPI, MODE_REDUCE1, WTN>(tr, ta.total * 4, st);
 }
 
 // Output tiles of each problem and the k split of the launch.
 struct TilePlan {
-  int nbm[2], tiles[2], total, ksplit;
+  int nbm[2], tiles[2], total, ksplit, wtn;
 };
 
 TilePlan plan_tiles(const int* M, const int* N, int nseg, int K, int epi) {
   TilePlan p{};
-  const int bno = epi == EPI_SWIGLU ? kBN / 2 : kBN;
-  for (int s = 0; s < nseg; ++s) {
-    p.nbm[s] = (M[s] + kBM - 1) / kBM;
-    p.tiles[s] = M[s] > 0 ? ((N[s] + bno - 1) / bno) * p.nbm[s] : 0;
-    p.total += p.tiles[s];
+  auto count = [&](int bno) {
+    p.total = 0;
+    for (int s = 0; s < nseg; ++s) {
+      p.nbm[s] = (M[s] + kBM - 1) / kBM;
+      p.tiles[s] = M[s] > 0 ? ((N[s] + bno - 1) / bno) * p.nbm[s] : 0;
+      p.total += p.tiles[s];
+    }
+  };
+  // SwiGLU whose 128-output tiles leave CUs idle takes 96-output tiles
+  // (three 32-row blocks per wave) when those still fit one pipelined round
+  // without a k split
+  p.wtn = 4;
+  count(epi == EPI_SWIGLU ? kBN / 2 : kBN);
+  if (epi == EPI_SWIGLU && p.total < kPipeItems) {
+    count(96);
+    if (p.total > kPipeItems || p.total < kSplitBelow) count(kBN / 2);
+    else p.wtn = 3;
   }
   // split K when the tiles leave CUs idle, keeping at least kMinSlice stages a slice
   p.ksplit = 1;
   const int nk = K / kBK;
   if (p.total > 0 && p.total < kSplitBelow) {
-    int sp = (kSplitTarget + p.total - 1) / p.total;
+    int sp = kSplitTarget / p.total;   // rounded down: the slices stay one pipelined round
     const int smax = nk / kMinSlice;
     sp = sp < smax ? sp : smax;
     p.ksplit = sp > 1 ? sp : 1;
@@ -627,7 +674,8 @@ hipError_t launch_gemm_tiled(const GemmArgs* segs, int nseg, int epi, float* par
     case EPI_STORE_F32: return launch_tile_e<EPI_STORE_F32>(ta, st);
     case EPI_STORE_ACT: return launch_tile_e<EPI_STORE_ACT>(ta, st);
     case EPI_RESID: return launch_tile_e<EPI_RESID>(ta, st);
-    case EPI_SWIGLU: return launch_tile_e<EPI_SWIGLU>(ta, st);
+    case EPI_SWIGLU:
+      return p.wtn == 3 ? launch_tile_e<EPI_SWIGLU, 3>(ta, st) : launch_tile_e<EPI_SWIGLU, 4>(ta, st);
     case EPI_ARGMAX: return launch_tile_e<EPI_ARGMAX>(ta, st);
     default: return hipErrorInvalidValue;
   }
