@@ -66,11 +66,11 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk
 // alternate gate and up rows of the same 64 outputs).
 template <int EPI, int WTN>
 __device__ __forceinline__ long weight_row(const GemmArgs& a, int nb, int l) {
-  if (EPI == EPI_SWIGLU && WTN == 3) {
-    // 96 rows per wave: each 32-row block holds the gate rows (first 16) and
-    // the up rows (last 16) of the same 16 outputs
-    const int w = l / 96, r = l % 96, i = r >> 5, h = r & 31;
-    int n = nb * 96 + w * 48 + i * 16 + (h & 15);
+  if (EPI == EPI_SWIGLU && WTN != 4) {
+    // 32 WTN rows per wave: each 32-row block holds the gate rows (first 16)
+    // and the up rows (last 16) of the same 16 outputs
+    const int w = l / (32 * WTN), r = l % (32 * WTN), i = r >> 5, h = r & 31;
+    int n = nb * (32 * WTN) + w * (16 * WTN) + i * 16 + (h & 15);
     n = n < a.N ? n : a.N - 1;
     return n + ((h & 16) ? a.pair_off : 0);
   }
@@ -86,7 +86,7 @@ __device__ __forceinline__ long weight_row(const GemmArgs& a, int nb, int l) {
 
 template <int EPI, int MODE, int PIPE, int WTN>
 __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs ta) {
-  static_assert(WTN == 4 || EPI == EPI_SWIGLU, "three-block waves only for SwiGLU");
+  static_assert(WTN == 4 || EPI == EPI_SWIGLU, "three- and six-block waves only for SwiGLU");
   constexpr int WTM = 2;                      // 32-token blocks per wave
   constexpr int kBN = 64 * WTN;               // weight rows per tile (WTN 32-row blocks per wave)
   constexpr int WR = 32 * WTN;                // weight rows per wave
@@ -430,14 +430,14 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
   auto store_u = [&](int u, auto chk) {
     constexpr bool CHK = decltype(chk)::value;
     const long orow = a.omap.row(a.tok0 + tk[u]);
-    if (EPI == EPI_SWIGLU && WTN == 3) {
+    if (EPI == EPI_SWIGLU && WTN != 4) {
       // gate rows 8 q + 4 fk + e (q < 2) and up rows 16 + the same of each block
       uint16_t* out = static_cast<uint16_t*>(a.out) + orow * a.ld_out;
 #pragma unroll
       for (int i = 0; i < WTN; ++i)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const int n = nb * 96 + wn * 48 + i * 16 + 8 * q + 4 * fk;
+          const int n = nb * (32 * WTN) + wn * (16 * WTN) + i * 16 + 8 * q + 4 * fk;
           if (CHK && n >= a.N) continue;
           uint32_t h[2];
 #pragma unroll
@@ -629,6 +629,11 @@ TilePlan plan_tiles(const int* M, const int* N, int nseg, int K, int epi) {
     count(96);
     if (p.total > kPipeItems || p.total < kSplitBelow) count(kBN / 2);
     else p.wtn = 3;
+  } else if (epi == EPI_SWIGLU && p.total > kPipeItems) {
+    // too many for one pipelined round: 192-output tiles (six blocks per wave)
+    count(192);
+    if (p.total > kPipeItems) count(kBN / 2);
+    else p.wtn = 6;
   }
   // split K when the tiles leave CUs idle, keeping at least kMinSlice stages a slice
   p.ksplit = 1;
@@ -675,7 +680,9 @@ hipError_t launch_gemm_tiled(const GemmArgs* segs, int nseg, int epi, float* par
     case EPI_STORE_ACT: return launch_tile_e<EPI_STORE_ACT>(ta, st);
     case EPI_RESID: return launch_tile_e<EPI_RESID>(ta, st);
     case EPI_SWIGLU:
-      return p.wtn == 3 ? launch_tile_e<EPI_SWIGLU, 3>(ta, st) : launch_tile_e<EPI_SWIGLU, 4>(ta, st);
+      if (p.wtn == 3) return launch_tile_e<EPI_SWIGLU, 3>(ta, st);
+      if (p.wtn == 6) return launch_tile_t1<EPI_SWIGLU, MODE_FULL, 1, 6>(ta, ta.total, st);   // one round, never split
+      return launch_tile_e<EPI_SWIGLU, 4>(ta, st);
     case EPI_ARGMAX: return launch_tile_e<EPI_ARGMAX>(ta, st);
     default: return hipErrorInvalidValue;
   }
