@@ -49,7 +49,7 @@ constexpr int kMinSlice = 4;             // stages per k slice, at least
 constexpr int kDirectSum = 2;            // slices the epilogue pass adds itself
 constexpr int kPipeItems = 256;          // work items up to which the main loop is pipelined
 
-// MODE_REDUCE1: the reduce pass with one wave per workgroup (4 workgroups
+// MODE_REDUCE1: the reduce pass with one wave per workgroup (8 workgroups
 // per output tile) for epilogues that need no exchange between waves.
 enum Mode { MODE_FULL = 0, MODE_SLICE = 1, MODE_REDUCE = 2, MODE_REDUCE1 = 3 };
 
@@ -108,7 +108,9 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
   //      fastest, then the k slice, then the weight tile, so the token tiles
   //      of one weight slice run side by side on one XCD
   const int S = MODE == MODE_SLICE ? ta.ksplit : 1;
-  constexpr int Q4 = MODE == MODE_REDUCE1 ? 4 : 1;   // workgroups per tile
+  // MODE_REDUCE1: eight one-wave workgroups per tile, one per (wave
+  // quarter, 32-token block)
+  constexpr int Q4 = MODE == MODE_REDUCE1 ? 8 : 1;   // workgroups per tile
   const int bid = blockIdx.x;
   int t = (bid & 7) * ta.per_xcd + (bid >> 3);
   if (t >= ta.total * S * Q4) return;
@@ -125,7 +127,8 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
 
   // tid: the thread's place in the 4-wave tile layout (one wave per
   // workgroup in MODE_REDUCE1)
-  const int tid = MODE == MODE_REDUCE1 ? quarter * 64 + static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x);
+  const int tid = MODE == MODE_REDUCE1 ? (quarter >> 1) * 64 + static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x);
+  const int uq = MODE == MODE_REDUCE1 ? (quarter & 1) : -1;   // the one token block of a reduce wave
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   const int fr = lane & 31, fk = lane >> 5;
@@ -286,7 +289,8 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
 #pragma unroll
       for (int i = 0; i < WTN; ++i)
 #pragma unroll
-        for (int u = 0; u < WTM; ++u)
+        for (int u = 0; u < WTM; ++u) {
+          if (MODE == MODE_REDUCE1 && u != uq) continue;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float4 v = pp[((i * WTM + u) * 4 + q) * NT + tid];
@@ -295,6 +299,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
             acc[i][u][4 * q + 2] += v.z;
             acc[i][u][4 * q + 3] += v.w;
           }
+        }
     }
   }
 
@@ -539,7 +544,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void gemm_tile_kernel(TileArgs t
 #pragma unroll
   for (int u = 0; u < WTM; ++u) {
     // the ssq shuffle pairs lanes fr and fr + 32, which share tok_ok
-    if (!tok_ok[u]) continue;
+    if (!tok_ok[u] || (MODE == MODE_REDUCE1 && u != uq)) continue;
     if (full) store_u(u, std::integral_constant<bool, false>());
     else store_u(u, std::integral_constant<bool, true>());
   }
@@ -602,7 +607,7 @@ hipError_t launch_tile_e(const TileArgs& ta, hipStream_t st) {
     tr.nsum = 1;
   }
   if constexpr (EPI == EPI_ARGMAX) return launch_tile_t<EPI, MODE_REDUCE, WTN>(tr, ta.total, st);
-  else return launch_tile_t<EPI, MODE_REDUCE1, WTN>(tr, ta.total * 4, st);
+  else return launch_tile_t<EPI, MODE_REDUCE1, WTN>(tr, ta.total * 8, st);
 }
 
 // Output tiles of each problem and the k split of the launch.
