@@ -5,19 +5,33 @@
 // no longer streamed past a tiny token block.  The output is cut into tiles of
 // 256 weight rows x 128 tokens; four waves each own a 128 x 64 block of one
 // tile and compute it with 32x32x16 MFMAs whose fragments come from LDS.  K is
-// walked in 64-wide stages: the next stage's weight and token rows are
-// fetched with 16-byte loads into registers while the current stage (one LDS
-// buffer of 48 KB) is multiplied.  Two workgroups share a CU (LDS and
-// registers are sized for it), so one's loads, barriers and epilogue overlap
-// the other's MFMAs.  LDS rows are 128 bytes with the 16-byte chunks of row R
-// stored at position (chunk ^ ((R >> 1) & 7)), so each 16-lane group of a
-// fragment load (16 consecutive rows) hits distinct banks without padding.
+// walked in 64-wide stages fetched with 16-byte loads into registers.  LDS
+// rows are 128 bytes with the 16-byte chunks of row R stored at position
+// (chunk ^ ((R >> 1) & 7)), so each 16-lane group of a fragment load (16
+// consecutive rows) hits distinct banks without padding.
 //
-// Launches with fewer output tiles than CUs split K: work item (tile, slice)
-// stores its fp32 accumulators as a partial tile, and a second launch of the
-// same kernel adds the slices of each tile in slice order (deterministic) and
-// runs the epilogue.
+// Launches of at most 256 work items run the pipelined loop, one workgroup
+// per CU: two register stages in flight and two 48 KB LDS buffers, one
+// barrier per stage, the next stage's stores interleaved with the MFMAs and
+// the fragments read one k step ahead.  Its steady-state loads are
+// unconditional: with conditional loads the compiler's wait counting loses
+// track of which register stage is older and waits for every load.  Larger
+// launches keep one register stage and one buffer, with two workgroups per CU
+// so that one's loads and barriers overlap the other's MFMAs.
 //
+// SwiGLU (gate/up) tiles are sized so that the launch fills one pipelined
+// round: 128 outputs (four 32-row blocks per wave, gate and up rows in
+// alternate 64-row halves), 96 outputs (three blocks) when 128-output tiles
+// would leave CUs idle, 192 outputs (six blocks) when they would need a
+// second round; in the three- and six-block shapes each 32-row block holds
+// the gate rows and then the up rows of the same 16 outputs.
+//
+// Launches with fewer output tiles than CUs split K (rounded down, so the
+// slices stay one round): work item (tile, slice) stores its fp32
+// accumulators as a partial tile, and a second launch of the same kernel adds
+// the slices of each tile in slice order (deterministic) and runs the
+// epilogue, one wave per (128-row quarter, 32-token block) of a tile.
+
 // Tiles are numbered with the token tile fastest and handed out per XCD in
 // contiguous ranges, so the token tiles that share a weight tile run side by
 // side on one XCD and read the weight tile through one L2.  Up to two
